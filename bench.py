@@ -1,0 +1,208 @@
+"""Throughput of the NeRF forward-render hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload hierarchical|coarse|tiny|hash]
+                    [--dtype bf16|f32] [--no-cpu-baseline]
+
+A step is one ``nerf_render`` over the whole workload with rays, weights
+and tables already resident in HBM.  Default workload: the hierarchical
+render, 4 poses x 800x800 rays (focal 1110), 64 stratified + 128
+inverse-CDF samples per ray, 8x256 coarse and fine networks in bfloat16.
+
+Prints one JSON line: rays/s (``value``), samples/s, the dominant kernel's
+achieved throughput against its roofline (timed live with HIP events on
+the launch stream), and the CPU oracle's throughput on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X
+MACS_8x256 = 593408
+MACS_4x64 = 21952
+MACS_HASH_FIELD = 19712
+
+WORKLOADS = {
+    # name: (poses, hemisphere, H, W, focal, n_coarse, n_fine, net kind, chunk)
+    "hierarchical": dict(poses=4, hemi=True, H=800, W=800, focal=1110.0, nc=64, nf=128, kind=1, chunk=0),
+    "coarse": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=1, chunk=65536),
+    "tiny": dict(poses=1, hemi=False, H=32, W=32, focal=40.0, nc=16, nf=0, kind=2, chunk=0),
+    "hash": dict(poses=1, hemi=True, H=256, W=256, focal=355.2, nc=128, nf=0, kind=4, chunk=0),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="hierarchical", choices=sorted(WORKLOADS))
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s):
+    """The oracle (float64 definition) timed on a bounded sample of rays."""
+    from oracle import render as oren
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Lp = 6 if kind == 2 else 10
+
+    def run(n):
+        sel = np.linspace(0, rays_o.shape[0] - 1, n).astype(np.int64)
+        t = time.perf_counter()
+        if kind == 4:
+            from oracle import encoding as oenc
+            grid, tabs, field = coarse
+            oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0)
+        else:
+            oren.render_nerf(rays_o[sel], rays_d[sel], near[sel], far[sel], coarse, fine if wl["nf"] else None,
+                             wl["nc"], wl["nf"], Lp, 4, seed=0)
+        return time.perf_counter() - t
+
+    n = 8
+    dt = run(n)
+    n2 = int(min(rays_o.shape[0], max(n, n * target_s / max(dt, 1e-3))))
+    dt2 = run(n2)
+    return {"value": n2 / dt2, "unit": "rays/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n2} rays evenly spaced over the workload, float64 oracle, {dt2:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rays shard independently; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import seeded_inputs as si
+    import volume_rendering_amd as v
+    from volume_rendering_amd import _binding as B
+
+    wl = WORKLOADS[args.workload]
+    dtype = 1 if args.dtype == "bf16" else 0
+    kind = wl["kind"]
+    if kind == 2 and args.dtype == "bf16" and args.workload == "tiny":
+        dtype = 0  # the tiny workload is defined in float32
+    dt_name = "bf16" if dtype else "f32"
+    dev = torch.device("cuda")
+
+    # rays on the device
+    P = si.poses(wl["poses"], seed=0, hemisphere=wl["hemi"])
+    H, W, f = wl["H"], wl["W"], wl["focal"]
+    R = wl["poses"] * H * W
+    ro = torch.empty((R, 3), device=dev)
+    rd = torch.empty((R, 3), device=dev)
+    for p in range(wl["poses"]):
+        v.nerf_gen_rays(P[p], W, H, f, f, 0.5 * W, 0.5 * H, ro[p * H * W:(p + 1) * H * W],
+                        rd[p * H * W:(p + 1) * H * W])
+    near = torch.full((R,), 2.0, device=dev)
+    far = torch.full((R,), 6.0, device=dev)
+
+    grid_keep = None
+    if kind == 4:
+        from oracle import encoding as _unused  # noqa: F401  (oracle only used for the cpu baseline)
+        g = v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048)
+        tabs = si.hash_tables(list(g.size)[:16], seed=0, scale=1.0)
+        tdev = torch.from_numpy(np.concatenate(tabs, 0)).to(dev)
+        g.tables = tdev.data_ptr()
+        field = si.hash_field_params(seed=0)
+        nets = [v.weights.pack_to_device(4, dtype, field)]
+        grid_keep = (g, tdev)
+        coarse_p, fine_p = field, None
+        mode = B.NERF_MODE_HASH
+    else:
+        shape = si.NERF_8x256 if kind == 1 else si.NERF_4x64
+        coarse_p = si.nerf_params(shape, seed=0, net_id=0)
+        fine_p = si.nerf_params(shape, seed=0, net_id=1)
+        nets = [v.weights.pack_to_device(kind, dtype, coarse_p), v.weights.pack_to_device(kind, dtype, fine_p)]
+        mode = B.NERF_MODE_NERF
+    cfg = B.nerf_render_cfg(mode=mode, n_coarse=wl["nc"], n_fine=wl["nf"], use_pi=1, jitter=1, seed=0,
+                            chunk=wl["chunk"], box_lo=-1.5, box_hi=1.5)
+    w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), coarse=nets[0].data_ptr(),
+                       fine=nets[1].data_ptr() if len(nets) > 1 else None)
+    if grid_keep is not None:
+        import ctypes
+        w.grid = ctypes.pointer(grid_keep[0])
+    rgb = torch.empty((R, 3), device=dev)
+    depth = torch.empty((R,), device=dev)
+    acc = torch.empty((R,), device=dev)
+
+    def step():
+        v.nerf_render(ro, rd, near, far, w, cfg, rgb, depth, acc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_kernel = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    n_mlp_samples = R * (wl["nc"] + (wl["nc"] + wl["nf"] if wl["nf"] else 0))
+    macs = MACS_8x256 if kind == 1 else MACS_4x64 if kind == 2 else MACS_HASH_FIELD
+    flops = 2.0 * macs * n_mlp_samples  # algorithmic network FLOPs per launch (all chunks of one step)
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    peak = PEAK[dt_name]
+    out = {
+        "metric": "rays/sec & samples/sec (coarse64+fine128, 8x256 MLP); MFMA util %, HBM GB/s %",
+        "value": R / (ms_step * 1e-3),
+        "unit": "rays/s",
+        "samples_per_sec": n_mlp_samples / (ms_step * 1e-3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic: seeded hemisphere poses, He-uniform random weights",
+        "config": {"workload": args.workload, "rays": R, "poses": wl["poses"], "H": H, "W": W, "focal": f,
+                   "n_coarse": wl["nc"], "n_fine": wl["nf"], "net": {1: "8x256", 2: "4x64", 4: "hash-field"}[kind],
+                   "chunk": wl["chunk"]},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "k_render_nerf" if kind != 4 else "k_render_hash", "kernel_ms": ms_kernel,
+                     "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        o_h, d_h = ro.cpu().numpy(), rd.cpu().numpy()
+        nf_h = near.cpu().numpy()
+        ff_h = far.cpu().numpy()
+        if kind == 4:
+            from oracle import encoding as oenc
+            og = oenc.hashgrid_3d()
+            base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, (og, tabs, coarse_p), None, args.cpu_seconds)
+        else:
+            base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, coarse_p, fine_p, args.cpu_seconds)
+        out["cpu_baseline"] = base
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,310 @@
+// C ABI of libnerf_mi355x.so: argument validation, error reporting and
+// dispatch to the gfx950 launchers.  Nothing is enqueued unless every
+// argument checks out.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "abi_util.hpp"
+#include "launch.hpp"
+#include "nerf_mi355x.h"
+#include "nets.hpp"
+
+using namespace nerf;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Clears an unrelated pending error, so the check after a launch reports
+// only this call's failure.
+void clear_pending() { (void)hipGetLastError(); }
+
+nerf_status check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return nerf_fail(NERF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return NERF_OK;
+}
+
+#define NERF_REQUIRE(cond, ...)                                  \
+    do {                                                         \
+        if (!(cond)) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
+    } while (0)
+
+bool net_is_nerf_family(int kind) { return kind == NET_8x256 || kind == NET_4x64 || kind == NET_CELL_2x32; }
+
+GridArgs grid_args(const nerf_hashgrid* g) {
+    GridArgs a{};
+    a.n_levels = g->n_levels;
+    a.tmask = g->table_size - 1;
+    for (int l = 0; l < g->n_levels; ++l) {
+        a.res[l] = g->res[l];
+        a.direct[l] = g->direct[l];
+        a.offset[l] = g->offset[l];
+    }
+    a.tables = g->tables;
+    return a;
+}
+
+nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
+    if (!g) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid is NULL", who);
+    if (!g->tables) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid tables are NULL", who);
+    if (g->n_levels < 1 || g->n_levels > NERF_HASH_MAX_LEVELS || g->n_feat != 2)
+        return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid not initialised (levels %d, features %d)", who,
+                         g->n_levels, g->n_feat);
+    if (g->table_size == 0 || (g->table_size & (g->table_size - 1)))
+        return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: table size %u not a power of two", who, g->table_size);
+    if (!aligned4(g->tables)) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 4-byte aligned", who);
+    for (int l = 0; l < g->n_levels; ++l) {
+        const int N = g->res[l];
+        if (N < 1 || N > 65535) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d resolution %d", who, l, N);
+        const uint64_t verts = (uint64_t)(N + 1) * (N + 1) * (N + 1);
+        const uint64_t need = g->direct[l] ? verts : g->table_size;
+        if (g->direct[l] && verts > g->table_size)
+            return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d marked direct but has %llu vertices", who, l,
+                             (unsigned long long)verts);
+        if (g->offset[l] + need > g->total_entries)
+            return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d overruns the tables", who, l);
+    }
+    return NERF_OK;
+}
+
+}  // namespace
+
+nerf_status nerf_fail(nerf_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+extern "C" {
+
+int nerf_abi_version(void) { return NERF_ABI_VERSION; }
+
+const char* nerf_status_str(nerf_status s) {
+    switch (s) {
+        case NERF_OK:
+            return "NERF_OK";
+        case NERF_ERR_INVALID_ARGUMENT:
+            return "NERF_ERR_INVALID_ARGUMENT";
+        case NERF_ERR_UNSUPPORTED:
+            return "NERF_ERR_UNSUPPORTED";
+        case NERF_ERR_WORKSPACE:
+            return "NERF_ERR_WORKSPACE";
+        case NERF_ERR_HIP:
+            return "NERF_ERR_HIP";
+    }
+    return "NERF_ERR_UNKNOWN";
+}
+
+const char* nerf_last_error(void) { return g_last_error.c_str(); }
+
+nerf_status nerf_gen_rays(const float* pose, const nerf_intrinsics* K, float* rays_o, float* rays_d, void* stream) {
+    NERF_REQUIRE(pose && K && rays_o && rays_d, "nerf_gen_rays: NULL argument");
+    NERF_REQUIRE(K->W >= 1 && K->H >= 1, "nerf_gen_rays: image %dx%d", K->W, K->H);
+    NERF_REQUIRE((int64_t)K->W * K->H <= (int64_t)1 << 31, "nerf_gen_rays: image too large");
+    NERF_REQUIRE(K->fx != 0.0f && K->fy != 0.0f, "nerf_gen_rays: zero focal length");
+    NERF_REQUIRE(aligned4(rays_o) && aligned4(rays_d), "nerf_gen_rays: misaligned output");
+    clear_pending();
+    launch_gen_rays(pose, K->W, K->H, K->fx, K->fy, K->cx, K->cy, rays_o, rays_d, as_stream(stream));
+    return check_launch("nerf_gen_rays");
+}
+
+nerf_status nerf_sample_stratified(const float* t_near, const float* t_far, int64_t n_rays, int n, uint64_t seed,
+                                   uint64_t ray_offset, int jitter, float* z, void* stream) {
+    NERF_REQUIRE(n_rays >= 0, "nerf_sample_stratified: n_rays %lld", (long long)n_rays);
+    NERF_REQUIRE(n >= 1 && n <= 256, "nerf_sample_stratified: %d samples outside 1..256", n);
+    if (n_rays == 0) return NERF_OK;
+    NERF_REQUIRE(t_near && t_far && z, "nerf_sample_stratified: NULL argument");
+    clear_pending();
+    launch_stratified(t_near, t_far, n_rays, n, seed, ray_offset, jitter, z, as_stream(stream));
+    return check_launch("nerf_sample_stratified");
+}
+
+nerf_status nerf_encode_freq(const float* x, int64_t n, int in_dim, int n_freq, int include_input, int use_pi,
+                             int out_dtype, void* out, void* stream) {
+    NERF_REQUIRE(n >= 0, "nerf_encode_freq: n %lld", (long long)n);
+    NERF_REQUIRE(in_dim >= 1 && in_dim <= 4, "nerf_encode_freq: in_dim %d outside 1..4", in_dim);
+    NERF_REQUIRE(n_freq >= 0 && n_freq <= 16, "nerf_encode_freq: n_freq %d outside 0..16", n_freq);
+    NERF_REQUIRE(out_dtype == NERF_F32 || out_dtype == NERF_BF16, "nerf_encode_freq: dtype %d", out_dtype);
+    NERF_REQUIRE(include_input || n_freq > 0, "nerf_encode_freq: empty encoding");
+    if (n == 0) return NERF_OK;
+    NERF_REQUIRE(x && out, "nerf_encode_freq: NULL argument");
+    clear_pending();
+    launch_encode_freq(x, n, in_dim, n_freq, include_input ? 1 : 0, use_pi ? 1 : 0, out_dtype == NERF_BF16, out,
+                       as_stream(stream));
+    return check_launch("nerf_encode_freq");
+}
+
+nerf_status nerf_encode_sh16(const float* dirs, int64_t n, float* out, void* stream) {
+    NERF_REQUIRE(n >= 0, "nerf_encode_sh16: n %lld", (long long)n);
+    if (n == 0) return NERF_OK;
+    NERF_REQUIRE(dirs && out, "nerf_encode_sh16: NULL argument");
+    clear_pending();
+    launch_sh16(dirs, n, out, as_stream(stream));
+    return check_launch("nerf_encode_sh16");
+}
+
+nerf_status nerf_encode_hashgrid(const float* x, int64_t n, const nerf_hashgrid* g, float* out, uint32_t* idx_dbg,
+                                 void* stream) {
+    NERF_REQUIRE(n >= 0, "nerf_encode_hashgrid: n %lld", (long long)n);
+    const nerf_status gs = check_grid(g, "nerf_encode_hashgrid");
+    if (gs != NERF_OK) return gs;
+    if (n == 0) return NERF_OK;
+    NERF_REQUIRE(x && out, "nerf_encode_hashgrid: NULL argument");
+    NERF_REQUIRE(aligned16(out) || ((reinterpret_cast<uintptr_t>(out) & 7u) == 0),
+                 "nerf_encode_hashgrid: out not 8-byte aligned");
+    clear_pending();
+    const GridArgs a = grid_args(g);
+    launch_encode_hash(x, n, a, out, idx_dbg, as_stream(stream));
+    return check_launch("nerf_encode_hashgrid");
+}
+
+nerf_status nerf_mlp(const nerf_mlp_desc* net, const void* packed, const float* enc_x, const float* enc_v, int64_t n,
+                     int samples_per_ray, float* raw, void* stream) {
+    NERF_REQUIRE(net, "nerf_mlp: net is NULL");
+    if (nerf_mlp_packed_bytes(net) == 0)
+        return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_mlp: unsupported network kind %d / dtype %d", net->kind,
+                         net->dtype);
+    NERF_REQUIRE(n >= 0, "nerf_mlp: n %lld", (long long)n);
+    NERF_REQUIRE(samples_per_ray >= 1, "nerf_mlp: samples_per_ray %d", samples_per_ray);
+    if (n == 0) return NERF_OK;
+    NERF_REQUIRE(packed && enc_x && enc_v && raw, "nerf_mlp: NULL argument");
+    NERF_REQUIRE(aligned16(packed) && aligned16(raw), "nerf_mlp: packed weights and raw must be 16-byte aligned");
+    clear_pending();
+    launch_mlp(net->kind, net->dtype == NERF_BF16, packed, enc_x, enc_v, n, samples_per_ray, raw, as_stream(stream));
+    return check_launch("nerf_mlp");
+}
+
+nerf_status nerf_composite(const float* raw, const float* z, const float* rays_d, int64_t n_rays, int n,
+                           int white_bkgd, float* rgb, float* depth, float* acc, float* weights, void* stream) {
+    NERF_REQUIRE(n_rays >= 0, "nerf_composite: n_rays %lld", (long long)n_rays);
+    NERF_REQUIRE(n >= 1 && n <= 4096, "nerf_composite: %d samples outside 1..4096", n);
+    if (n_rays == 0) return NERF_OK;
+    NERF_REQUIRE(raw && z && rays_d && rgb && depth && acc, "nerf_composite: NULL argument");
+    NERF_REQUIRE(aligned16(raw), "nerf_composite: raw must be 16-byte aligned");
+    clear_pending();
+    launch_composite(raw, z, rays_d, n_rays, n, white_bkgd ? 1 : 0, rgb, depth, acc, weights, as_stream(stream));
+    return check_launch("nerf_composite");
+}
+
+nerf_status nerf_sample_pdf(const float* z_coarse, const float* w_coarse, int64_t n_rays, int n_coarse, int n_fine,
+                            uint64_t seed, uint64_t ray_offset, float* z_fine, int32_t* bin_idx, float* z_merged,
+                            void* stream) {
+    NERF_REQUIRE(n_rays >= 0, "nerf_sample_pdf: n_rays %lld", (long long)n_rays);
+    NERF_REQUIRE(n_coarse >= 3, "nerf_sample_pdf: n_coarse %d < 3", n_coarse);
+    NERF_REQUIRE(n_fine >= 1, "nerf_sample_pdf: n_fine %d < 1", n_fine);
+    NERF_REQUIRE(n_coarse + n_fine <= 256, "nerf_sample_pdf: n_coarse + n_fine = %d > 256", n_coarse + n_fine);
+    if (n_rays == 0) return NERF_OK;
+    NERF_REQUIRE(z_coarse && w_coarse, "nerf_sample_pdf: NULL input");
+    clear_pending();
+    launch_sample_pdf(z_coarse, w_coarse, n_rays, n_coarse, n_fine, seed, ray_offset, z_fine, bin_idx, z_merged,
+                      as_stream(stream));
+    return check_launch("nerf_sample_pdf");
+}
+
+size_t nerf_render_workspace_size(const nerf_render_cfg* cfg, int64_t n_rays) {
+    (void)cfg;
+    (void)n_rays;
+    return 0;
+}
+
+nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
+                        int64_t n_rays, const nerf_weights* w, const nerf_render_cfg* cfg, float* rgb, float* depth,
+                        float* acc, void* stream) {
+    NERF_REQUIRE(w && cfg, "nerf_render: NULL weights or cfg");
+    NERF_REQUIRE(n_rays >= 0, "nerf_render: n_rays %lld", (long long)n_rays);
+    NERF_REQUIRE(cfg->n_coarse >= 1 && cfg->n_coarse <= 256, "nerf_render: n_coarse %d outside 1..256",
+                 cfg->n_coarse);
+    NERF_REQUIRE(cfg->n_fine >= 0, "nerf_render: n_fine %d", cfg->n_fine);
+    NERF_REQUIRE(cfg->chunk >= 0, "nerf_render: chunk %lld", (long long)cfg->chunk);
+    if (nerf_mlp_packed_bytes(&w->net) == 0)
+        return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: unsupported network kind %d / dtype %d", w->net.kind,
+                         w->net.dtype);
+    const int bf16 = w->net.dtype == NERF_BF16;
+    RenderArgs a{};
+    a.n_coarse = cfg->n_coarse;
+    a.n_fine = cfg->n_fine;
+    a.use_pi = cfg->use_pi;
+    a.white = cfg->white_bkgd;
+    a.jitter = cfg->jitter;
+    a.seed = cfg->seed;
+    a.box_lo = cfg->box_lo;
+    a.box_hi = cfg->box_hi;
+    GridArgs ga{};
+    switch (cfg->mode) {
+        case NERF_MODE_NERF:
+            if (w->net.kind != NET_8x256 && w->net.kind != NET_4x64)
+                return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: NeRF mode needs the 8x256 or 4x64 network");
+            NERF_REQUIRE(w->coarse, "nerf_render: coarse network is NULL");
+            if (cfg->n_fine > 0) {
+                NERF_REQUIRE(w->fine, "nerf_render: fine network is NULL");
+                NERF_REQUIRE(cfg->n_coarse >= 3, "nerf_render: resampling needs n_coarse >= 3");
+                NERF_REQUIRE(cfg->n_coarse + cfg->n_fine <= 256, "nerf_render: n_coarse + n_fine > 256");
+            }
+            NERF_REQUIRE(aligned16(w->coarse) && (!w->fine || aligned16(w->fine)),
+                         "nerf_render: packed networks must be 16-byte aligned");
+            break;
+        case NERF_MODE_HASH: {
+            if (w->net.kind != NET_HASH_FIELD)
+                return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: hash mode needs the hash-field network");
+            NERF_REQUIRE(w->coarse, "nerf_render: field network is NULL");
+            NERF_REQUIRE(aligned16(w->coarse), "nerf_render: packed network must be 16-byte aligned");
+            NERF_REQUIRE(cfg->n_fine == 0, "nerf_render: hash mode has no resampling pass");
+            const nerf_status gs = check_grid(w->grid, "nerf_render");
+            if (gs != NERF_OK) return gs;
+            if (w->grid->n_levels != 16)
+                return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: the field network takes 16 levels x 2 features");
+            NERF_REQUIRE(cfg->box_hi > cfg->box_lo, "nerf_render: empty scene box");
+            ga = grid_args(w->grid);
+            break;
+        }
+        case NERF_MODE_KILO:
+            return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: many-network mode not built");
+        default:
+            return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_render: mode %d", cfg->mode);
+    }
+    if (n_rays == 0) return NERF_OK;
+    NERF_REQUIRE(rays_o && rays_d && t_near && t_far && rgb && depth && acc, "nerf_render: NULL ray or output");
+    const int64_t chunk = cfg->chunk > 0 ? cfg->chunk : n_rays;
+    const int n_total = cfg->mode == NERF_MODE_NERF ? cfg->n_coarse + cfg->n_fine : cfg->n_coarse;
+    clear_pending();
+    for (int64_t r0 = 0; r0 < n_rays; r0 += chunk) {
+        const int64_t nr = (n_rays - r0) < chunk ? (n_rays - r0) : chunk;
+        RenderArgs c = a;
+        c.ro = rays_o + 3 * r0;
+        c.rd = rays_d + 3 * r0;
+        c.tn = t_near + r0;
+        c.tf = t_far + r0;
+        c.n_rays = nr;
+        c.ray_offset = cfg->ray_offset + (uint64_t)r0;
+        c.coarse = w->coarse;
+        c.fine = w->fine;
+        c.rgb = rgb + 3 * r0;
+        c.depth = depth + r0;
+        c.acc = acc + r0;
+        c.dbg_z = cfg->dbg_z ? cfg->dbg_z + r0 * n_total : nullptr;
+        c.dbg_w = cfg->dbg_w_coarse ? cfg->dbg_w_coarse + r0 * cfg->n_coarse : nullptr;
+        if (cfg->mode == NERF_MODE_NERF)
+            launch_render_nerf(w->net.kind, bf16, c, as_stream(stream));
+        else
+            launch_render_hash(bf16, c, ga, as_stream(stream));
+        const nerf_status st = check_launch("nerf_render");
+        if (st != NERF_OK) return st;
+    }
+    return NERF_OK;
+}
+
+}  // extern "C"

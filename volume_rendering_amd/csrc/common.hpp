@@ -1,0 +1,123 @@
+// Shared device helpers for the gfx950 kernels: the Philox generator,
+// wave-level scans, bfloat16 packing and float32 steps with explicit
+// rounding.  Only code built for gfx950 (wave64, MFMA) lives here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nerf {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64-bit products with
+// the key bumped by the Weyl constants between rounds.  Only the first
+// output word is used.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_w0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    return c0;
+}
+
+// Uniform in [0, 1 - 2^-24] on the 2^-24 grid from the top 24 bits.
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t ray, uint32_t index, uint32_t stream) {
+    const uint32_t w = philox_w0((uint32_t)ray, index, (uint32_t)(ray >> 32), stream, (uint32_t)seed,
+                                 (uint32_t)(seed >> 32));
+    return (float)(w >> 8) * 0x1p-24f;
+}
+
+constexpr uint32_t kStreamJitter = 0;
+constexpr uint32_t kStreamPdf = 1;
+
+// Stratified sample i of n on [near, far] as rounded float32 operations:
+// z = near + ((far - near)/n) * (i + u).
+__device__ __forceinline__ float stratified_z(float near, float far, int i, int n, float u) {
+    const float step = __fdiv_rn(__fsub_rn(far, near), (float)n);
+    return __fadd_rn(near, __fmul_rn(step, __fadd_rn((float)i, u)));
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Orders this wave's LDS traffic: every lane's earlier LDS writes are visible
+// to every lane of the wave after the call.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Hides a wave-uniform pointer from loop-invariant code motion, so weight
+// loads inside a per-block loop stay next to their use instead of being
+// hoisted (and kept live) across the whole loop.
+template <class P>
+__device__ __forceinline__ P* opaque(P* p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Inclusive product scan over the 64 lanes.
+__device__ __forceinline__ float wave_scan_mul(float v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(v, off, kWave);
+        if (l >= off) v *= o;
+    }
+    return v;
+}
+
+// Inclusive sum scan over the 64 lanes (float64).
+__device__ __forceinline__ double wave_scan_add_f64(double v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(v, off, kWave);
+        if (l >= off) v += o;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Numerics
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }  // v_cvt_pk_bf16_f32, nearest even
+__device__ __forceinline__ float bf16_round(float f) { return (float)(__bf16)f; }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace nerf

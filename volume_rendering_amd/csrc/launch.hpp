@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels and the plain argument structs
+// they take.  Shapes and pointers are validated by the C ABI layer before
+// any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nerf {
+
+struct GridArgs {
+    int n_levels;
+    uint32_t tmask;  // T - 1 (T a power of two)
+    int res[16];
+    int direct[16];
+    uint64_t offset[16];
+    const void* tables;  // float16 pairs, levels back to back
+};
+
+struct RenderArgs {
+    const float* ro;
+    const float* rd;
+    const float* tn;
+    const float* tf;
+    int64_t n_rays;
+    const void* coarse;
+    const void* fine;
+    int n_coarse, n_fine;
+    int use_pi, white, jitter;
+    uint64_t seed, ray_offset;
+    float box_lo, box_hi;
+    float* rgb;
+    float* depth;
+    float* acc;
+    float* dbg_z;
+    float* dbg_w;
+};
+
+void launch_gen_rays(const float* pose, int W, int H, float fx, float fy, float cx, float cy, float* ro, float* rd,
+                     hipStream_t s);
+void launch_stratified(const float* tn, const float* tf, int64_t n_rays, int n, uint64_t seed, uint64_t ray_offset,
+                       int jitter, float* z, hipStream_t s);
+void launch_encode_freq(const float* x, int64_t n, int d, int L, int inc, int use_pi, int bf16, void* out,
+                        hipStream_t s);
+void launch_sh16(const float* dirs, int64_t n, float* out, hipStream_t s);
+void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out, uint32_t* idx, hipStream_t s);
+void launch_composite(const float* raw, const float* z, const float* rd, int64_t n_rays, int n, int white, float* rgb,
+                      float* depth, float* acc, float* w, hipStream_t s);
+void launch_sample_pdf(const float* zc, const float* wc, int64_t n_rays, int nc, int nf, uint64_t seed,
+                       uint64_t ray_offset, float* zf, int32_t* bins, float* z2, hipStream_t s);
+void launch_mlp(int kind, int bf16, const void* packed, const float* ex, const float* ev, int64_t n, int spr,
+                float* raw, hipStream_t s);
+void launch_render_nerf(int kind, int bf16, const RenderArgs& a, hipStream_t s);
+void launch_render_hash(int bf16, const RenderArgs& a, const GridArgs& g, hipStream_t s);
+
+}  // namespace nerf

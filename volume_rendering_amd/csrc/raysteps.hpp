@@ -1,0 +1,201 @@
+// Per-wave building blocks shared by the standalone kernels and the fused
+// render: compositing of one ray, inverse-CDF resampling plus merge of one
+// ray, spherical harmonics and multiresolution hash-grid lookups.
+#pragma once
+
+#include <hip/hip_fp16.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nerf {
+
+// ---------------------------------------------------------------------------
+// Alpha compositing of one ray by one wave ("Spatial Intelligence - Part 1:
+// NeRF", Section 1 Theory, 3. Volume rendering; Section 2 Code, 5. Volume
+// rendering in code).  Samples are taken 64 at a time, one per lane; the
+// exclusive transmittance product is a wave-level multiplicative scan whose
+// last value carries into the next 64 samples.  `term_T` > 0 zeroes sample i
+// and every later sample once T_i < term_T.
+// ---------------------------------------------------------------------------
+struct CompositeOut {
+    float r, g, b, depth, acc;
+};
+
+__device__ __forceinline__ CompositeOut composite_ray(const float* z, const f32x4* raw, int n, float dnorm,
+                                                      float* w_out, float term_T) {
+    const int lane = lane_id();
+    float carry = 1.0f;
+    float sr = 0.f, sg = 0.f, sbl = 0.f, sd = 0.f, sa = 0.f;
+    bool stopped = false;
+    for (int base = 0; base < n; base += kWave) {
+        const int i = base + lane;
+        const bool valid = i < n;
+        float alpha = 0.f, zi = 0.f;
+        f32x4 r = {0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+            zi = z[i];
+            const float delta = (i + 1 < n) ? (z[i + 1] - zi) * dnorm : 1e10f * dnorm;
+            r = raw[i];
+            const float sigma = fmaxf(r[3], 0.0f);
+            alpha = 1.0f - expf(-sigma * delta);
+        }
+        const float surv = valid ? (1.0f - alpha + 1e-10f) : 1.0f;
+        const float incl = wave_scan_mul(surv);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 1.0f;
+        const float T = carry * excl;
+        bool stop_here = false;
+        if (term_T > 0.0f) {
+            // first sample of this block (in order) with T < term_T, unless already stopped
+            const unsigned long long m = __ballot(valid && T < term_T);
+            const int first = m ? __builtin_ctzll(m) : kWave;
+            stop_here = stopped || (lane >= first);
+            if (m) stopped = true;
+        }
+        float w = (valid && !stop_here) ? T * alpha : 0.0f;
+        if (valid && w_out) w_out[i] = w;
+        sa += w;
+        sd += w * zi;
+        sr += w * sigmoidf_(r[0]);
+        sg += w * sigmoidf_(r[1]);
+        sbl += w * sigmoidf_(r[2]);
+        carry *= __shfl(incl, kWave - 1, kWave);
+        if (stopped && term_T > 0.0f) break;
+    }
+    CompositeOut o;
+    o.r = wave_sum(sr);
+    o.g = wave_sum(sg);
+    o.b = wave_sum(sbl);
+    o.depth = wave_sum(sd);
+    o.acc = wave_sum(sa);
+    return o;
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF resampling of one ray by one wave (Section 1 Theory, 4.2
+// Hierarchical volume sampling; Section 2 Code, 6. Hierarchical sampling).
+// zc[0..nc) coarse samples, wc their weights.  Scratch: bins (nc-1 floats),
+// cdf (nc-1 doubles).  The cdf is the exact float64 running sum of
+// w'_j = w_{j+1} + 1e-5 divided by its total, so every comparison with u is
+// decided exactly as in any other exact evaluation.  Writes the fine samples
+// to zf[0..nf) (may alias zc + nc) and optionally bin indices.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void sample_pdf_ray(const float* zc, const float* wc, int nc, int nf, uint64_t seed,
+                                               uint64_t ray, float* bins, double* cdf, float* zf,
+                                               int32_t* bin_out) {
+    const int lane = lane_id();
+    const int B = nc - 2;  // weights used: w[1..nc-2]
+    for (int k = lane; k < nc - 1; k += kWave) bins[k] = __fmul_rn(0.5f, __fadd_rn(zc[k], zc[k + 1]));
+    double carry = 0.0;
+    for (int base = 0; base < B; base += kWave) {
+        const int j = base + lane;
+        const double v = j < B ? (double)__fadd_rn(wc[j + 1], 1e-5f) : 0.0;
+        const double incl = wave_scan_add_f64(v);
+        if (j < B) cdf[j + 1] = carry + incl;
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    wave_lds_sync();
+    const double total = carry;
+    for (int k = lane; k <= B; k += kWave) cdf[k] = k == 0 ? 0.0 : cdf[k] / total;
+    wave_lds_sync();
+    for (int m = lane; m < nf; m += kWave) {
+        const double u = (double)philox_uniform(seed, ray, (uint32_t)m, kStreamPdf);
+        int lo = 0, hi = B + 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (cdf[mid] <= u)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        const int below = lo - 1 > 0 ? lo - 1 : 0;
+        const int above = lo < B ? lo : B;
+        const double cb = cdf[below];
+        const double denom = fmax(__dsub_rn(cdf[above], cb), 1e-5);
+        const double t = __ddiv_rn(__dsub_rn(u, cb), denom);
+        const double bb = (double)bins[below];
+        const double ba = (double)bins[above];
+        zf[m] = (float)__dadd_rn(bb, __dmul_rn(t, __dsub_rn(ba, bb)));
+        if (bin_out) bin_out[m] = lo;
+    }
+    wave_lds_sync();
+}
+
+// Ascending merge of u[0..n) into out[0..n) by rank: element e goes to
+// #{q : u_q < u_e} + #{q < e : u_q == u_e}.
+__device__ __forceinline__ void merge_rank(const float* u, int n, float* out) {
+    const int lane = lane_id();
+    for (int e = lane; e < n; e += kWave) {
+        const float v = u[e];
+        int rank = 0;
+        for (int q = 0; q < n; ++q) {
+            const float w = u[q];
+            rank += (w < v) || (w == v && q < e);
+        }
+        out[rank] = v;
+    }
+    wave_lds_sync();
+}
+
+// ---------------------------------------------------------------------------
+// Real spherical harmonics, degrees 0..3, orthonormal, no Condon-Shortley
+// phase; order: l, then m = -l..l.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void sh16_eval(float x, float y, float z, float (&o)[16]) {
+    const float xx = x * x, yy = y * y, zz = z * z;
+    o[0] = 0.28209479177387814f;
+    o[1] = 0.4886025119029199f * y;
+    o[2] = 0.4886025119029199f * z;
+    o[3] = 0.4886025119029199f * x;
+    o[4] = 1.0925484305920792f * x * y;
+    o[5] = 1.0925484305920792f * y * z;
+    o[6] = 0.31539156525252005f * (3.0f * zz - 1.0f);
+    o[7] = 1.0925484305920792f * x * z;
+    o[8] = 0.5462742152960396f * (xx - yy);
+    o[9] = 0.5900435899266435f * y * (3.0f * xx - yy);
+    o[10] = 2.890611442640554f * x * y * z;
+    o[11] = 0.4570457994644658f * y * (5.0f * zz - 1.0f);
+    o[12] = 0.3731763325901154f * z * (5.0f * zz - 3.0f);
+    o[13] = 0.4570457994644658f * x * (5.0f * zz - 1.0f);
+    o[14] = 1.445305721320277f * z * (xx - yy);
+    o[15] = 0.5900435899266435f * x * (xx - 3.0f * yy);
+}
+
+// ---------------------------------------------------------------------------
+// Multiresolution hash grid ("Instant-NGP - Visual Experiments", shared
+// toolkit, extended to 3D).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t grid_index(int ix, int iy, int iz, int N, bool direct, uint32_t tmask) {
+    if (direct) return (uint32_t)((ix * (N + 1) + iy) * (N + 1) + iz);
+    return ((uint32_t)ix ^ ((uint32_t)iy * 2654435761u) ^ ((uint32_t)iz * 805459861u)) & tmask;
+}
+
+// Interpolated features (f0, f1) of level l at unit-cube point u; corner
+// indices optionally written to idx_out[0..8).
+__device__ __forceinline__ void grid_level(const GridArgs& g, int l, float ux, float uy, float uz, float& f0, float& f1,
+                                           uint32_t* idx_out) {
+    const int N = g.res[l];
+    const bool direct = g.direct[l] != 0;
+    const float cx = __fmul_rn(ux, (float)N), cy = __fmul_rn(uy, (float)N), cz = __fmul_rn(uz, (float)N);
+    const float fx = floorf(cx), fy = floorf(cy), fz = floorf(cz);
+    const float wx = cx - fx, wy = cy - fy, wz = cz - fz;
+    const int x0 = (int)fx, y0 = (int)fy, z0 = (int)fz;
+    const __half2* tab = reinterpret_cast<const __half2*>(g.tables) + g.offset[l];
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int dx = (c >> 2) & 1, dy = (c >> 1) & 1, dz = c & 1;
+        const int ix = min(max(x0 + dx, 0), N), iy = min(max(y0 + dy, 0), N), iz = min(max(z0 + dz, 0), N);
+        const uint32_t idx = grid_index(ix, iy, iz, N, direct, g.tmask);
+        if (idx_out) idx_out[c] = idx;
+        const float2 v = __half22float2(tab[idx]);
+        const float wt = (dx ? wx : 1.0f - wx) * (dy ? wy : 1.0f - wy) * (dz ? wz : 1.0f - wz);
+        a0 += wt * v.x;
+        a1 += wt * v.y;
+    }
+    f0 = a0;
+    f1 = a1;
+}
+
+}  // namespace nerf

@@ -1,0 +1,282 @@
+// Fused per-ray forward renders for gfx950: one wave renders one ray from
+// its first sample to its composited colour; samples, encodings and
+// activations stay in registers and the wave's LDS, nothing intermediate
+// goes to HBM.
+//
+// NeRF mode ("Spatial Intelligence - Part 1: NeRF", Section 2 Code,
+// 6. Hierarchical sampling, render_rays): stratified samples -> coarse
+// network -> compositing -> inverse-CDF resampling + merge -> fine network
+// -> compositing.  Both passes run through one copy of the network code (the
+// pass index selects weights and the sample source).
+//
+// Hash mode: stratified samples -> hash-grid features and harmonics ->
+// field network -> compositing.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "mlp.hpp"
+#include "raysteps.hpp"
+
+namespace nerf {
+
+constexpr int kMaxRaySamples = 256;
+
+struct RenderLds {
+    float zc[kMaxRaySamples];  // first-pass samples, then the fine samples (union for the merge)
+    float z2[kMaxRaySamples];  // merged samples of the second pass
+    f32x4 raw[kMaxRaySamples];
+    float w[kMaxRaySamples];
+    double cdf[kMaxRaySamples];
+    float bins[kMaxRaySamples];
+};
+
+template <class T, int KIND>
+__global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
+    __shared__ RenderLds lds_all[4];
+    using Fam = NerfFamily<KIND>;
+    constexpr Layer L0 = net_layers(KIND)[0];
+    constexpr Layer LD = net_layers(KIND)[Fam::D + 2];
+    constexpr int ES = seg_steps(L0.s0, T::prec);
+    constexpr int DS = seg_steps(LD.s1, T::prec);
+    constexpr int SB = T::SB;
+    constexpr int M = 32 * SB;
+
+    const int wave = threadIdx.x / kWave;
+    RenderLds& S = lds_all[wave];
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= a.n_rays) return;
+    const int lane = lane_id();
+    const int h = lane >> 5;
+    const uint64_t ray = a.ray_offset + (uint64_t)r;
+
+    const float o[3] = {a.ro[3 * r], a.ro[3 * r + 1], a.ro[3 * r + 2]};
+    const float d[3] = {a.rd[3 * r], a.rd[3 * r + 1], a.rd[3 * r + 2]};
+    const float near = a.tn[r], far = a.tf[r];
+    const float dn = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+
+    typename T::Op denc[DS][SB];
+    {
+        float v[SB][3];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) v[sb][k] = d[k] / dn;
+        enc_operands(denc, Fam::LDIR, v, a.use_pi != 0, lane);
+    }
+
+    const int nc = a.n_coarse, nf = a.n_fine;
+    const int npass = nf > 0 ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int N = pass ? nc + nf : nc;
+        const char* packed = pass ? (const char*)a.fine : (const char*)a.coarse;
+        for (int blk = 0; blk < N; blk += M) {
+            float x[SB][3];
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                const int s = blk + sb * 32 + (lane & 31);
+                const int sv = s < N ? s : N - 1;
+                float z;
+                if (pass) {
+                    z = S.z2[sv];
+                } else {
+                    const float u = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)sv, kStreamJitter) : 0.5f;
+                    z = stratified_z(near, far, sv, nc, u);
+                    if (h == 0 && s < N) S.zc[s] = z;
+                }
+#pragma unroll
+                for (int k = 0; k < 3; ++k) x[sb][k] = __fadd_rn(o[k], __fmul_rn(z, d[k]));
+            }
+            typename T::Op enc[ES][SB];
+            enc_operands(enc, Fam::LPOS, x, a.use_pi != 0, lane);
+            f32x16 sig[SB], rgb[SB];
+            nerf_forward<T, KIND>(enc, denc, opaque(packed), sig, rgb, lane);
+            if (lane < 32) {
+#pragma unroll
+                for (int sb = 0; sb < SB; ++sb) {
+                    const int s = blk + sb * 32 + lane;
+                    if (s < N) S.raw[s] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
+                }
+            }
+        }
+        wave_lds_sync();
+        const float* zp = pass ? S.z2 : S.zc;
+        const CompositeOut c = composite_ray(zp, S.raw, N, dn, pass == 0 ? S.w : nullptr, 0.0f);
+        wave_lds_sync();
+        if (pass == 0 && a.dbg_w)
+            for (int i = lane; i < nc; i += kWave) a.dbg_w[r * nc + i] = S.w[i];
+        if (pass == npass - 1) {
+            if (a.dbg_z)
+                for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = zp[i];
+            if (lane == 0) {
+                const float bg = a.white ? 1.0f - c.acc : 0.0f;
+                a.rgb[3 * r] = c.r + bg;
+                a.rgb[3 * r + 1] = c.g + bg;
+                a.rgb[3 * r + 2] = c.b + bg;
+                a.depth[r] = c.depth;
+                a.acc[r] = c.acc;
+            }
+        } else {
+            sample_pdf_ray(S.zc, S.w, nc, nf, a.seed, ray, S.bins, S.cdf, S.zc + nc, nullptr);
+            merge_rank(S.zc, nc + nf, S.z2);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Hash-grid field render
+// ---------------------------------------------------------------------------
+template <int NS>
+__device__ __forceinline__ void grid_operands(bf16x8 (&op)[NS][2], const GridArgs& g, const float (&u)[2][3],
+                                              int lane) {
+    static_assert(NS == 2, "32 grid features");
+    const int h = lane >> 5;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 v;
+#pragma unroll
+            for (int jl = 0; jl < 4; ++jl) {
+                float f0, f1;
+                grid_level(g, 8 * s + 4 * h + jl, u[sb][0], u[sb][1], u[sb][2], f0, f1, nullptr);
+                v[2 * jl] = to_bf16(f0);
+                v[2 * jl + 1] = to_bf16(f1);
+            }
+            op[s][sb] = v;
+        }
+}
+
+template <int NS>
+__device__ __forceinline__ void grid_operands(float (&op)[NS][1], const GridArgs& g, const float (&u)[1][3],
+                                              int lane) {
+    static_assert(NS == 16, "32 grid features");
+    const int h = lane >> 5;
+    float f0[8], f1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) grid_level(g, 8 * h + q, u[0][0], u[0][1], u[0][2], f0[q], f1[q], nullptr);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        // step s needs feature 2s+h = level s, component h; levels 8h..8h+7 are this lane's
+        const float send = h ? f0[s % 8] : f1[s % 8];
+        const float recv = __shfl_xor(send, 32, kWave);
+        const float mine = h ? f1[s % 8] : f0[s % 8];
+        op[s][0] = (s / 8 == h) ? mine : recv;
+    }
+}
+
+template <int NS>
+__device__ __forceinline__ void sh_operands(bf16x8 (&op)[NS][2], const float (&sh)[16], int lane) {
+    const int h = lane >> 5;
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = to_bf16(h ? sh[8 + j] : sh[j]);
+    op[0][0] = v;
+    op[0][1] = v;
+}
+
+template <int NS>
+__device__ __forceinline__ void sh_operands(float (&op)[NS][1], const float (&sh)[16], int lane) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) op[s][0] = h ? sh[2 * s + 1] : sh[2 * s];
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
+    __shared__ RenderLds lds_all[4];
+    constexpr int K = NET_HASH_FIELD;
+    constexpr int FS = seg_steps(net_layers(K)[0].s0, T::prec);
+    constexpr int DS = seg_steps(net_layers(K)[4].s1, T::prec);
+    constexpr int SB = T::SB;
+    constexpr int M = 32 * SB;
+
+    const int wave = threadIdx.x / kWave;
+    RenderLds& S = lds_all[wave];
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= a.n_rays) return;
+    const int lane = lane_id();
+    const int h = lane >> 5;
+    const uint64_t ray = a.ray_offset + (uint64_t)r;
+    const float o[3] = {a.ro[3 * r], a.ro[3 * r + 1], a.ro[3 * r + 2]};
+    const float d[3] = {a.rd[3 * r], a.rd[3 * r + 1], a.rd[3 * r + 2]};
+    const float near = a.tn[r], far = a.tf[r];
+    const float dn = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    const float lo = a.box_lo, span = __fsub_rn(a.box_hi, a.box_lo);
+
+    typename T::Op shop[DS][SB];
+    {
+        float sh[16];
+        sh16_eval(d[0] / dn, d[1] / dn, d[2] / dn, sh);
+        sh_operands(shop, sh, lane);
+    }
+    const int N = a.n_coarse;
+    for (int blk = 0; blk < N; blk += M) {
+        float u[SB][3];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+            const int s = blk + sb * 32 + (lane & 31);
+            const int sv = s < N ? s : N - 1;
+            const float uj = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)sv, kStreamJitter) : 0.5f;
+            const float z = stratified_z(near, far, sv, N, uj);
+            if (h == 0 && s < N) S.zc[s] = z;
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                u[sb][k] = __fdiv_rn(__fsub_rn(__fadd_rn(o[k], __fmul_rn(z, d[k])), lo), span);
+        }
+        typename T::Op feats[FS][SB];
+        grid_operands(feats, g, u, lane);
+        f32x16 sig[SB], rgb[SB];
+        hash_field_forward<T>(feats, shop, opaque((const char*)a.coarse), sig, rgb, lane);
+        if (lane < 32) {
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                const int s = blk + sb * 32 + lane;
+                if (s < N) S.raw[s] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
+            }
+        }
+    }
+    wave_lds_sync();
+    const CompositeOut c = composite_ray(S.zc, S.raw, N, dn, nullptr, 0.0f);
+    if (a.dbg_z)
+        for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = S.zc[i];
+    if (lane == 0) {
+        const float bg = a.white ? 1.0f - c.acc : 0.0f;
+        a.rgb[3 * r] = c.r + bg;
+        a.rgb[3 * r + 1] = c.g + bg;
+        a.rgb[3 * r + 2] = c.b + bg;
+        a.depth[r] = c.depth;
+        a.acc[r] = c.acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <class T, int KIND>
+static void launch_nerf_t(const RenderArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((k_render_nerf<T, KIND>), dim3((unsigned)((a.n_rays + 3) / 4)), dim3(256), 0, s, a);
+}
+
+void launch_render_nerf(int kind, int bf16, const RenderArgs& a, hipStream_t s) {
+    switch (kind) {
+        case NET_8x256:
+            bf16 ? launch_nerf_t<TBF16, NET_8x256>(a, s) : launch_nerf_t<TF32, NET_8x256>(a, s);
+            break;
+        case NET_4x64:
+            bf16 ? launch_nerf_t<TBF16, NET_4x64>(a, s) : launch_nerf_t<TF32, NET_4x64>(a, s);
+            break;
+        default:
+            break;
+    }
+}
+
+void launch_render_hash(int bf16, const RenderArgs& a, const GridArgs& g, hipStream_t s) {
+    const dim3 grid((unsigned)((a.n_rays + 3) / 4));
+    if (bf16)
+        hipLaunchKernelGGL(k_render_hash<TBF16>, grid, dim3(256), 0, s, a, g);
+    else
+        hipLaunchKernelGGL(k_render_hash<TF32>, grid, dim3(256), 0, s, a, g);
+}
+
+}  // namespace nerf
