@@ -188,6 +188,7 @@ void launch_composite(const float* raw, const float* z, const float* rd, int64_t
 // Standalone inverse-CDF resampling + merge: one wave per ray, per-wave LDS.
 // ===========================================================================
 constexpr int kMaxSamples = 256;
+constexpr int kMlpRing = 8;  // 128 KB weight ring
 
 struct PdfLds {
     double cdf[kMaxSamples];
@@ -253,8 +254,10 @@ __global__ void __launch_bounds__(256) k_mlp(const char* __restrict__ packed, co
     constexpr int DS = seg_steps(LD.s1, T::prec);
     constexpr int M = 32 * T::SB;
     const int lane = lane_id();
-    const int64_t base = (((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave) * M;
-    if (base >= n) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // every wave of the workgroup runs the network (the weight ring is shared);
+    // waves past the end compute on clamped rows and store nothing
+    const int64_t base = ((int64_t)blockIdx.x * 4 + wave) * M;
     const float* xr[T::SB];
     const float* vr[T::SB];
 #pragma unroll
@@ -268,10 +271,11 @@ __global__ void __launch_bounds__(256) k_mlp(const char* __restrict__ packed, co
     row_operands(enc, L0.s0, xr, lane);
     row_operands(denc, LD.s1, vr, lane);
     f32x16 sig[T::SB], rgb[T::SB];
+    LdsStream<T, KIND, kMlpRing> ws(packed, lane, wave);
     if constexpr (KIND == NET_HASH_FIELD)
-        hash_field_forward<T>(enc, denc, packed, sig, rgb, lane);
+        hash_field_forward<T>(enc, denc, ws, packed, sig, rgb, lane);
     else
-        nerf_forward<T, KIND>(enc, denc, packed, sig, rgb, lane);
+        nerf_forward<T, KIND>(enc, denc, ws, packed, sig, rgb, lane);
     if (lane < 32) {
 #pragma unroll
         for (int sb = 0; sb < T::SB; ++sb) {

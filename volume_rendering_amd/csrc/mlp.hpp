@@ -14,6 +14,20 @@
 
 namespace nerf {
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// Calls f(IntC<I>) for I = B..E-1 in order, fully unrolled.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 struct TBF16 {
     static constexpr int prec = PREC_BF16;
     static constexpr int SB = 2;
@@ -32,13 +46,158 @@ struct TF32 {
     }
 };
 
+#define NERF_AS_GLOBAL __attribute__((address_space(1)))
+#define NERF_AS_LDS __attribute__((address_space(3)))
+#define NERF_AS_CONST __attribute__((address_space(4)))
+
+// Compiler-only memory fence: no instruction, but no memory access moves
+// across it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
+// Weight streams.  A network's tiles are consumed strictly in packed order,
+// tile t at byte t*TB of the tile region, and get<t>() is only ever called
+// with compile-time t, in increasing order, once per forward pass.
+// ---------------------------------------------------------------------------
+
+// LdsStream: the 4 waves of a 256-thread workgroup share one ring of NBUF
+// LDS slots of kChunkBytes each.  Chunk k of the tile region is copied
+// global->LDS by direct loads (each wave moves a quarter of it, no VGPRs)
+// into slot k % NBUF, NBUF-1 chunks ahead of its use.  At the first tile of
+// chunk k every wave waits until its own copies of chunk k have landed and
+// its reads of chunk k-1 are done, the workgroup meets at a barrier, and
+// chunk k+NBUF-1 is issued into the slot chunk k-1 used.  Every wave of the
+// workgroup must run the same sequence of forward passes.
+constexpr int kChunkBytes = 16384;
+constexpr int kChunkDma = kChunkBytes / 1024 / 4;  // 1 KB copies per wave per chunk
+
+static __shared__ __attribute__((aligned(1024))) char g_ring0[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring1[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring2[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring3[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring4[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring5[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring6[kChunkBytes];
+static __shared__ __attribute__((aligned(1024))) char g_ring7[kChunkBytes];
+
+template <int S>
+__device__ __forceinline__ char* ring_slot() {
+    static_assert(S >= 0 && S < 8, "ring slot");
+    if constexpr (S == 0) return g_ring0;
+    else if constexpr (S == 1) return g_ring1;
+    else if constexpr (S == 2) return g_ring2;
+    else if constexpr (S == 3) return g_ring3;
+    else if constexpr (S == 4) return g_ring4;
+    else if constexpr (S == 5) return g_ring5;
+    else if constexpr (S == 6) return g_ring6;
+    else return g_ring7;
+}
+
+template <class T, int KIND, int NBUF, int LOOK = 3>
+struct LdsStream {
+    static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
+    using Op = typename T::Op;
+    static constexpr int TB = tile_bytes(T::prec);
+    static constexpr size_t BYTES = net_tiles_bytes(KIND, T::prec);
+    static constexpr int NT = (int)(BYTES / TB);               // tiles
+    static constexpr int NKB = (int)((BYTES + 1023) / 1024);  // 1 KB blocks in the tile region
+    static constexpr int NCH = (int)((BYTES + kChunkBytes - 1) / kChunkBytes);
+    const char* base;
+    int lane, wave;
+    Op buf[LOOK];  // tiles t..t+LOOK-1, read ahead of use
+
+    __device__ __forceinline__ LdsStream(const char* packed, int lane_, int wave_)
+        : base(packed), lane(lane_), wave(wave_) {}
+
+    template <int K>
+    __device__ __forceinline__ void issue() {
+        if constexpr (K < NCH) {
+            char* slot = ring_slot<K % NBUF>();
+#pragma unroll
+            for (int i = 0; i < kChunkDma; ++i) {
+                const int kb = wave * kChunkDma + i;  // 1 KB block of this chunk
+                int g = K * (kChunkBytes / 1024) + kb;
+                g = g < NKB ? g : NKB - 1;  // past the end: repeat the last block (never read)
+                const char* src = base + (size_t)g * 1024 + lane * 16;
+                __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)src, (NERF_AS_LDS void*)(slot + kb * 1024),
+                                                 16, 0, 0);
+            }
+        }
+    }
+
+    template <int K>
+    __device__ __forceinline__ void boundary() {
+        constexpr int ahead = (NCH - 1 - K) < (NBUF - 2) ? (NCH - 1 - K) : (NBUF - 2);
+        wait_vm_lgkm0<ahead * kChunkDma>();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        issue<K + NBUF - 1>();
+    }
+
+    template <int TILE>
+    __device__ __forceinline__ Op read() {
+        constexpr int off = TILE * TB;
+        constexpr int K = off / kChunkBytes;
+        if constexpr (off % kChunkBytes == 0) boundary<K>();
+        const char* p = ring_slot<K % NBUF>() + (off % kChunkBytes) + lane * (int)sizeof(Op);
+        return *reinterpret_cast<const Op*>(p);
+    }
+
+    // Start of a forward pass: every wave is done with the previous pass's
+    // slots and has no vector memory operation in flight; issue the first
+    // NBUF-1 chunks and read the first LOOK tiles.
+    __device__ __forceinline__ void begin() {
+        wait_all();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        static_for<0, NBUF - 1>([&](auto k) { issue<k.value>(); });
+        static_for<0, LOOK>([&](auto t) {
+            if constexpr (t.value < NT) buf[t.value] = read<t.value>();
+        });
+    }
+
+    template <int TILE>
+    __device__ __forceinline__ Op get() {
+        const Op cur = buf[TILE % LOOK];
+        if constexpr (TILE + LOOK < NT) buf[TILE % LOOK] = read<TILE + LOOK>();
+        return cur;
+    }
+};
+
+// GlobalStream: each wave reads its tiles straight from global memory (for
+// waves that evaluate different networks).
+template <class T, int KIND>
+struct GlobalStream {
+    static constexpr int TB = tile_bytes(T::prec);
+    const char* base;
+    int lane;
+    __device__ __forceinline__ GlobalStream(const char* packed, int lane_, int) : base(packed), lane(lane_) {}
+    __device__ __forceinline__ void begin() {}
+    template <int TILE>
+    __device__ __forceinline__ typename T::Op get() {
+        const NERF_AS_GLOBAL char* p = (const NERF_AS_GLOBAL char*)base + TILE * TB + lane * (int)sizeof(typename T::Op);
+        return *reinterpret_cast<const NERF_AS_GLOBAL typename T::Op*>(p);
+    }
+};
+
 template <class T, int KIND, int LAYER>
 struct LayerInfo {
     static constexpr Layer L = net_layers(KIND)[LAYER];
     static constexpr int S1 = seg_steps(L.s0, T::prec);
     static constexpr int S2 = seg_steps(L.s1, T::prec);
     static constexpr int OB = out_blocks(L.n_out);
-    static constexpr size_t tiles = net_tile_offset(KIND, T::prec, LAYER);
+    static constexpr int tile0 = (int)(net_tile_offset(KIND, T::prec, LAYER) / tile_bytes(T::prec));
     static constexpr size_t bias = net_bias_offset(KIND, T::prec, LAYER);
 };
 
@@ -48,35 +207,48 @@ constexpr int out_steps() {
     return seg_steps(Seg{SEG_HIDDEN, net_layers(KIND)[LAYER].n_out, 0}, T::prec);
 }
 
-__device__ __forceinline__ f32x16 load_bias16(const float* __restrict__ bias, int ob, int h) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(bias) + (ob * 2 + h) * 4;
-    const f32x4 a = p[0], b = p[1], c = p[2], d = p[3];
-    typedef float f32x8 __attribute__((ext_vector_type(8)));
-    const f32x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    const f32x8 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+// Bias of output block ob for this lane's half, read with scalar loads (both
+// halves' 32 values are wave-uniform) and selected per lane.
+__device__ __forceinline__ f32x16 load_bias16(const char* packed, size_t off, int ob, int h) {
+    const NERF_AS_CONST f32x16* p = (const NERF_AS_CONST f32x16*)(packed + off) + 2 * ob;
+    const f32x16 b0 = p[0], b1 = p[1];
+    return h ? b1 : b0;
 }
 
-template <class T, int S1, int S2, class In1, class In2>
-__device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const In1& in1, const In2& in2,
-                                          const typename T::Op* __restrict__ t, int lane) {
+template <class T, int TILE0, int S1, int S2, class In1, class In2, class WS>
+__device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const In1& in1, const In2& in2, WS& ws) {
+    static_for<0, S1>([&](auto s) {
+        const typename T::Op a = ws.template get<TILE0 + s.value>();
 #pragma unroll
-    for (int s = 0; s < S1; ++s) {
-        const typename T::Op a = t[s * kWave + lane];
+        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in1[s.value][sb], acc[sb]);
+    });
+    static_for<0, S2>([&](auto s) {
+        const typename T::Op a = ws.template get<TILE0 + S1 + s.value>();
 #pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in1[s][sb], acc[sb]);
-    }
-#pragma unroll
-    for (int s = 0; s < S2; ++s) {
-        const typename T::Op a = t[(S1 + s) * kWave + lane];
-#pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in2[s][sb], acc[sb]);
-    }
+        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in2[s.value][sb], acc[sb]);
+    });
 }
 
+// ReLU on the bit pattern: negative floats are negative integers, so one
+// integer max clamps them to +0.
 template <bool RELU>
 __device__ __forceinline__ float act(float v) {
-    return RELU ? fmaxf(v, 0.0f) : v;
+    if constexpr (RELU) {
+        return __builtin_bit_cast(float, max(__builtin_bit_cast(int, v), 0));
+    } else {
+        return v;
+    }
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Places a bf16x8 operand in accumulation registers: matrix instructions
+// read their A/B operands from them directly, which leaves the
+// architectural registers to the weight tiles in flight and the epilogue.
+__device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
+    i32x4 bits = __builtin_bit_cast(i32x4, v);
+    asm volatile("" : "+a"(bits));
+    return __builtin_bit_cast(bf16x8, bits);
 }
 
 template <bool RELU, class Out>
@@ -88,7 +260,7 @@ __device__ __forceinline__ void store_hidden(TBF16, const f32x16 (&acc)[2], Out&
             bf16x8 v;
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = to_bf16(act<RELU>(acc[sb][8 * q + j]));
-            out[2 * ob + q][sb] = v;
+            out[2 * ob + q][sb] = to_agpr(v);
         }
 }
 
@@ -99,36 +271,32 @@ __device__ __forceinline__ void store_hidden(TF32, const f32x16 (&acc)[1], Out& 
 }
 
 // A hidden layer: out = act(W [in1, in2] + b), kept as next-layer operands.
-template <class T, int KIND, int LAYER, class In1, class In2, class Out>
-__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, const char* __restrict__ packed,
+template <class T, int KIND, int LAYER, class In1, class In2, class Out, class WS>
+__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws, const char* packed,
                                             int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
-    const typename T::Op* tiles = reinterpret_cast<const typename T::Op*>(packed + I::tiles);
-    const float* bias = reinterpret_cast<const float*>(packed + I::bias);
     const int h = lane >> 5;
-#pragma unroll
-    for (int ob = 0; ob < I::OB; ++ob) {
-        const f32x16 b = load_bias16(bias, ob, h);
+    static_for<0, I::OB>([&](auto obc) {
+        constexpr int ob = obc.value;
+        const f32x16 b = load_bias16(packed, I::bias, ob, h);
         f32x16 acc[T::SB];
 #pragma unroll
         for (int sb = 0; sb < T::SB; ++sb) acc[sb] = b;
-        mma_block<T, I::S1, I::S2>(acc, in1, in2, tiles + (size_t)ob * (I::S1 + I::S2) * kWave, lane);
+        mma_block<T, I::tile0 + ob * (I::S1 + I::S2), I::S1, I::S2>(acc, in1, in2, ws);
         store_hidden<I::L.relu != 0>(T{}, acc, out, ob);
-    }
+    });
 }
 
 // A head (one output block, no activation): raw accumulators.
-template <class T, int KIND, int LAYER, class In1, class In2>
-__device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB],
-                                           const char* __restrict__ packed, int lane) {
+template <class T, int KIND, int LAYER, class In1, class In2, class WS>
+__device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB], WS& ws,
+                                           const char* packed, int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
     static_assert(I::OB == 1, "head layers have one output block");
-    const typename T::Op* tiles = reinterpret_cast<const typename T::Op*>(packed + I::tiles);
-    const float* bias = reinterpret_cast<const float*>(packed + I::bias);
-    const f32x16 b = load_bias16(bias, 0, lane >> 5);
+    const f32x16 b = load_bias16(packed, I::bias, 0, lane >> 5);
 #pragma unroll
     for (int sb = 0; sb < T::SB; ++sb) acc[sb] = b;
-    mma_block<T, I::S1, I::S2>(acc, in1, in2, tiles, lane);
+    mma_block<T, I::tile0, I::S1, I::S2>(acc, in1, in2, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -142,52 +310,54 @@ struct NerfFamily {
     static constexpr int LDIR = net_layers(KIND)[D + 2].s1.L;
 };
 
-template <class T, int KIND, int I, int D, class H, class E>
-__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, const char* __restrict__ packed, int lane) {
+template <class T, int KIND, int I, int D, class H, class E, class WS>
+__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, const char* packed, int lane) {
     if constexpr (I < D) {
-        dense_layer<T, KIND, I>(cur, enc, nxt, packed, lane);  // enc is read only by a skip layer (S2 > 0)
-        hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, packed, lane);
+        dense_layer<T, KIND, I>(cur, enc, nxt, ws, packed, lane);  // enc is read only by a skip layer (S2 > 0)
+        hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, packed, lane);
     }
 }
 
 // enc: position-encoding operands; denc: direction-encoding operands.
 // sig[sb] accumulator 0 and rgb[sb] accumulators 0..2 of lanes 0..31 hold the
 // outputs of sample (sb*32 + lane).
-template <class T, int KIND, class E, class DE>
-__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, const char* __restrict__ packed,
+template <class T, int KIND, class E, class DE, class WS>
+__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& ws, const char* packed,
                                              f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
     using Fam = NerfFamily<KIND>;
     constexpr int D = Fam::D;
     constexpr int HS = out_steps<T, KIND, 0>();
     constexpr int GS = out_steps<T, KIND, D + 2>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
-    dense_layer<T, KIND, 0>(enc, enc, hA, packed, lane);
-    hidden_chain<T, KIND, 1, D>(hA, hB, enc, packed, lane);
+    ws.begin();
+    dense_layer<T, KIND, 0>(enc, enc, hA, ws, packed, lane);
+    hidden_chain<T, KIND, 1, D>(hA, hB, enc, ws, packed, lane);
     // the last hidden layer (index D-1) wrote hB when D-1 is odd, else hA
     auto& hl = ((D - 1) % 2 == 1) ? hB : hA;
     auto& hf = ((D - 1) % 2 == 1) ? hA : hB;
-    dense_head<T, KIND, D>(hl, hl, sig, packed, lane);
-    dense_layer<T, KIND, D + 1>(hl, hl, hf, packed, lane);
+    dense_head<T, KIND, D>(hl, hl, sig, ws, packed, lane);
+    dense_layer<T, KIND, D + 1>(hl, hl, hf, ws, packed, lane);
     typename T::Op g[GS][T::SB];
-    dense_layer<T, KIND, D + 2>(hf, denc, g, packed, lane);
-    dense_head<T, KIND, D + 3>(g, g, rgb, packed, lane);
+    dense_layer<T, KIND, D + 2>(hf, denc, g, ws, packed, lane);
+    dense_head<T, KIND, D + 3>(g, g, rgb, ws, packed, lane);
 }
 
 // Hash-grid field: density 0, 1; density head 2; feature 3; colour 4 (with
 // harmonics), 5; rgb head 6.
-template <class T, class FE, class DE>
-__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, const char* __restrict__ packed,
+template <class T, class FE, class DE, class WS>
+__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, WS& ws, const char* packed,
                                                    f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
     constexpr int K = NET_HASH_FIELD;
     constexpr int HS = out_steps<T, K, 0>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
-    dense_layer<T, K, 0>(feats, feats, hA, packed, lane);
-    dense_layer<T, K, 1>(hA, hA, hB, packed, lane);
-    dense_head<T, K, 2>(hB, hB, sig, packed, lane);
-    dense_layer<T, K, 3>(hB, hB, hA, packed, lane);
-    dense_layer<T, K, 4>(hA, sh, hB, packed, lane);
-    dense_layer<T, K, 5>(hB, hB, hA, packed, lane);
-    dense_head<T, K, 6>(hA, hA, rgb, packed, lane);
+    ws.begin();
+    dense_layer<T, K, 0>(feats, feats, hA, ws, packed, lane);
+    dense_layer<T, K, 1>(hA, hA, hB, ws, packed, lane);
+    dense_head<T, K, 2>(hB, hB, sig, ws, packed, lane);
+    dense_layer<T, K, 3>(hB, hB, hA, ws, packed, lane);
+    dense_layer<T, K, 4>(hA, sh, hB, ws, packed, lane);
+    dense_layer<T, K, 5>(hB, hB, hA, ws, packed, lane);
+    dense_head<T, K, 6>(hA, hA, rgb, ws, packed, lane);
 }
 
 // ---------------------------------------------------------------------------

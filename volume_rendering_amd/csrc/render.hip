@@ -21,6 +21,7 @@
 namespace nerf {
 
 constexpr int kMaxRaySamples = 256;
+constexpr int kRenderRing = 6;  // 96 KB weight ring next to 40 KB of per-wave state
 
 struct RenderLds {
     float zc[kMaxRaySamples];  // first-pass samples, then the fine samples (union for the merge)
@@ -42,10 +43,13 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
     constexpr int SB = T::SB;
     constexpr int M = 32 * SB;
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     RenderLds& S = lds_all[wave];
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r >= a.n_rays) return;
+    // every wave runs the same passes (the weight ring is shared); a wave past
+    // the last ray renders the last ray again and stores nothing
+    const int64_t r0 = (int64_t)blockIdx.x * 4 + wave;
+    const bool live = r0 < a.n_rays;
+    const int64_t r = live ? r0 : a.n_rays - 1;
     const int lane = lane_id();
     const int h = lane >> 5;
     const uint64_t ray = a.ray_offset + (uint64_t)r;
@@ -90,7 +94,9 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
             typename T::Op enc[ES][SB];
             enc_operands(enc, Fam::LPOS, x, a.use_pi != 0, lane);
             f32x16 sig[SB], rgb[SB];
-            nerf_forward<T, KIND>(enc, denc, opaque(packed), sig, rgb, lane);
+            const char* pk = opaque(packed);
+            LdsStream<T, KIND, kRenderRing> ws(pk, lane, wave);
+            nerf_forward<T, KIND>(enc, denc, ws, pk, sig, rgb, lane);
             if (lane < 32) {
 #pragma unroll
                 for (int sb = 0; sb < SB; ++sb) {
@@ -103,12 +109,12 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
         const float* zp = pass ? S.z2 : S.zc;
         const CompositeOut c = composite_ray(zp, S.raw, N, dn, pass == 0 ? S.w : nullptr, 0.0f);
         wave_lds_sync();
-        if (pass == 0 && a.dbg_w)
+        if (pass == 0 && a.dbg_w && live)
             for (int i = lane; i < nc; i += kWave) a.dbg_w[r * nc + i] = S.w[i];
         if (pass == npass - 1) {
-            if (a.dbg_z)
+            if (a.dbg_z && live)
                 for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = zp[i];
-            if (lane == 0) {
+            if (lane == 0 && live) {
                 const float bg = a.white ? 1.0f - c.acc : 0.0f;
                 a.rgb[3 * r] = c.r + bg;
                 a.rgb[3 * r + 1] = c.g + bg;
@@ -191,10 +197,11 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
     constexpr int SB = T::SB;
     constexpr int M = 32 * SB;
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     RenderLds& S = lds_all[wave];
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r >= a.n_rays) return;
+    const int64_t r0 = (int64_t)blockIdx.x * 4 + wave;
+    const bool live = r0 < a.n_rays;
+    const int64_t r = live ? r0 : a.n_rays - 1;
     const int lane = lane_id();
     const int h = lane >> 5;
     const uint64_t ray = a.ray_offset + (uint64_t)r;
@@ -227,7 +234,9 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         typename T::Op feats[FS][SB];
         grid_operands(feats, g, u, lane);
         f32x16 sig[SB], rgb[SB];
-        hash_field_forward<T>(feats, shop, opaque((const char*)a.coarse), sig, rgb, lane);
+        const char* pk = opaque((const char*)a.coarse);
+        LdsStream<T, NET_HASH_FIELD, kRenderRing> ws(pk, lane, wave);
+        hash_field_forward<T>(feats, shop, ws, pk, sig, rgb, lane);
         if (lane < 32) {
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb) {
@@ -238,9 +247,9 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
     }
     wave_lds_sync();
     const CompositeOut c = composite_ray(S.zc, S.raw, N, dn, nullptr, 0.0f);
-    if (a.dbg_z)
+    if (a.dbg_z && live)
         for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = S.zc[i];
-    if (lane == 0) {
+    if (lane == 0 && live) {
         const float bg = a.white ? 1.0f - c.acc : 0.0f;
         a.rgb[3 * r] = c.r + bg;
         a.rgb[3 * r + 1] = c.g + bg;
