@@ -270,12 +270,16 @@ __global__ void __launch_bounds__(256) k_mlp(const char* __restrict__ packed, co
     typename T::Op enc[ES][T::SB], denc[DS][T::SB];
     row_operands(enc, L0.s0, xr, lane);
     row_operands(denc, LD.s1, vr, lane);
+    __shared__ __attribute__((aligned(16))) float bias_lds[BiasRegion<KIND, T::prec>::floats];
+    bias_to_lds<KIND, T::prec>((NERF_AS_LDS float*)bias_lds, packed, threadIdx.x, blockDim.x);
+    __syncthreads();
+    const NERF_AS_LDS float* bias = (const NERF_AS_LDS float*)bias_lds;
     f32x16 sig[T::SB], rgb[T::SB];
     LdsStream<T, KIND, kMlpRing> ws(packed, lane, wave);
     if constexpr (KIND == NET_HASH_FIELD)
-        hash_field_forward<T>(enc, denc, ws, packed, sig, rgb, lane);
+        hash_field_forward<T>(enc, denc, ws, bias, sig, rgb, lane);
     else
-        nerf_forward<T, KIND>(enc, denc, ws, packed, sig, rgb, lane);
+        nerf_forward<T, KIND>(enc, denc, ws, bias, sig, rgb, lane);
     if (lane < 32) {
 #pragma unroll
         for (int sb = 0; sb < T::SB; ++sb) {

@@ -191,6 +191,33 @@ struct GlobalStream {
     }
 };
 
+// Biases.  A network's bias region (all layers, [ob][half][16] float32) is
+// copied once per workgroup into LDS; a lane reads the 16 biases of its half
+// of an output block with broadcast LDS reads, in order with the tile reads.
+template <int KIND, int PREC>
+struct BiasRegion {
+    static constexpr size_t begin = net_bias_offset(KIND, PREC, 0);
+    static constexpr size_t bytes = net_packed_bytes(KIND, PREC) - begin;
+    static constexpr int floats = (int)(bytes / sizeof(float));
+    template <int LAYER>
+    static constexpr int layer_float() {
+        return (int)((net_bias_offset(KIND, PREC, LAYER) - begin) / sizeof(float));
+    }
+};
+
+// Copies the bias region of a packed network to LDS; every thread of the
+// workgroup takes part; the caller synchronises the workgroup afterwards.
+template <int KIND, int PREC>
+__device__ __forceinline__ void bias_to_lds(NERF_AS_LDS float* dst, const char* packed, int tid, int nthreads) {
+    using BR = BiasRegion<KIND, PREC>;
+    const f32x4* src = reinterpret_cast<const f32x4*>(packed + BR::begin);
+    for (int i = tid; i < BR::floats / 4; i += nthreads) reinterpret_cast<NERF_AS_LDS f32x4*>(dst)[i] = src[i];
+}
+
+__device__ __forceinline__ f32x16 load_bias16(const NERF_AS_LDS float* bias, int layer_float, int ob, int h) {
+    return reinterpret_cast<const NERF_AS_LDS f32x16*>(bias + layer_float)[2 * ob + h];
+}
+
 template <class T, int KIND, int LAYER>
 struct LayerInfo {
     static constexpr Layer L = net_layers(KIND)[LAYER];
@@ -198,7 +225,7 @@ struct LayerInfo {
     static constexpr int S2 = seg_steps(L.s1, T::prec);
     static constexpr int OB = out_blocks(L.n_out);
     static constexpr int tile0 = (int)(net_tile_offset(KIND, T::prec, LAYER) / tile_bytes(T::prec));
-    static constexpr size_t bias = net_bias_offset(KIND, T::prec, LAYER);
+    static constexpr int bias = BiasRegion<KIND, T::prec>::template layer_float<LAYER>();
 };
 
 // Steps of the output of LAYER as an input of the next layer.
@@ -207,27 +234,6 @@ constexpr int out_steps() {
     return seg_steps(Seg{SEG_HIDDEN, net_layers(KIND)[LAYER].n_out, 0}, T::prec);
 }
 
-// Bias of output block ob for this lane's half, read with scalar loads (both
-// halves' 32 values are wave-uniform) and selected per lane.
-__device__ __forceinline__ f32x16 load_bias16(const char* packed, size_t off, int ob, int h) {
-    const NERF_AS_CONST f32x16* p = (const NERF_AS_CONST f32x16*)(packed + off) + 2 * ob;
-    const f32x16 b0 = p[0], b1 = p[1];
-    return h ? b1 : b0;
-}
-
-template <class T, int TILE0, int S1, int S2, class In1, class In2, class WS>
-__device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const In1& in1, const In2& in2, WS& ws) {
-    static_for<0, S1>([&](auto s) {
-        const typename T::Op a = ws.template get<TILE0 + s.value>();
-#pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in1[s.value][sb], acc[sb]);
-    });
-    static_for<0, S2>([&](auto s) {
-        const typename T::Op a = ws.template get<TILE0 + S1 + s.value>();
-#pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = T::mma(a, in2[s.value][sb], acc[sb]);
-    });
-}
 
 // ReLU on the bit pattern: negative floats are negative integers, so one
 // integer max clamps them to +0.
@@ -251,52 +257,82 @@ __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
     return __builtin_bit_cast(bf16x8, bits);
 }
 
-template <bool RELU, class Out>
-__device__ __forceinline__ void store_hidden(TBF16, const f32x16 (&acc)[2], Out& out, int ob) {
+// Epilogue of one output block, cut into pieces so it can run between the
+// matrix instructions of the next block.  bf16: piece p = (sb, q) turns 8
+// accumulators into one operand of the next layer; f32: piece p copies
+// accumulator p.
+template <class T>
+struct Epi;
+template <>
+struct Epi<TBF16> {
+    static constexpr int pieces = 4;
+    template <int P, bool RELU, class Out>
+    __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
+        constexpr int sb = P / 2, q = P % 2;
+        bf16x8 v;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            bf16x8 v;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = to_bf16(act<RELU>(acc[sb][8 * q + j]));
-            out[2 * ob + q][sb] = to_agpr(v);
-        }
-}
+        for (int j = 0; j < 8; ++j) v[j] = to_bf16(act<RELU>(acc[sb][8 * q + j]));
+        out[2 * ob + q][sb] = to_agpr(v);
+    }
+};
+template <>
+struct Epi<TF32> {
+    static constexpr int pieces = 16;
+    template <int P, bool RELU, class Out>
+    __device__ static __forceinline__ void piece(const f32x16 (&acc)[1], Out& out, int ob) {
+        out[16 * ob + P][0] = act<RELU>(acc[0][P]);
+    }
+};
 
-template <bool RELU, class Out>
-__device__ __forceinline__ void store_hidden(TF32, const f32x16 (&acc)[1], Out& out, int ob) {
+// acc = W(ob) [in1, in2] + bias; the bias enters as the C operand of the
+// first step.  After step s, piece s of the previous block's epilogue runs
+// (PREV_OB >= 0), so its vector work overlaps the matrix instructions.
+template <class T, int TILE0, int S1, int S2, bool RELU, int PREV_OB, class In1, class In2, class WS, class Out>
+__device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bias, const In1& in1, const In2& in2,
+                                          WS& ws, const f32x16 (&prev)[T::SB], Out& out) {
+    constexpr int S = S1 + S2;
+    static_for<0, S>([&](auto sc) {
+        constexpr int st = sc.value;
+        const typename T::Op a = ws.template get<TILE0 + st>();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[16 * ob + r][0] = act<RELU>(acc[0][r]);
+        for (int sb = 0; sb < T::SB; ++sb) {
+            const typename T::Op b = st < S1 ? in1[st < S1 ? st : 0][sb] : in2[st >= S1 ? st - S1 : 0][sb];
+            acc[sb] = T::mma(a, b, st == 0 ? bias : acc[sb]);
+        }
+        if constexpr (PREV_OB >= 0 && st < Epi<T>::pieces) Epi<T>::template piece<st, RELU>(prev, out, PREV_OB);
+    });
+    if constexpr (PREV_OB >= 0)
+        static_for<S, Epi<T>::pieces>([&](auto pc) { Epi<T>::template piece<pc.value, RELU>(prev, out, PREV_OB); });
 }
 
 // A hidden layer: out = act(W [in1, in2] + b), kept as next-layer operands.
 template <class T, int KIND, int LAYER, class In1, class In2, class Out, class WS>
-__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws, const char* packed,
-                                            int lane) {
+__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws,
+                                            const NERF_AS_LDS float* bias, int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
+    constexpr bool RELU = I::L.relu != 0;
     const int h = lane >> 5;
+    f32x16 prev[T::SB];
     static_for<0, I::OB>([&](auto obc) {
         constexpr int ob = obc.value;
-        const f32x16 b = load_bias16(packed, I::bias, ob, h);
+        const f32x16 b = load_bias16(bias, I::bias, ob, h);
         f32x16 acc[T::SB];
+        mma_block<T, I::tile0 + ob * (I::S1 + I::S2), I::S1, I::S2, RELU, ob - 1>(acc, b, in1, in2, ws, prev, out);
 #pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) acc[sb] = b;
-        mma_block<T, I::tile0 + ob * (I::S1 + I::S2), I::S1, I::S2>(acc, in1, in2, ws);
-        store_hidden<I::L.relu != 0>(T{}, acc, out, ob);
+        for (int sb = 0; sb < T::SB; ++sb) prev[sb] = acc[sb];
     });
+    static_for<0, Epi<T>::pieces>([&](auto pc) { Epi<T>::template piece<pc.value, RELU>(prev, out, I::OB - 1); });
 }
 
 // A head (one output block, no activation): raw accumulators.
 template <class T, int KIND, int LAYER, class In1, class In2, class WS>
 __device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB], WS& ws,
-                                           const char* packed, int lane) {
+                                           const NERF_AS_LDS float* bias, int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
     static_assert(I::OB == 1, "head layers have one output block");
-    const f32x16 b = load_bias16(packed, I::bias, 0, lane >> 5);
-#pragma unroll
-    for (int sb = 0; sb < T::SB; ++sb) acc[sb] = b;
-    mma_block<T, I::tile0, I::S1, I::S2>(acc, in1, in2, ws);
+    const f32x16 b = load_bias16(bias, I::bias, 0, lane >> 5);
+    f32x16 none[T::SB];
+    mma_block<T, I::tile0, I::S1, I::S2, false, -1>(acc, b, in1, in2, ws, none, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -311,10 +347,11 @@ struct NerfFamily {
 };
 
 template <class T, int KIND, int I, int D, class H, class E, class WS>
-__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, const char* packed, int lane) {
+__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, const NERF_AS_LDS float* bias,
+                                             int lane) {
     if constexpr (I < D) {
-        dense_layer<T, KIND, I>(cur, enc, nxt, ws, packed, lane);  // enc is read only by a skip layer (S2 > 0)
-        hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, packed, lane);
+        dense_layer<T, KIND, I>(cur, enc, nxt, ws, bias, lane);  // enc is read only by a skip layer (S2 > 0)
+        hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, bias, lane);
     }
 }
 
@@ -322,7 +359,7 @@ __device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& w
 // sig[sb] accumulator 0 and rgb[sb] accumulators 0..2 of lanes 0..31 hold the
 // outputs of sample (sb*32 + lane).
 template <class T, int KIND, class E, class DE, class WS>
-__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& ws, const char* packed,
+__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& ws, const NERF_AS_LDS float* bias,
                                              f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
     using Fam = NerfFamily<KIND>;
     constexpr int D = Fam::D;
@@ -330,34 +367,35 @@ __device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& w
     constexpr int GS = out_steps<T, KIND, D + 2>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
     ws.begin();
-    dense_layer<T, KIND, 0>(enc, enc, hA, ws, packed, lane);
-    hidden_chain<T, KIND, 1, D>(hA, hB, enc, ws, packed, lane);
+    dense_layer<T, KIND, 0>(enc, enc, hA, ws, bias, lane);
+    hidden_chain<T, KIND, 1, D>(hA, hB, enc, ws, bias, lane);
     // the last hidden layer (index D-1) wrote hB when D-1 is odd, else hA
     auto& hl = ((D - 1) % 2 == 1) ? hB : hA;
     auto& hf = ((D - 1) % 2 == 1) ? hA : hB;
-    dense_head<T, KIND, D>(hl, hl, sig, ws, packed, lane);
-    dense_layer<T, KIND, D + 1>(hl, hl, hf, ws, packed, lane);
+    dense_head<T, KIND, D>(hl, hl, sig, ws, bias, lane);
+    dense_layer<T, KIND, D + 1>(hl, hl, hf, ws, bias, lane);
     typename T::Op g[GS][T::SB];
-    dense_layer<T, KIND, D + 2>(hf, denc, g, ws, packed, lane);
-    dense_head<T, KIND, D + 3>(g, g, rgb, ws, packed, lane);
+    dense_layer<T, KIND, D + 2>(hf, denc, g, ws, bias, lane);
+    dense_head<T, KIND, D + 3>(g, g, rgb, ws, bias, lane);
 }
 
 // Hash-grid field: density 0, 1; density head 2; feature 3; colour 4 (with
 // harmonics), 5; rgb head 6.
 template <class T, class FE, class DE, class WS>
-__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, WS& ws, const char* packed,
-                                                   f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
+__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, WS& ws,
+                                                   const NERF_AS_LDS float* bias, f32x16 (&sig)[T::SB],
+                                                   f32x16 (&rgb)[T::SB], int lane) {
     constexpr int K = NET_HASH_FIELD;
     constexpr int HS = out_steps<T, K, 0>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
     ws.begin();
-    dense_layer<T, K, 0>(feats, feats, hA, ws, packed, lane);
-    dense_layer<T, K, 1>(hA, hA, hB, ws, packed, lane);
-    dense_head<T, K, 2>(hB, hB, sig, ws, packed, lane);
-    dense_layer<T, K, 3>(hB, hB, hA, ws, packed, lane);
-    dense_layer<T, K, 4>(hA, sh, hB, ws, packed, lane);
-    dense_layer<T, K, 5>(hB, hB, hA, ws, packed, lane);
-    dense_head<T, K, 6>(hA, hA, rgb, ws, packed, lane);
+    dense_layer<T, K, 0>(feats, feats, hA, ws, bias, lane);
+    dense_layer<T, K, 1>(hA, hA, hB, ws, bias, lane);
+    dense_head<T, K, 2>(hB, hB, sig, ws, bias, lane);
+    dense_layer<T, K, 3>(hB, hB, hA, ws, bias, lane);
+    dense_layer<T, K, 4>(hA, sh, hB, ws, bias, lane);
+    dense_layer<T, K, 5>(hB, hB, hA, ws, bias, lane);
+    dense_head<T, K, 6>(hA, hA, rgb, ws, bias, lane);
 }
 
 // ---------------------------------------------------------------------------

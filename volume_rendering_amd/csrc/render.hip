@@ -71,6 +71,12 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
 
     const int nc = a.n_coarse, nf = a.n_fine;
     const int npass = nf > 0 ? 2 : 1;
+    constexpr int NBF = BiasRegion<KIND, T::prec>::floats;
+    __shared__ __attribute__((aligned(16))) float bias_lds[2][NBF];
+    bias_to_lds<KIND, T::prec>((NERF_AS_LDS float*)bias_lds[0], (const char*)a.coarse, threadIdx.x, blockDim.x);
+    if (npass == 2)
+        bias_to_lds<KIND, T::prec>((NERF_AS_LDS float*)bias_lds[1], (const char*)a.fine, threadIdx.x, blockDim.x);
+    __syncthreads();
     for (int pass = 0; pass < npass; ++pass) {
         const int N = pass ? nc + nf : nc;
         const char* packed = pass ? (const char*)a.fine : (const char*)a.coarse;
@@ -96,7 +102,7 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
             f32x16 sig[SB], rgb[SB];
             const char* pk = opaque(packed);
             LdsStream<T, KIND, kRenderRing> ws(pk, lane, wave);
-            nerf_forward<T, KIND>(enc, denc, ws, pk, sig, rgb, lane);
+            nerf_forward<T, KIND>(enc, denc, ws, (const NERF_AS_LDS float*)bias_lds[pass], sig, rgb, lane);
             if (lane < 32) {
 #pragma unroll
                 for (int sb = 0; sb < SB; ++sb) {
@@ -217,6 +223,9 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         sh16_eval(d[0] / dn, d[1] / dn, d[2] / dn, sh);
         sh_operands(shop, sh, lane);
     }
+    __shared__ __attribute__((aligned(16))) float bias_lds[BiasRegion<NET_HASH_FIELD, T::prec>::floats];
+    bias_to_lds<NET_HASH_FIELD, T::prec>((NERF_AS_LDS float*)bias_lds, (const char*)a.coarse, threadIdx.x, blockDim.x);
+    __syncthreads();
     const int N = a.n_coarse;
     for (int blk = 0; blk < N; blk += M) {
         float u[SB][3];
@@ -236,7 +245,7 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         f32x16 sig[SB], rgb[SB];
         const char* pk = opaque((const char*)a.coarse);
         LdsStream<T, NET_HASH_FIELD, kRenderRing> ws(pk, lane, wave);
-        hash_field_forward<T>(feats, shop, ws, pk, sig, rgb, lane);
+        hash_field_forward<T>(feats, shop, ws, (const NERF_AS_LDS float*)bias_lds, sig, rgb, lane);
         if (lane < 32) {
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb) {
