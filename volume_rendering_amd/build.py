@@ -26,7 +26,10 @@ SOURCES = ["kernels.hip", "render.hip", "kilo.hip", "abi.cpp", "pack.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-function"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# matrix-instruction accumulators in architectural VGPRs (operands stay in
+# AGPRs where the kernels place them), so epilogues read results directly
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

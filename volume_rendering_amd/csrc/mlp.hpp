@@ -77,7 +77,10 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // its reads of chunk k-1 are done, the workgroup meets at a barrier, and
 // chunk k+NBUF-1 is issued into the slot chunk k-1 used.  Every wave of the
 // workgroup must run the same sequence of forward passes.
-constexpr int kChunkBytes = 16384;
+#ifndef NERF_CHUNK_KB
+#define NERF_CHUNK_KB 16
+#endif
+constexpr int kChunkBytes = NERF_CHUNK_KB * 1024;
 constexpr int kChunkDma = kChunkBytes / 1024 / 4;  // 1 KB copies per wave per chunk
 
 static __shared__ __attribute__((aligned(1024))) char g_ring0[kChunkBytes];
@@ -102,7 +105,10 @@ __device__ __forceinline__ char* ring_slot() {
     else return g_ring7;
 }
 
-template <class T, int KIND, int NBUF, int LOOK = 3>
+#ifndef NERF_LOOK
+#define NERF_LOOK 3
+#endif
+template <class T, int KIND, int NBUF, int LOOK = NERF_LOOK>
 struct LdsStream {
     static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
     using Op = typename T::Op;
@@ -263,17 +269,52 @@ __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
 // accumulator p.
 template <class T>
 struct Epi;
+#ifndef NERF_EPI16
+#define NERF_EPI16 0
+#endif
 template <>
 struct Epi<TBF16> {
+#if NERF_EPI16
+    // piece p writes 32-bit register c of operand (sb, q) of the next layer:
+    // two accumulators rounded to bf16 and packed, then ReLU as a packed
+    // 16-bit integer max (negative bf16 values are negative int16)
+    static constexpr int pieces = 16;
+    template <int P, bool RELU, class Out>
+    __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
+        constexpr int sb = P / 8, q = (P / 4) % 2, c = P % 4;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef short i16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 f = {acc[sb][8 * q + 2 * c], acc[sb][8 * q + 2 * c + 1]};
+        const bf16x2 v = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32
+        i16x2 w = __builtin_bit_cast(i16x2, v);
+        if constexpr (RELU) w = __builtin_elementwise_max(w, i16x2{0, 0});
+        int bits = __builtin_bit_cast(int, w);
+        asm volatile("" : "+a"(bits));
+        i32x4 t = __builtin_bit_cast(i32x4, out[2 * ob + q][sb]);
+        t[c] = bits;
+        out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
+    }
+#else
     static constexpr int pieces = 4;
     template <int P, bool RELU, class Out>
     __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
         constexpr int sb = P / 2, q = P % 2;
-        bf16x8 v;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef short i16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        i32x4 t;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = to_bf16(act<RELU>(acc[sb][8 * q + j]));
-        out[2 * ob + q][sb] = to_agpr(v);
+        for (int c = 0; c < 4; ++c) {
+            const f32x2 f = {acc[sb][8 * q + 2 * c], acc[sb][8 * q + 2 * c + 1]};
+            i16x2 w = __builtin_bit_cast(i16x2, __builtin_convertvector(f, bf16x2));
+            if constexpr (RELU) w = __builtin_elementwise_max(w, i16x2{0, 0});
+            t[c] = __builtin_bit_cast(int, w);
+        }
+        asm volatile("" : "+a"(t));
+        out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
     }
+#endif
 };
 template <>
 struct Epi<TF32> {

@@ -21,7 +21,10 @@
 namespace nerf {
 
 constexpr int kMaxRaySamples = 256;
-constexpr int kRenderRing = 6;  // 96 KB weight ring next to 40 KB of per-wave state
+#ifndef NERF_RENDER_RING
+#define NERF_RENDER_RING 6
+#endif
+constexpr int kRenderRing = NERF_RENDER_RING;  // weight ring slots next to 40 KB of per-wave state
 
 struct RenderLds {
     float zc[kMaxRaySamples];  // first-pass samples, then the fine samples (union for the merge)
