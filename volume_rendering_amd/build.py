@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libnerf_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "render.hip", "kilo.hip", "abi.cpp", "pack.cpp"]
+SOURCES = ["render_nerf_bf16.hip", "render_nerf_f32.hip", "render_hash.hip", "mlp_bf16.hip", "mlp_f32.hip",
+           "kernels.hip", "kilo.hip", "abi.cpp", "pack.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-function"]

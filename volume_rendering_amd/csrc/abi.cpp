@@ -184,7 +184,10 @@ nerf_status nerf_mlp(const nerf_mlp_desc* net, const void* packed, const float* 
     NERF_REQUIRE(packed && enc_x && enc_v && raw, "nerf_mlp: NULL argument");
     NERF_REQUIRE(aligned16(packed) && aligned16(raw), "nerf_mlp: packed weights and raw must be 16-byte aligned");
     clear_pending();
-    launch_mlp(net->kind, net->dtype == NERF_BF16, packed, enc_x, enc_v, n, samples_per_ray, raw, as_stream(stream));
+    if (net->dtype == NERF_BF16)
+        launch_mlp_bf16(net->kind, packed, enc_x, enc_v, n, samples_per_ray, raw, as_stream(stream));
+    else
+        launch_mlp_f32(net->kind, packed, enc_x, enc_v, n, samples_per_ray, raw, as_stream(stream));
     return check_launch("nerf_mlp");
 }
 

@@ -48,9 +48,13 @@ void launch_composite(const float* raw, const float* z, const float* rd, int64_t
                       float* depth, float* acc, float* w, hipStream_t s);
 void launch_sample_pdf(const float* zc, const float* wc, int64_t n_rays, int nc, int nf, uint64_t seed,
                        uint64_t ray_offset, float* zf, int32_t* bins, float* z2, hipStream_t s);
-void launch_mlp(int kind, int bf16, const void* packed, const float* ex, const float* ev, int64_t n, int spr,
-                float* raw, hipStream_t s);
 void launch_render_nerf(int kind, int bf16, const RenderArgs& a, hipStream_t s);
+void launch_render_nerf_bf16(int kind, const RenderArgs& a, hipStream_t s);
+void launch_render_nerf_f32(int kind, const RenderArgs& a, hipStream_t s);
+void launch_mlp_bf16(int kind, const void* packed, const float* ex, const float* ev, int64_t n, int spr, float* raw,
+                     hipStream_t s);
+void launch_mlp_f32(int kind, const void* packed, const float* ex, const float* ev, int64_t n, int spr, float* raw,
+                    hipStream_t s);
 void launch_render_hash(int bf16, const RenderArgs& a, const GridArgs& g, hipStream_t s);
 
 }  // namespace nerf

@@ -81,6 +81,7 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 #define NERF_CHUNK_KB 16
 #endif
 constexpr int kChunkBytes = NERF_CHUNK_KB * 1024;
+static_assert(kTileRegionAlign % kChunkBytes == 0, "chunks tile the padded weight region");
 constexpr int kChunkDma = kChunkBytes / 1024 / 4;  // 1 KB copies per wave per chunk
 
 static __shared__ __attribute__((aligned(1024))) char g_ring0[kChunkBytes];
@@ -105,6 +106,9 @@ __device__ __forceinline__ char* ring_slot() {
     else return g_ring7;
 }
 
+#ifndef NERF_SCHED_MASK
+#define NERF_SCHED_MASK 0  // nothing crosses a step boundary
+#endif
 #ifndef NERF_LOOK
 #define NERF_LOOK 3
 #endif
@@ -115,28 +119,25 @@ struct LdsStream {
     static constexpr int TB = tile_bytes(T::prec);
     static constexpr size_t BYTES = net_tiles_bytes(KIND, T::prec);
     static constexpr int NT = (int)(BYTES / TB);               // tiles
-    static constexpr int NKB = (int)((BYTES + 1023) / 1024);  // 1 KB blocks in the tile region
     static constexpr int NCH = (int)((BYTES + kChunkBytes - 1) / kChunkBytes);
-    const char* base;
-    int lane, wave;
-    Op buf[LOOK];  // tiles t..t+LOOK-1, read ahead of use
+    const char* src;  // this wave's first byte of chunk 0
+    int dst;          // this wave's byte offset within a slot
+    int lane;
+    Op buf[LOOK];     // tiles t..t+LOOK-1, read ahead of use
 
-    __device__ __forceinline__ LdsStream(const char* packed, int lane_, int wave_)
-        : base(packed), lane(lane_), wave(wave_) {}
+    // Each wave copies kChunkDma consecutive kilobytes of every chunk.
+    __device__ __forceinline__ LdsStream(const char* packed, int lane_, int wave)
+        : src(packed + wave * (kChunkDma * 1024) + lane_ * 16), dst(wave * (kChunkDma * 1024)), lane(lane_) {}
 
     template <int K>
     __device__ __forceinline__ void issue() {
         if constexpr (K < NCH) {
-            char* slot = ring_slot<K % NBUF>();
+            const char* p = src + (size_t)K * kChunkBytes;  // within the padded region
+            char* slot = ring_slot<K % NBUF>() + dst;
 #pragma unroll
-            for (int i = 0; i < kChunkDma; ++i) {
-                const int kb = wave * kChunkDma + i;  // 1 KB block of this chunk
-                int g = K * (kChunkBytes / 1024) + kb;
-                g = g < NKB ? g : NKB - 1;  // past the end: repeat the last block (never read)
-                const char* src = base + (size_t)g * 1024 + lane * 16;
-                __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)src, (NERF_AS_LDS void*)(slot + kb * 1024),
-                                                 16, 0, 0);
-            }
+            for (int i = 0; i < kChunkDma; ++i)
+                __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)(p + i * 1024),
+                                                 (NERF_AS_LDS void*)(slot + i * 1024), 16, 0, 0);
         }
     }
 
@@ -341,6 +342,11 @@ __device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bi
             acc[sb] = T::mma(a, b, st == 0 ? bias : acc[sb]);
         }
         if constexpr (PREV_OB >= 0 && st < Epi<T>::pieces) Epi<T>::template piece<st, RELU>(prev, out, PREV_OB);
+#if NERF_SCHED_MASK >= 0
+        // each step keeps its own tile read, matrix instructions and epilogue
+        // piece, so the read-ahead distance survives scheduling
+        __builtin_amdgcn_sched_barrier(NERF_SCHED_MASK);
+#endif
     });
     if constexpr (PREV_OB >= 0)
         static_for<S, Epi<T>::pieces>([&](auto pc) { Epi<T>::template piece<pc.value, RELU>(prev, out, PREV_OB); });

@@ -24,7 +24,7 @@
 // (sin, cos)(pi 2^(P/3) x[P%3]); pair 3L is (x, y); pair 3L+1 is (z, 0).
 //
 // Packed buffer: all A tiles (layer order; within a layer output block
-// major, k-step minor; 64 operands per tile), padding to a 1 KB boundary,
+// major, k-step minor; 64 operands per tile), zero padding to a 16 KB boundary,
 // then all biases (layer order; [ob][half][16] float32 in accumulator
 // order).
 #pragma once
@@ -120,10 +120,14 @@ NERF_HD constexpr size_t net_tile_offset(int kind, int prec, int layer) {
 NERF_HD constexpr size_t net_tiles_bytes(int kind, int prec) {
     return net_tile_offset(kind, prec, net_n_layers(kind));
 }
-// Biases start on a 1 KB boundary after the tiles, so whole-kilobyte copies
-// of the tile region never run past the buffer.
+// The tile region is padded to a whole number of 16 KB chunks (the unit in
+// which kernels copy weights into LDS), so chunk copies never run past it.
+constexpr size_t kTileRegionAlign = 16384;
+NERF_HD constexpr size_t net_tiles_padded(int kind, int prec) {
+    return (net_tiles_bytes(kind, prec) + kTileRegionAlign - 1) / kTileRegionAlign * kTileRegionAlign;
+}
 NERF_HD constexpr size_t net_bias_offset(int kind, int prec, int layer) {
-    size_t off = (net_tiles_bytes(kind, prec) + 1023) / 1024 * 1024;
+    size_t off = net_tiles_padded(kind, prec);
     for (int i = 0; i < layer; ++i) off += (size_t)out_blocks(net_layers(kind)[i].n_out) * 32 * sizeof(float);
     return off;
 }

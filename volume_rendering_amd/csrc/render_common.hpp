@@ -11,6 +11,8 @@
 //
 // Hash mode: stratified samples -> hash-grid features and harmonics ->
 // field network -> compositing.
+#pragma once
+
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -269,35 +271,6 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         a.depth[r] = c.depth;
         a.acc[r] = c.acc;
     }
-}
-
-// ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
-template <class T, int KIND>
-static void launch_nerf_t(const RenderArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((k_render_nerf<T, KIND>), dim3((unsigned)((a.n_rays + 3) / 4)), dim3(256), 0, s, a);
-}
-
-void launch_render_nerf(int kind, int bf16, const RenderArgs& a, hipStream_t s) {
-    switch (kind) {
-        case NET_8x256:
-            bf16 ? launch_nerf_t<TBF16, NET_8x256>(a, s) : launch_nerf_t<TF32, NET_8x256>(a, s);
-            break;
-        case NET_4x64:
-            bf16 ? launch_nerf_t<TBF16, NET_4x64>(a, s) : launch_nerf_t<TF32, NET_4x64>(a, s);
-            break;
-        default:
-            break;
-    }
-}
-
-void launch_render_hash(int bf16, const RenderArgs& a, const GridArgs& g, hipStream_t s) {
-    const dim3 grid((unsigned)((a.n_rays + 3) / 4));
-    if (bf16)
-        hipLaunchKernelGGL(k_render_hash<TBF16>, grid, dim3(256), 0, s, a, g);
-    else
-        hipLaunchKernelGGL(k_render_hash<TF32>, grid, dim3(256), 0, s, a, g);
 }
 
 }  // namespace nerf
