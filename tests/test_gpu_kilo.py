@@ -1,0 +1,135 @@
+"""Parity of the many-tiny-networks render (16^3 cell networks, 128^3
+occupancy, early termination) with the CPU oracle, through the C ABI."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import render as oren
+from tests.gpu_util import dev, empty, host, max_abs, page_rays, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+RGB_TOL, ACC_TOL, DEPTH_TOL = 1e-4, 1e-4, 1e-3
+
+
+@pytest.fixture(scope="module")
+def scene():
+    torch = torch_cuda()
+    import volume_rendering_amd as v
+    cells = si.cell_params_stacked(4096, seed=0)
+    occ_bits = si.occupancy_bits(128, 0.1, seed=0)
+    pose = si.poses(1, seed=0)[0]
+    o, d = page_rays(800, 800, 1110.0, pose)
+    return dict(v=v, torch=torch, cells=cells, occ_bits=occ_bits, occ=si.occupancy_dense(occ_bits), o=o, d=d)
+
+
+def _pack_cells(v, stacked, dtype, sigma_shift=0.0):
+    params = []
+    for c in range(4096):
+        p = si.cell_slice(stacked, c)
+        if sigma_shift:
+            p = dict(p, sigma=(p["sigma"][0], p["sigma"][1] + np.float32(sigma_shift)))
+        params.append(p)
+    return v.weights.pack_many_to_device(3, dtype, params), params
+
+
+def _render(v, torch, o, d, cells_dev, occ_bits, n_samples=192, term_T=1e-2, chunk=0, workspace=False, dtype=0,
+            occ_p=None):
+    import volume_rendering_amd._binding as B
+    R = o.shape[0]
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    occ_dev = dev(occ_bits.view(np.int32))
+    cfg = B.nerf_render_cfg(mode=2, n_coarse=n_samples, n_fine=0, use_pi=1, jitter=1, seed=0, chunk=chunk,
+                            term_T=term_T, box_lo=-1.5, box_hi=1.5, occ_res=128, cell_res=16,
+                            occ=occ_dev.data_ptr())
+    dz = empty((R, n_samples))
+    nlive = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cfg.dbg_z, cfg.dbg_n_live = dz.data_ptr(), nlive.data_ptr()
+    ws = None
+    if workspace:
+        nbytes = B.nerf_render_workspace_size(cfg, R if not chunk else min(R, chunk))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), nbytes
+    w = B.nerf_weights(net=B.nerf_mlp_desc(3, dtype), cells=cells_dev.data_ptr(), n_cells=4096)
+    rgb, depth, acc = empty((R, 3)), empty(R), empty(R)
+    v.nerf_render(dev(o), dev(d), dev(near), dev(far), w, cfg, rgb, depth, acc)
+    return host(rgb), host(depth), host(acc), host(dz), int(host(nlive)[0]), near, far
+
+
+def _oracle(o, d, near, far, occ, params, term_T=1e-2, n_samples=192):
+    return oren.render_kilo(o, d, near, far, occ, lambda c: params[c], n_samples=n_samples, seed=0, term_T=term_T)
+
+
+def test_kilo_render_matches_oracle(scene):
+    say("kilo render, 10% occupancy")
+    v, torch = scene["v"], scene["torch"]
+    sel = si.subset(800 * 800, 600, seed=4)
+    o, d = scene["o"][sel], scene["d"][sel]
+    cells_dev, params = _pack_cells(v, scene["cells"], 0)
+    rgb, depth, acc, dz, n_live, near, far = _render(v, torch, o, d, cells_dev, scene["occ_bits"])
+    ref = _oracle(o, d, near, far, scene["occ"], params)
+    assert np.array_equal(dz, ref["z"])
+    assert n_live == ref["n_live"], (n_live, ref["n_live"])
+    say(f"  live samples {n_live}, rgb err {max_abs(rgb, ref['rgb']):.2e}")
+    assert max_abs(rgb, ref["rgb"]) <= RGB_TOL
+    assert max_abs(acc, ref["acc"]) <= ACC_TOL
+    assert max_abs(depth, ref["depth"]) <= DEPTH_TOL
+
+
+def test_kilo_early_termination(scene):
+    """Dense cells (density bias +30) so rays stop well before their last
+    sample; a ray whose stopping transmittance lies within 1e-5 (relative) of
+    the threshold may legitimately stop one sample apart and is excluded."""
+    say("kilo render, early termination")
+    v, torch = scene["v"], scene["torch"]
+    sel = si.subset(800 * 800, 500, seed=5)
+    o, d = scene["o"][sel], scene["d"][sel]
+    cells_dev, params = _pack_cells(v, scene["cells"], 0, sigma_shift=30.0)
+    full_bits = si.occupancy_bits(128, 1.0, seed=0)
+    full = si.occupancy_dense(full_bits)
+    rgb, depth, acc, dz, n_live, near, far = _render(v, torch, o, d, cells_dev, full_bits)
+    ref = _oracle(o, d, near, far, full, params)
+    assert n_live == ref["n_live"]
+    w = ref["w"]
+    # transmittance before each sample (up to the 1e-10 term), to find stopped
+    # and threshold-adjacent rays
+    T = 1.0 - np.concatenate([np.zeros((len(sel), 1)), np.cumsum(w, 1)[:, :-1]], 1)
+    stopped = np.any(T < 1e-2, axis=1)
+    say(f"  rays stopped early: {int(stopped.sum())} of {len(sel)}")
+    assert stopped.sum() > 0.2 * len(sel)
+    near_thr = np.any(np.abs(T / 1e-2 - 1.0) < 1e-5, axis=1)
+    keep = ~near_thr
+    assert max_abs(rgb[keep], ref["rgb"][keep]) <= RGB_TOL
+    assert max_abs(acc[keep], ref["acc"][keep]) <= ACC_TOL
+    assert max_abs(depth[keep], ref["depth"][keep]) <= DEPTH_TOL
+
+
+def test_kilo_chunks_and_workspace(scene):
+    say("kilo chunks/workspace")
+    v, torch = scene["v"], scene["torch"]
+    sel = si.subset(800 * 800, 333, seed=6)
+    o, d = scene["o"][sel], scene["d"][sel]
+    cells_dev, _ = _pack_cells(v, scene["cells"], 0)
+    a = _render(v, torch, o, d, cells_dev, scene["occ_bits"])
+    b = _render(v, torch, o, d, cells_dev, scene["occ_bits"], chunk=70)
+    c = _render(v, torch, o, d, cells_dev, scene["occ_bits"], workspace=True)
+    e = _render(v, torch, o, d, cells_dev, scene["occ_bits"], chunk=70, workspace=True)
+    for x in (b, c, e):
+        for p, q in zip(a[:4], x[:4]):
+            assert np.array_equal(p, q)
+        assert a[4] == x[4]
+
+
+def test_kilo_bf16_cells(scene):
+    say("kilo bf16 cell networks")
+    v, torch = scene["v"], scene["torch"]
+    sel = si.subset(800 * 800, 400, seed=7)
+    o, d = scene["o"][sel], scene["d"][sel]
+    cells_dev, params = _pack_cells(v, scene["cells"], 1)
+    rgb, depth, acc, dz, n_live, near, far = _render(v, torch, o, d, cells_dev, scene["occ_bits"], dtype=1)
+    ref = _oracle(o, d, near, far, scene["occ"], params)
+    assert n_live == ref["n_live"]
+    say(f"  rgb err {max_abs(rgb, ref['rgb']):.2e}")
+    assert max_abs(rgb, ref["rgb"]) <= 2e-2

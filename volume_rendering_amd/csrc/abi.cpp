@@ -77,6 +77,15 @@ nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
     return NERF_OK;
 }
 
+// Rays per launch of the many-network mode: the caller's chunk, capped so
+// that every per-chunk sample index fits 32 bits.
+int64_t kilo_chunk(const nerf_render_cfg* cfg, int64_t n_rays) {
+    int64_t c = cfg->chunk > 0 ? cfg->chunk : n_rays;
+    const int64_t cap = ((int64_t)1 << 31) / (cfg->n_coarse > 0 ? cfg->n_coarse : 1);
+    if (c > cap) c = cap;
+    return c < n_rays ? c : n_rays;
+}
+
 }  // namespace
 
 nerf_status nerf_fail(nerf_status s, const char* fmt, ...) {
@@ -219,9 +228,10 @@ nerf_status nerf_sample_pdf(const float* z_coarse, const float* w_coarse, int64_
 }
 
 size_t nerf_render_workspace_size(const nerf_render_cfg* cfg, int64_t n_rays) {
-    (void)cfg;
-    (void)n_rays;
-    return 0;
+    if (!cfg || cfg->mode != NERF_MODE_KILO || n_rays <= 0 || cfg->n_coarse < 1 || cfg->cell_res < 1) return 0;
+    const int64_t chunk = kilo_chunk(cfg, n_rays);
+    const int n_cells = cfg->cell_res * cfg->cell_res * cfg->cell_res;
+    return kilo_workspace_layout(chunk, cfg->n_coarse, n_cells, nullptr, nullptr);
 }
 
 nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
@@ -274,15 +284,63 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
             ga = grid_args(w->grid);
             break;
         }
-        case NERF_MODE_KILO:
-            return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: many-network mode not built");
+        case NERF_MODE_KILO: {
+            if (w->net.kind != NET_CELL_2x32)
+                return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: many-network mode needs the 2x32 cell network");
+            NERF_REQUIRE(cfg->n_fine == 0, "nerf_render: many-network mode has no resampling pass");
+            NERF_REQUIRE(cfg->cell_res >= 1 && cfg->cell_res <= 40, "nerf_render: cell_res %d outside 1..40",
+                         cfg->cell_res);
+            NERF_REQUIRE(cfg->occ_res >= 1 && cfg->occ_res <= 2048, "nerf_render: occ_res %d outside 1..2048",
+                         cfg->occ_res);
+            NERF_REQUIRE(w->n_cells == cfg->cell_res * cfg->cell_res * cfg->cell_res,
+                         "nerf_render: n_cells %d != cell_res^3", w->n_cells);
+            NERF_REQUIRE(w->cells && cfg->occ, "nerf_render: cell networks or occupancy grid is NULL");
+            NERF_REQUIRE(aligned16(w->cells), "nerf_render: packed cell networks must be 16-byte aligned");
+            NERF_REQUIRE(cfg->box_hi > cfg->box_lo, "nerf_render: empty scene box");
+            NERF_REQUIRE(cfg->term_T >= 0.0f, "nerf_render: term_T %g < 0", (double)cfg->term_T);
+            break;
+        }
         default:
             return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_render: mode %d", cfg->mode);
     }
     if (n_rays == 0) return NERF_OK;
     NERF_REQUIRE(rays_o && rays_d && t_near && t_far && rgb && depth && acc, "nerf_render: NULL ray or output");
-    const int64_t chunk = cfg->chunk > 0 ? cfg->chunk : n_rays;
     const int n_total = cfg->mode == NERF_MODE_NERF ? cfg->n_coarse + cfg->n_fine : cfg->n_coarse;
+    int64_t chunk = cfg->chunk > 0 ? cfg->chunk : n_rays;
+    KiloArgs ka{};
+    void* own_ws = nullptr;
+    if (cfg->mode == NERF_MODE_KILO) {
+        chunk = kilo_chunk(cfg, n_rays);
+        const int n_cells = cfg->cell_res * cfg->cell_res * cfg->cell_res;
+        const size_t need = kilo_workspace_layout(chunk, cfg->n_coarse, n_cells, nullptr, nullptr);
+        char* ws = static_cast<char*>(cfg->workspace);
+        if (ws) {
+            if (cfg->workspace_bytes < need)
+                return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: workspace has %zu bytes, needs %zu",
+                                 cfg->workspace_bytes, need);
+            NERF_REQUIRE(aligned16(ws), "nerf_render: workspace must be 16-byte aligned");
+        } else {
+            clear_pending();
+            const hipError_t e = hipMallocAsync(&own_ws, need, as_stream(stream));
+            if (e != hipSuccess)
+                return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: cannot allocate %zu workspace bytes: %s", need,
+                                 hipGetErrorString(e));
+            ws = static_cast<char*>(own_ws);
+        }
+        kilo_workspace_layout(chunk, cfg->n_coarse, n_cells, ws, &ka);
+        ka.lo = cfg->box_lo;
+        ka.hi = cfg->box_hi;
+        const double span = (double)cfg->box_hi - (double)cfg->box_lo;
+        ka.vscale = (float)((double)cfg->occ_res / span);
+        ka.cscale = (float)((double)cfg->cell_res / span);
+        ka.occ_res = cfg->occ_res;
+        ka.cell_res = cfg->cell_res;
+        ka.term_T = cfg->term_T;
+        ka.occ = cfg->occ;
+        ka.cells = w->cells;
+        ka.cell_stride = nerf_mlp_packed_bytes(&w->net);
+        ka.dbg_n_live = cfg->dbg_n_live;
+    }
     clear_pending();
     for (int64_t r0 = 0; r0 < n_rays; r0 += chunk) {
         const int64_t nr = (n_rays - r0) < chunk ? (n_rays - r0) : chunk;
@@ -302,10 +360,19 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
         c.dbg_w = cfg->dbg_w_coarse ? cfg->dbg_w_coarse + r0 * cfg->n_coarse : nullptr;
         if (cfg->mode == NERF_MODE_NERF)
             launch_render_nerf(w->net.kind, bf16, c, as_stream(stream));
-        else
+        else if (cfg->mode == NERF_MODE_HASH)
             launch_render_hash(bf16, c, ga, as_stream(stream));
+        else
+            launch_render_kilo(bf16, c, ka, r0 > 0, as_stream(stream));
         const nerf_status st = check_launch("nerf_render");
-        if (st != NERF_OK) return st;
+        if (st != NERF_OK) {
+            if (own_ws) (void)hipFreeAsync(own_ws, as_stream(stream));
+            return st;
+        }
+    }
+    if (own_ws) {
+        const hipError_t e = hipFreeAsync(own_ws, as_stream(stream));
+        if (e != hipSuccess) return nerf_fail(NERF_ERR_HIP, "nerf_render: workspace free: %s", hipGetErrorString(e));
     }
     return NERF_OK;
 }

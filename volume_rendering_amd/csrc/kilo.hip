@@ -1,0 +1,415 @@
+// Many tiny networks for gfx950 ("KiloNeRF: Speeding up Neural Radiance
+// Fields with Thousands of Tiny MLPs", abstract: the scene is divided among
+// thousands of small networks, with further optimisations such as skipping
+// empty space and stopping rays early).
+//
+// One render pass runs as a pipeline of small kernels, with no host
+// synchronisation:
+//   count     one wave per ray: stratified samples, box and occupancy test,
+//             number of live samples per ray
+//   scan      exclusive prefix sum of the counts (ray start offsets)
+//   compact   one wave per ray: live samples written in (ray, sample) order
+//             with their cell id; per-cell histogram
+//   cells     one workgroup: per-cell start offsets, tile counts, tile list
+//   scatter   live samples into per-cell buckets
+//   mlp       persistent waves over the tile list: each tile is up to 64
+//             (bf16) or 32 (f32) samples of one cell, evaluated by that
+//             cell's network read straight from global memory
+//   composite one wave per ray: samples in order, density 0 for dead ones,
+//             stop at the first sample with transmittance below term_T
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "mlp.hpp"
+#include "raysteps.hpp"
+
+namespace nerf {
+
+constexpr int kScanBlock = 1024;  // elements per local-scan block (256 threads x 4)
+
+// ---------------------------------------------------------------------------
+// Scans
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_up(v, off, kWave);
+        if (l >= off) v += o;
+    }
+    return v;
+}
+
+// Exclusive scan of one value per thread over the workgroup (blockDim.x a
+// multiple of 64, at most 1024).  lds needs 17 entries.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, nw = blockDim.x / kWave;
+    const uint32_t incl = wave_incl_scan_u32(v);
+    if (lane == kWave - 1) lds[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t t = lane < nw ? lds[lane] : 0u;
+        const uint32_t ti = wave_incl_scan_u32(t);
+        if (lane < nw) lds[lane] = ti - t;
+        if (lane == nw - 1) lds[16] = ti;
+    }
+    __syncthreads();
+    const uint32_t res = lds[wave] + incl - v;
+    total = lds[16];
+    __syncthreads();
+    return res;
+}
+
+__global__ void __launch_bounds__(256) k_scan_local(const uint32_t* __restrict__ in, uint32_t* __restrict__ out,
+                                                    int64_t n, uint32_t* __restrict__ block_sums) {
+    __shared__ uint32_t lds[17];
+    const int64_t base = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * 4;
+    uint32_t v[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = base + j < n ? in[base + j] : 0u;
+        s += v[j];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan(s, lds, total);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (base + j < n) out[base + j] = run;
+        run += v[j];
+    }
+    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+// One workgroup: exclusive scan of the block sums in place; entry nb = total.
+__global__ void __launch_bounds__(1024) k_scan_blocks(uint32_t* __restrict__ bs, int64_t nb) {
+    __shared__ uint32_t lds[17];
+    uint32_t carry = 0;
+    for (int64_t b0 = 0; b0 < nb; b0 += blockDim.x) {
+        const int64_t i = b0 + threadIdx.x;
+        const uint32_t v = i < nb ? bs[i] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(v, lds, tot);
+        if (i < nb) bs[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) bs[nb] = carry;
+}
+
+__global__ void __launch_bounds__(256) k_scan_add(uint32_t* __restrict__ out, int64_t n,
+                                                  const uint32_t* __restrict__ bs, int64_t nb) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] += bs[i / kScanBlock];
+    if (i == n) out[n] = bs[nb];
+}
+
+__global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Samples and their classification
+// ---------------------------------------------------------------------------
+struct RayIn {
+    float o[3], d[3], near, far;
+};
+
+__device__ __forceinline__ RayIn load_ray(const RenderArgs& a, int64_t r) {
+    RayIn R;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        R.o[k] = a.ro[3 * r + k];
+        R.d[k] = a.rd[3 * r + k];
+    }
+    R.near = a.tn[r];
+    R.far = a.tf[r];
+    return R;
+}
+
+// Sample i of ray r (global counter ray_offset + r): z and the point.
+__device__ __forceinline__ float sample_point(const RenderArgs& a, const RayIn& R, int64_t r, int i, float (&x)[3]) {
+    const float u = a.jitter ? philox_uniform(a.seed, a.ray_offset + (uint64_t)r, (uint32_t)i, kStreamJitter) : 0.5f;
+    const float z = stratified_z(R.near, R.far, i, a.n_coarse, u);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) x[k] = __fadd_rn(R.o[k], __fmul_rn(z, R.d[k]));
+    return z;
+}
+
+__device__ __forceinline__ int grid_coord(float t, float scale, int res) {
+    const float f = floorf(__fmul_rn(t, scale));
+    return (int)fminf(fmaxf(f, 0.0f), (float)(res - 1));  // NaN -> 0
+}
+
+// Live = inside the closed box and in an occupied voxel; also the cell id.
+// Coordinates are floor((x - lo) * scale) of rounded float32 operations,
+// clamped to the grid; ids are x-major.
+__device__ __forceinline__ bool classify(const KiloArgs& k, const float (&x)[3], int& cell) {
+    bool inside = true;
+    int v[3], c[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        inside = inside && (x[a] >= k.lo) && (x[a] <= k.hi);
+        const float t = __fsub_rn(x[a], k.lo);
+        v[a] = grid_coord(t, k.vscale, k.occ_res);
+        c[a] = grid_coord(t, k.cscale, k.cell_res);
+    }
+    const uint32_t vox = ((uint32_t)v[0] * k.occ_res + v[1]) * k.occ_res + v[2];
+    cell = (c[0] * k.cell_res + c[1]) * k.cell_res + c[2];
+    const bool occ = (k.occ[vox >> 5] >> (vox & 31)) & 1u;
+    return inside && occ;
+}
+
+__global__ void __launch_bounds__(256) k_kilo_count(RenderArgs a, KiloArgs k) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (r >= a.n_rays) return;
+    const RayIn R = load_ray(a, r);
+    const int lane = lane_id();
+    uint32_t cnt = 0;
+    for (int base = 0; base < a.n_coarse; base += kWave) {
+        const int i = base + lane;
+        bool live = false;
+        if (i < a.n_coarse) {
+            float x[3];
+            sample_point(a, R, r, i, x);
+            int cell;
+            live = classify(k, x, cell);
+        }
+        cnt += __popcll(__ballot(live));
+    }
+    if (lane == 0) k.live_count[r] = cnt;
+}
+
+__global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (r >= a.n_rays) return;
+    const RayIn R = load_ray(a, r);
+    const int lane = lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    uint32_t pos = k.ray_start[r];
+    for (int base = 0; base < a.n_coarse; base += kWave) {
+        const int i = base + lane;
+        bool live = false;
+        int cell = 0;
+        if (i < a.n_coarse) {
+            float x[3];
+            sample_point(a, R, r, i, x);
+            live = classify(k, x, cell);
+        }
+        const unsigned long long m = __ballot(live);
+        if (live) {
+            const uint32_t e = pos + (uint32_t)__popcll(m & below);
+            k.ent_ray[e] = (uint32_t)r;
+            k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
+            atomicAdd(&k.cell_count[cell], 1u);
+        }
+        pos += (uint32_t)__popcll(m);
+    }
+}
+
+// One workgroup of 1024 threads: cell start offsets, tiles per cell and the
+// tile list.
+__global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells, int tile) {
+    __shared__ uint32_t lds[17];
+    uint32_t carry_s = 0, carry_t = 0;
+    for (int c0 = 0; c0 < n_cells; c0 += blockDim.x) {
+        const int c = c0 + threadIdx.x;
+        const uint32_t cnt = c < n_cells ? k.cell_count[c] : 0u;
+        const uint32_t nt = (cnt + tile - 1) / tile;
+        uint32_t ts, tt;
+        const uint32_t es = block_excl_scan(cnt, lds, ts);
+        const uint32_t et = block_excl_scan(nt, lds, tt);
+        if (c < n_cells) {
+            k.cell_start[c] = carry_s + es;
+            k.tile_start[c] = carry_t + et;
+            k.cell_fill[c] = 0u;
+        }
+        carry_s += ts;
+        carry_t += tt;
+    }
+    if (threadIdx.x == 0) {
+        k.cell_start[n_cells] = carry_s;
+        k.tile_start[n_cells] = carry_t;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < n_cells; c += blockDim.x) {
+        const uint32_t t0 = k.tile_start[c], t1 = k.tile_start[c + 1];
+        for (uint32_t t = t0; t < t1; ++t) {
+            k.tile_cell[t] = (uint32_t)c;
+            k.tile_off[t] = (t - t0) * (uint32_t)tile;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_kilo_scatter(KiloArgs k, int64_t n_rays) {
+    const uint32_t total = k.ray_start[n_rays];
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const uint32_t c = k.ent_meta[e] & 0xFFFFu;
+        const uint32_t p = k.cell_start[c] + atomicAdd(&k.cell_fill[c], 1u);
+        k.bucket[p] = e;
+    }
+}
+
+// Persistent waves over the tile list: tile t holds samples
+// [tile_off, tile_off + 32*SB) of its cell's bucket.
+template <class T>
+__global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int n_cells) {
+    constexpr int K = NET_CELL_2x32;
+    constexpr int SB = T::SB;
+    constexpr int ES = seg_steps(net_layers(K)[0].s0, T::prec);
+    constexpr int DS = seg_steps(net_layers(K)[4].s1, T::prec);
+    const int lane = lane_id();
+    const uint32_t total_tiles = k.tile_start[n_cells];
+    const uint32_t nwaves = gridDim.x * (blockDim.x / kWave);
+    for (uint32_t t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < total_tiles; t += nwaves) {
+        const uint32_t c = k.tile_cell[t], off = k.tile_off[t];
+        const uint32_t cs = k.cell_start[c], cnt = k.cell_start[c + 1] - cs;
+        uint32_t e[SB];
+        bool valid[SB];
+        float x[SB][3], v[SB][3];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+            const uint32_t j = off + sb * 32 + (lane & 31);
+            valid[sb] = j < cnt;
+            e[sb] = k.bucket[cs + (valid[sb] ? j : off)];
+            const uint32_t r = k.ent_ray[e[sb]];
+            const int i = (int)(k.ent_meta[e[sb]] >> 16);
+            const RayIn R = load_ray(a, r);
+            sample_point(a, R, r, i, x[sb]);
+            const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) v[sb][q] = R.d[q] / dn;
+        }
+        typename T::Op enc[ES][SB], denc[DS][SB];
+        enc_operands(enc, 10, x, a.use_pi != 0, lane);
+        enc_operands(denc, 4, v, a.use_pi != 0, lane);
+        const char* packed = (const char*)k.cells + (size_t)c * k.cell_stride;
+        GlobalStream<T, K> ws(packed, lane, 0);
+        const float* bias = (const float*)(packed + net_bias_offset(K, T::prec, 0));
+        f32x16 sig[SB], rgb[SB];
+        nerf_forward<T, K>(enc, denc, ws, bias, sig, rgb, lane);
+        if (lane < 32) {
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb)
+                if (valid[sb])
+                    reinterpret_cast<f32x4*>(k.raw_live)[e[sb]] =
+                        f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
+        }
+    }
+}
+
+struct KiloLds {
+    float z[256];
+    f32x4 raw[256];
+};
+
+__global__ void __launch_bounds__(256) k_kilo_composite(RenderArgs a, KiloArgs k) {
+    __shared__ KiloLds lds_all[4];
+    const int wave = threadIdx.x / kWave;
+    KiloLds& S = lds_all[wave];
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= a.n_rays) return;
+    const RayIn R = load_ray(a, r);
+    const int lane = lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int N = a.n_coarse;
+    uint32_t pos = k.ray_start[r];
+    for (int base = 0; base < N; base += kWave) {
+        const int i = base + lane;
+        bool live = false;
+        if (i < N) {
+            float x[3];
+            S.z[i] = sample_point(a, R, r, i, x);
+            int cell;
+            live = classify(k, x, cell);
+        }
+        const unsigned long long m = __ballot(live);
+        if (i < N)
+            S.raw[i] = live ? reinterpret_cast<const f32x4*>(k.raw_live)[pos + __popcll(m & below)]
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        pos += (uint32_t)__popcll(m);
+    }
+    wave_lds_sync();
+    const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
+    const CompositeOut c = composite_ray(S.z, S.raw, N, dn, nullptr, k.term_T);
+    if (a.dbg_z)
+        for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = S.z[i];
+    if (lane == 0) {
+        const float bg = a.white ? 1.0f - c.acc : 0.0f;
+        a.rgb[3 * r] = c.r + bg;
+        a.rgb[3 * r + 1] = c.g + bg;
+        a.rgb[3 * r + 2] = c.b + bg;
+        a.depth[r] = c.depth;
+        a.acc[r] = c.acc;
+    }
+}
+
+// Number of live samples of this chunk, written (first chunk) or added.
+__global__ void k_kilo_n_live(const uint32_t* __restrict__ ray_start, int64_t n_rays, int64_t* out, int add) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *out = (add ? *out : 0) + (int64_t)ray_start[n_rays];
+}
+
+// ---------------------------------------------------------------------------
+// Workspace and launch
+// ---------------------------------------------------------------------------
+size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k) {
+    const uint64_t max_live = (uint64_t)n_rays * (uint64_t)n_samples;
+    const uint64_t max_tiles = (max_live + 31) / 32 + (uint64_t)n_cells;
+    const uint64_t nb = (uint64_t)((n_rays + kScanBlock - 1) / kScanBlock);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
+                 o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
+                 o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
+                 o_cf = take(4 * (size_t)n_cells), o_ts = take(4 * ((size_t)n_cells + 1)),
+                 o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
+                 o_raw = take(16 * max_live);
+    if (base && k) {
+        k->live_count = (uint32_t*)(base + o_live);
+        k->ray_start = (uint32_t*)(base + o_start);
+        k->block_sums = (uint32_t*)(base + o_bs);
+        k->ent_ray = (uint32_t*)(base + o_er);
+        k->ent_meta = (uint32_t*)(base + o_em);
+        k->cell_count = (uint32_t*)(base + o_cc);
+        k->cell_start = (uint32_t*)(base + o_cs);
+        k->cell_fill = (uint32_t*)(base + o_cf);
+        k->tile_start = (uint32_t*)(base + o_ts);
+        k->tile_cell = (uint32_t*)(base + o_tc);
+        k->tile_off = (uint32_t*)(base + o_to);
+        k->bucket = (uint32_t*)(base + o_bk);
+        k->raw_live = (float*)(base + o_raw);
+    }
+    return off;
+}
+
+void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int add_n_live, hipStream_t s) {
+    const int64_t n = a.n_rays;
+    const int n_cells = k.cell_res * k.cell_res * k.cell_res;
+    const dim3 rays4((unsigned)((n + 3) / 4));
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((n_cells + 255) / 256)), dim3(256), 0, s, k.cell_count,
+                       (int64_t)n_cells, 0u);
+    hipLaunchKernelGGL(k_kilo_count, rays4, dim3(256), 0, s, a, k);
+    const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(k_scan_local, dim3((unsigned)nb), dim3(256), 0, s, k.live_count, k.ray_start, n, k.block_sums);
+    hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, k.block_sums, nb);
+    hipLaunchKernelGGL(k_scan_add, dim3((unsigned)((n + 1 + 255) / 256)), dim3(256), 0, s, k.ray_start, n,
+                       k.block_sums, nb);
+    hipLaunchKernelGGL(k_kilo_compact, rays4, dim3(256), 0, s, a, k);
+    const int tile = bf16 ? 64 : 32;
+    hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells, tile);
+    hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n);
+    const dim3 persist(256 * 16);
+    if (bf16)
+        hipLaunchKernelGGL(k_kilo_mlp<TBF16>, persist, dim3(256), 0, s, a, k, n_cells);
+    else
+        hipLaunchKernelGGL(k_kilo_mlp<TF32>, persist, dim3(256), 0, s, a, k, n_cells);
+    hipLaunchKernelGGL(k_kilo_composite, rays4, dim3(256), 0, s, a, k);
+    if (k.dbg_n_live)
+        hipLaunchKernelGGL(k_kilo_n_live, dim3(1), dim3(64), 0, s, k.ray_start, n, k.dbg_n_live, add_n_live);
+}
+
+}  // namespace nerf

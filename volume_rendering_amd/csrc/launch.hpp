@@ -36,6 +36,39 @@ struct RenderArgs {
     float* dbg_w;
 };
 
+// Many-tiny-networks render: scene box, occupancy grid, cell networks and
+// the device workspace carved by the ABI layer.
+struct KiloArgs {
+    float lo, hi;       // scene box
+    float vscale;       // occ_res / (hi - lo), rounded to float32 once
+    float cscale;       // cell_res / (hi - lo), rounded to float32 once
+    int occ_res, cell_res;
+    float term_T;
+    const uint32_t* occ;
+    const void* cells;  // packed cell networks back to back
+    size_t cell_stride; // bytes per packed network
+    int64_t* dbg_n_live;
+    // workspace
+    uint32_t* live_count;  // [n_rays]
+    uint32_t* ray_start;   // [n_rays + 1]
+    uint32_t* block_sums;  // [scan blocks + 1]
+    uint32_t* ent_ray;     // [max_live]
+    uint32_t* ent_meta;    // [max_live]: sample << 16 | cell
+    uint32_t* cell_count;  // [n_cells]
+    uint32_t* cell_start;  // [n_cells + 1]
+    uint32_t* cell_fill;   // [n_cells]
+    uint32_t* tile_start;  // [n_cells + 1]
+    uint32_t* tile_cell;   // [max_tiles]
+    uint32_t* tile_off;    // [max_tiles]
+    uint32_t* bucket;      // [max_live]
+    float* raw_live;       // [max_live, 4]
+};
+
+// Workspace layout of the many-tiny-networks render for n_rays x n_samples.
+size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k);
+
+void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int add_n_live, hipStream_t s);
+
 void launch_gen_rays(const float* pose, int W, int H, float fx, float fy, float cx, float cy, float* ro, float* rd,
                      hipStream_t s);
 void launch_stratified(const float* tn, const float* tf, int64_t n_rays, int n, uint64_t seed, uint64_t ray_offset,

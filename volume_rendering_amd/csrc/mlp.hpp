@@ -225,6 +225,12 @@ __device__ __forceinline__ f32x16 load_bias16(const NERF_AS_LDS float* bias, int
     return reinterpret_cast<const NERF_AS_LDS f32x16*>(bias + layer_float)[2 * ob + h];
 }
 
+// Global-memory variant, for waves that each evaluate a different network
+// (the bias pointer is the start of that network's bias region).
+__device__ __forceinline__ f32x16 load_bias16(const float* bias, int layer_float, int ob, int h) {
+    return ((const NERF_AS_GLOBAL f32x16*)(bias + layer_float))[2 * ob + h];
+}
+
 template <class T, int KIND, int LAYER>
 struct LayerInfo {
     static constexpr Layer L = net_layers(KIND)[LAYER];
@@ -353,9 +359,8 @@ __device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bi
 }
 
 // A hidden layer: out = act(W [in1, in2] + b), kept as next-layer operands.
-template <class T, int KIND, int LAYER, class In1, class In2, class Out, class WS>
-__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws,
-                                            const NERF_AS_LDS float* bias, int lane) {
+template <class T, int KIND, int LAYER, class In1, class In2, class Out, class WS, class BP>
+__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws, BP bias, int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
     constexpr bool RELU = I::L.relu != 0;
     const int h = lane >> 5;
@@ -372,9 +377,9 @@ __device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out&
 }
 
 // A head (one output block, no activation): raw accumulators.
-template <class T, int KIND, int LAYER, class In1, class In2, class WS>
-__device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB], WS& ws,
-                                           const NERF_AS_LDS float* bias, int lane) {
+template <class T, int KIND, int LAYER, class In1, class In2, class WS, class BP>
+__device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB], WS& ws, BP bias,
+                                           int lane) {
     using I = LayerInfo<T, KIND, LAYER>;
     static_assert(I::OB == 1, "head layers have one output block");
     const f32x16 b = load_bias16(bias, I::bias, 0, lane >> 5);
@@ -393,9 +398,8 @@ struct NerfFamily {
     static constexpr int LDIR = net_layers(KIND)[D + 2].s1.L;
 };
 
-template <class T, int KIND, int I, int D, class H, class E, class WS>
-__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, const NERF_AS_LDS float* bias,
-                                             int lane) {
+template <class T, int KIND, int I, int D, class H, class E, class WS, class BP>
+__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, BP bias, int lane) {
     if constexpr (I < D) {
         dense_layer<T, KIND, I>(cur, enc, nxt, ws, bias, lane);  // enc is read only by a skip layer (S2 > 0)
         hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, bias, lane);
@@ -405,9 +409,9 @@ __device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& w
 // enc: position-encoding operands; denc: direction-encoding operands.
 // sig[sb] accumulator 0 and rgb[sb] accumulators 0..2 of lanes 0..31 hold the
 // outputs of sample (sb*32 + lane).
-template <class T, int KIND, class E, class DE, class WS>
-__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& ws, const NERF_AS_LDS float* bias,
-                                             f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
+template <class T, int KIND, class E, class DE, class WS, class BP>
+__device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& ws, BP bias, f32x16 (&sig)[T::SB],
+                                             f32x16 (&rgb)[T::SB], int lane) {
     using Fam = NerfFamily<KIND>;
     constexpr int D = Fam::D;
     constexpr int HS = out_steps<T, KIND, 0>();
@@ -428,10 +432,9 @@ __device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& w
 
 // Hash-grid field: density 0, 1; density head 2; feature 3; colour 4 (with
 // harmonics), 5; rgb head 6.
-template <class T, class FE, class DE, class WS>
-__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, WS& ws,
-                                                   const NERF_AS_LDS float* bias, f32x16 (&sig)[T::SB],
-                                                   f32x16 (&rgb)[T::SB], int lane) {
+template <class T, class FE, class DE, class WS, class BP>
+__device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh, WS& ws, BP bias,
+                                                   f32x16 (&sig)[T::SB], f32x16 (&rgb)[T::SB], int lane) {
     constexpr int K = NET_HASH_FIELD;
     constexpr int HS = out_steps<T, K, 0>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
