@@ -1,6 +1,6 @@
 """Throughput of the NeRF forward-render hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload hierarchical|coarse|tiny|hash]
+    python bench.py [--steps K] [--warmup W] [--workload hierarchical|coarse|tiny|hash|kilo]
                     [--dtype bf16|f32] [--no-cpu-baseline]
 
 A step is one ``nerf_render`` over the whole workload with rays, weights
@@ -31,6 +31,12 @@ PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X
 MACS_8x256 = 593408
 MACS_4x64 = 21952
 MACS_HASH_FIELD = 19712
+MACS_CELL_2x32 = 5088
+
+# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by a 1 GiB copy (x2.0 and x1.0), keyed by
+# (workload, dtype).  An entry is removed whenever that kernel changes.
+MEASURED_TRAFFIC = {("hierarchical", "bf16"): 513.1e6}
 
 WORKLOADS = {
     # name: (poses, hemisphere, H, W, focal, n_coarse, n_fine, net kind, chunk)
@@ -38,6 +44,7 @@ WORKLOADS = {
     "coarse": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=1, chunk=65536),
     "tiny": dict(poses=1, hemi=False, H=32, W=32, focal=40.0, nc=16, nf=0, kind=2, chunk=0),
     "hash": dict(poses=1, hemi=True, H=256, W=256, focal=355.2, nc=128, nf=0, kind=4, chunk=0),
+    "kilo": dict(poses=1, hemi=True, H=800, W=800, focal=1110.0, nc=192, nf=0, kind=3, chunk=0),
 }
 
 
@@ -50,6 +57,10 @@ def parse():
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    ap.add_argument("--poses", type=int, default=0, help="override the workload's pose count")
+    ap.add_argument("--n-fine", type=int, default=-1, help="override the workload's inverse-CDF samples")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device copy of MIB mebibytes (counter calibration)")
     return ap.parse_args()
 
 
@@ -62,11 +73,17 @@ def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     Lp = 6 if kind == 2 else 10
+    if kind == 3:
+        target_s = min(target_s, 6.0)
 
     def run(n):
         sel = np.linspace(0, rays_o.shape[0] - 1, n).astype(np.int64)
         t = time.perf_counter()
-        if kind == 4:
+        if kind == 3:
+            cells, occ = coarse
+            oren.render_kilo(rays_o[sel], rays_d[sel], near[sel], far[sel], occ, lambda c: cells[c], wl["nc"], seed=0,
+                             term_T=1e-2)
+        elif kind == 4:
             from oracle import encoding as oenc
             grid, tabs, field = coarse
             oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0)
@@ -96,7 +113,11 @@ def main():
     import volume_rendering_amd as v
     from volume_rendering_amd import _binding as B
 
-    wl = WORKLOADS[args.workload]
+    wl = dict(WORKLOADS[args.workload])
+    if args.poses > 0:
+        wl["poses"] = args.poses
+    if args.n_fine >= 0:
+        wl["nf"] = args.n_fine
     dtype = 1 if args.dtype == "bf16" else 0
     kind = wl["kind"]
     if kind == 2 and args.dtype == "bf16" and args.workload == "tiny":
@@ -117,7 +138,19 @@ def main():
     far = torch.full((R,), 6.0, device=dev)
 
     grid_keep = None
-    if kind == 4:
+    kilo_keep = None
+    if kind == 3:
+        stacked = si.cell_params_stacked(4096, seed=0)
+        cell_list = [si.cell_slice(stacked, c) for c in range(4096)]
+        cells_dev = v.weights.pack_many_to_device(3, dtype, cell_list)
+        occ_bits = si.occupancy_bits(128, 0.1, seed=0)
+        occ_dev = torch.from_numpy(occ_bits.view(np.int32)).to(dev)
+        nlive = torch.zeros(1, dtype=torch.int64, device=dev)
+        kilo_keep = (cells_dev, occ_dev, nlive)
+        coarse_p, fine_p = (cell_list, si.occupancy_dense(occ_bits)), None
+        nets = []
+        mode = B.NERF_MODE_KILO
+    elif kind == 4:
         from oracle import encoding as _unused  # noqa: F401  (oracle only used for the cpu baseline)
         g = v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048)
         tabs = si.hash_tables(list(g.size)[:16], seed=0, scale=1.0)
@@ -135,9 +168,17 @@ def main():
         nets = [v.weights.pack_to_device(kind, dtype, coarse_p), v.weights.pack_to_device(kind, dtype, fine_p)]
         mode = B.NERF_MODE_NERF
     cfg = B.nerf_render_cfg(mode=mode, n_coarse=wl["nc"], n_fine=wl["nf"], use_pi=1, jitter=1, seed=0,
-                            chunk=wl["chunk"], box_lo=-1.5, box_hi=1.5)
-    w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), coarse=nets[0].data_ptr(),
-                       fine=nets[1].data_ptr() if len(nets) > 1 else None)
+                            chunk=wl["chunk"], box_lo=-1.5, box_hi=1.5, term_T=1e-2, occ_res=128, cell_res=16)
+    if kilo_keep is not None:
+        w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), cells=kilo_keep[0].data_ptr(), n_cells=4096)
+        cfg.occ = kilo_keep[1].data_ptr()
+        cfg.dbg_n_live = kilo_keep[2].data_ptr()
+        ws_bytes = B.nerf_render_workspace_size(cfg, R)
+        kilo_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        cfg.workspace, cfg.workspace_bytes = kilo_ws.data_ptr(), ws_bytes
+    else:
+        w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), coarse=nets[0].data_ptr(),
+                           fine=nets[1].data_ptr() if len(nets) > 1 else None)
     if grid_keep is not None:
         import ctypes
         w.grid = ctypes.pointer(grid_keep[0])
@@ -148,6 +189,13 @@ def main():
     def step():
         v.nerf_render(ro, rd, near, far, w, cfg, rgb, depth, acc)
 
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # plain device copy of known size, for counter calibration
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -163,8 +211,11 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     ms_kernel = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
 
-    n_mlp_samples = R * (wl["nc"] + (wl["nc"] + wl["nf"] if wl["nf"] else 0))
-    macs = MACS_8x256 if kind == 1 else MACS_4x64 if kind == 2 else MACS_HASH_FIELD
+    if kind == 3:
+        n_mlp_samples = int(kilo_keep[2].item())  # live samples the cell networks evaluated
+    else:
+        n_mlp_samples = R * (wl["nc"] + (wl["nc"] + wl["nf"] if wl["nf"] else 0))
+    macs = {1: MACS_8x256, 2: MACS_4x64, 3: MACS_CELL_2x32, 4: MACS_HASH_FIELD}[kind]
     flops = 2.0 * macs * n_mlp_samples  # algorithmic network FLOPs per launch (all chunks of one step)
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     peak = PEAK[dt_name]
@@ -183,11 +234,13 @@ def main():
         "dtype": dt_name,
         "data": "synthetic: seeded hemisphere poses, He-uniform random weights",
         "config": {"workload": args.workload, "rays": R, "poses": wl["poses"], "H": H, "W": W, "focal": f,
-                   "n_coarse": wl["nc"], "n_fine": wl["nf"], "net": {1: "8x256", 2: "4x64", 4: "hash-field"}[kind],
+                   "n_coarse": wl["nc"], "n_fine": wl["nf"],
+                   "net": {1: "8x256", 2: "4x64", 3: "4096 cells 2x32", 4: "hash-field"}[kind],
                    "chunk": wl["chunk"]},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "kernel": "k_render_nerf" if kind != 4 else "k_render_hash", "kernel_ms": ms_kernel,
+                     "frac": achieved / peak, "traffic": MEASURED_TRAFFIC.get((args.workload, dt_name)),
+                     "kernel": {1: "k_render_nerf", 2: "k_render_nerf", 3: "kilo pipeline", 4: "k_render_hash"}[kind],
+                     "kernel_ms": ms_kernel,
                      "flop_per_launch": flops},
     }
     if not args.no_cpu_baseline:
