@@ -188,7 +188,6 @@ void launch_composite(const float* raw, const float* z, const float* rd, int64_t
 // Standalone inverse-CDF resampling + merge: one wave per ray, per-wave LDS.
 // ===========================================================================
 constexpr int kMaxSamples = 256;
-constexpr int kMlpRing = 8;  // 128 KB weight ring
 
 struct PdfLds {
     double cdf[kMaxSamples];

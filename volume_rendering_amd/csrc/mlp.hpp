@@ -221,8 +221,15 @@ __device__ __forceinline__ void bias_to_lds(NERF_AS_LDS float* dst, const char* 
     for (int i = tid; i < BR::floats / 4; i += nthreads) reinterpret_cast<NERF_AS_LDS f32x4*>(dst)[i] = src[i];
 }
 
+// Four 16-byte reads, not one 64-byte read: the compiler splits a 64-byte LDS
+// read into four without keeping its alias information, then cannot tell it
+// apart from the weight ring's direct loads and waits for every one of them
+// in flight (vmcnt(0)) before the read.
 __device__ __forceinline__ f32x16 load_bias16(const NERF_AS_LDS float* bias, int layer_float, int ob, int h) {
-    return reinterpret_cast<const NERF_AS_LDS f32x16*>(bias + layer_float)[2 * ob + h];
+    const NERF_AS_LDS f32x4* p = reinterpret_cast<const NERF_AS_LDS f32x4*>(bias + layer_float) + 4 * (2 * ob + h);
+    const f32x4 q0 = p[0], q1 = p[1], q2 = p[2], q3 = p[3];
+    return f32x16{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3],
+                  q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
 }
 
 // Global-memory variant, for waves that each evaluate a different network
@@ -521,8 +528,11 @@ __device__ __forceinline__ void row_operands(bf16x8 (&op)[NS][2], Seg seg, const
             bf16x8 v;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
+                // padding columns (c < 0) load column 0 and discard it, so
+                // every load issues unconditionally and back to back
                 const int c = seg_col(seg, PREC_BF16, s, h, j);
-                v[j] = to_bf16(c >= 0 ? row[sb][c] : 0.0f);
+                const float x = row[sb][c >= 0 ? c : 0];
+                v[j] = to_bf16(c >= 0 ? x : 0.0f);
             }
             op[s][sb] = v;
         }
@@ -534,7 +544,8 @@ __device__ __forceinline__ void row_operands(float (&op)[NS][1], Seg seg, const 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int c = seg_col(seg, PREC_F32, s, h, 0);
-        op[s][0] = c >= 0 ? row[0][c] : 0.0f;
+        const float x = row[0][c >= 0 ? c : 0];
+        op[s][0] = c >= 0 ? x : 0.0f;
     }
 }
 
