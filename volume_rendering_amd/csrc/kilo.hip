@@ -9,9 +9,12 @@
 //             number of live samples per ray
 //   scan      exclusive prefix sum of the counts (ray start offsets)
 //   compact   one wave per ray: live samples written in (ray, sample) order
-//             with their cell id; per-cell histogram
+//             with their cell id; per-cell histogram, whose running counts
+//             give each sample its slot in the cell's bucket
 //   cells     one workgroup: per-cell start offsets, tile counts, tile list
-//   scatter   live samples into per-cell buckets
+//   scatter   live samples into per-cell buckets (bucket order within a
+//             cell is arbitrary: each sample is its own matrix column and
+//             writes only its own entry)
 //   mlp       persistent waves over the tile list: each tile is up to 64
 //             (bf16) or 32 (f32) samples of one cell, evaluated by that
 //             cell's network read straight from global memory
@@ -26,6 +29,7 @@
 namespace nerf {
 
 constexpr int kScanBlock = 1024;  // elements per local-scan block (256 threads x 4)
+constexpr int kXcds = 8;          // accelerator complex dies; the persistent grid is a multiple
 
 // ---------------------------------------------------------------------------
 // Scans
@@ -196,11 +200,25 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
             live = classify(k, x, cell);
         }
         const unsigned long long m = __ballot(live);
+        // per-cell histogram, one atomic per distinct cell of the wave (the
+        // samples of a ray segment fall into a few neighbouring cells); the
+        // count it returns places each live sample in its cell's bucket
+        uint32_t slot = 0;
+        for (unsigned long long rem = m; rem;) {
+            const int leader = __ffsll((long long)rem) - 1;
+            const int c = __shfl(cell, leader, kWave);
+            const unsigned long long same = __ballot(live && cell == c);
+            uint32_t b = 0;
+            if (lane == leader) b = atomicAdd(&k.cell_count[c], (uint32_t)__popcll(same));
+            b = __shfl(b, leader, kWave);
+            if ((same >> lane) & 1ull) slot = b + (uint32_t)__popcll(same & below);
+            rem &= ~same;
+        }
         if (live) {
             const uint32_t e = pos + (uint32_t)__popcll(m & below);
             k.ent_ray[e] = (uint32_t)r;
             k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
-            atomicAdd(&k.cell_count[cell], 1u);
+            k.ent_slot[e] = slot;
         }
         pos += (uint32_t)__popcll(m);
     }
@@ -221,7 +239,6 @@ __global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells, in
         if (c < n_cells) {
             k.cell_start[c] = carry_s + es;
             k.tile_start[c] = carry_t + et;
-            k.cell_fill[c] = 0u;
         }
         carry_s += ts;
         carry_t += tt;
@@ -245,8 +262,7 @@ __global__ void __launch_bounds__(256) k_kilo_scatter(KiloArgs k, int64_t n_rays
     const uint32_t stride = gridDim.x * blockDim.x;
     for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const uint32_t c = k.ent_meta[e] & 0xFFFFu;
-        const uint32_t p = k.cell_start[c] + atomicAdd(&k.cell_fill[c], 1u);
-        k.bucket[p] = e;
+        k.bucket[k.cell_start[c] + k.ent_slot[e]] = e;
     }
 }
 
@@ -259,9 +275,16 @@ __global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int 
     constexpr int ES = seg_steps(net_layers(K)[0].s0, T::prec);
     constexpr int DS = seg_steps(net_layers(K)[4].s1, T::prec);
     const int lane = lane_id();
+    // The tile list is cell-major.  Workgroups are dealt to the 8 XCDs
+    // round robin (blockIdx % 8), so XCD x takes the x-th eighth of the list:
+    // the tiles of one cell then run on one XCD, close together in time, and
+    // that cell's network is fetched into one L2 once.
     const uint32_t total_tiles = k.tile_start[n_cells];
-    const uint32_t nwaves = gridDim.x * (blockDim.x / kWave);
-    for (uint32_t t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < total_tiles; t += nwaves) {
+    const uint32_t xcd = blockIdx.x % kXcds, bx = blockIdx.x / kXcds;
+    const uint32_t t_end = (uint32_t)((uint64_t)total_tiles * (xcd + 1) / kXcds);
+    const uint32_t nwaves = gridDim.x / kXcds * (blockDim.x / kWave);
+    for (uint32_t t = (uint32_t)((uint64_t)total_tiles * xcd / kXcds) + bx * (blockDim.x / kWave) + threadIdx.x / kWave;
+         t < t_end; t += nwaves) {
         const uint32_t c = k.tile_cell[t], off = k.tile_off[t];
         const uint32_t cs = k.cell_start[c], cnt = k.cell_start[c + 1] - cs;
         uint32_t e[SB];
@@ -281,8 +304,8 @@ __global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int 
             for (int q = 0; q < 3; ++q) v[sb][q] = R.d[q] / dn;
         }
         typename T::Op enc[ES][SB], denc[DS][SB];
-        enc_operands(enc, 10, x, a.use_pi != 0, lane);
-        enc_operands(denc, 4, v, a.use_pi != 0, lane);
+        enc_operands<10>(enc, x, a.use_pi != 0, lane);
+        enc_operands<4>(denc, v, a.use_pi != 0, lane);
         const char* packed = (const char*)k.cells + (size_t)c * k.cell_stride;
         GlobalStream<T, K> ws(packed, lane, 0);
         const float* bias = (const float*)(packed + net_bias_offset(K, T::prec, 0));
@@ -365,7 +388,7 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
     const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
                  o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
                  o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
-                 o_cf = take(4 * (size_t)n_cells), o_ts = take(4 * ((size_t)n_cells + 1)),
+                 o_sl = take(4 * max_live), o_ts = take(4 * ((size_t)n_cells + 1)),
                  o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
                  o_raw = take(16 * max_live);
     if (base && k) {
@@ -376,7 +399,7 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
         k->ent_meta = (uint32_t*)(base + o_em);
         k->cell_count = (uint32_t*)(base + o_cc);
         k->cell_start = (uint32_t*)(base + o_cs);
-        k->cell_fill = (uint32_t*)(base + o_cf);
+        k->ent_slot = (uint32_t*)(base + o_sl);
         k->tile_start = (uint32_t*)(base + o_ts);
         k->tile_cell = (uint32_t*)(base + o_tc);
         k->tile_off = (uint32_t*)(base + o_to);
@@ -402,7 +425,7 @@ void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int ad
     const int tile = bf16 ? 64 : 32;
     hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells, tile);
     hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n);
-    const dim3 persist(256 * 16);
+    const dim3 persist(256 * 16);  // a multiple of kXcds (the tile partition)
     if (bf16)
         hipLaunchKernelGGL(k_kilo_mlp<TBF16>, persist, dim3(256), 0, s, a, k, n_cells);
     else

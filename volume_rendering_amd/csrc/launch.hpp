@@ -54,9 +54,9 @@ struct KiloArgs {
     uint32_t* block_sums;  // [scan blocks + 1]
     uint32_t* ent_ray;     // [max_live]
     uint32_t* ent_meta;    // [max_live]: sample << 16 | cell
+    uint32_t* ent_slot;    // [max_live]: place in the cell's bucket
     uint32_t* cell_count;  // [n_cells]
     uint32_t* cell_start;  // [n_cells + 1]
-    uint32_t* cell_fill;   // [n_cells]
     uint32_t* tile_start;  // [n_cells + 1]
     uint32_t* tile_cell;   // [max_tiles]
     uint32_t* tile_off;    // [max_tiles]

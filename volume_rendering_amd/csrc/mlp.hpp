@@ -183,18 +183,30 @@ struct LdsStream {
 };
 
 // GlobalStream: each wave reads its tiles straight from global memory (for
-// waves that evaluate different networks).
-template <class T, int KIND>
+// waves that evaluate different networks), LOOK tiles ahead of use.
+template <class T, int KIND, int LOOK = 6>
 struct GlobalStream {
+    using Op = typename T::Op;
     static constexpr int TB = tile_bytes(T::prec);
-    const char* base;
-    int lane;
-    __device__ __forceinline__ GlobalStream(const char* packed, int lane_, int) : base(packed), lane(lane_) {}
-    __device__ __forceinline__ void begin() {}
+    static constexpr int NT = (int)(net_tiles_bytes(KIND, T::prec) / TB);  // real tiles, no padding
+    const NERF_AS_GLOBAL char* base;  // this lane's bytes of tile 0
+    Op buf[LOOK];
+    __device__ __forceinline__ GlobalStream(const char* packed, int lane, int)
+        : base((const NERF_AS_GLOBAL char*)packed + lane * (int)sizeof(Op)) {}
     template <int TILE>
-    __device__ __forceinline__ typename T::Op get() {
-        const NERF_AS_GLOBAL char* p = (const NERF_AS_GLOBAL char*)base + TILE * TB + lane * (int)sizeof(typename T::Op);
-        return *reinterpret_cast<const NERF_AS_GLOBAL typename T::Op*>(p);
+    __device__ __forceinline__ Op read() const {
+        return *reinterpret_cast<const NERF_AS_GLOBAL Op*>(base + TILE * TB);
+    }
+    __device__ __forceinline__ void begin() {
+        static_for<0, LOOK>([&](auto t) {
+            if constexpr (t.value < NT) buf[t.value] = read<t.value>();
+        });
+    }
+    template <int TILE>
+    __device__ __forceinline__ Op get() {
+        const Op cur = buf[TILE % LOOK];
+        if constexpr (TILE + LOOK < NT) buf[TILE % LOOK] = read<TILE + LOOK>();
+        return cur;
     }
 };
 
@@ -459,23 +471,41 @@ __device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh
 // Input operands
 // ---------------------------------------------------------------------------
 
-// Value pair P of the frequency encoding of (x0, x1, x2) with L frequencies.
-__device__ __forceinline__ void enc_pair_value(int P, int L, float x0, float x1, float x2, bool use_pi, float& a,
-                                               float& b) {
-    if (P < 3 * L) {
-        const int k = P / 3;
-        const int ax = P - 3 * k;
-        const float v = ax == 0 ? x0 : (ax == 1 ? x1 : x2);
-        const float arg = ldexpf(v, k);  // exact
-        if (use_pi)
-            sincospif(arg, &a, &b);
-        else
-            sincosf(arg, &a, &b);
-    } else if (P == 3 * L) {
-        a = x0;
-        b = x1;
-    } else if (P == 3 * L + 1) {
-        a = x2;
+// Frequency encoding of (x0, x1, x2) with L frequencies, as value pairs:
+// pair P = 3k + a (k < L) is (sin, cos) of 2^k x_a (times pi when use_pi),
+// pair 3L is (x0, x1), pair 3L + 1 is (x2, 0), later pairs are zero.
+struct PairSrc {
+    int kind;  // 0 sin/cos, 1 (x0, x1), 2 (x2, 0), 3 zero
+    int k, ax;
+};
+NERF_HD constexpr PairSrc pair_src(int P, int L) {
+    return P < 3 * L ? PairSrc{0, P / 3, P % 3}
+                     : (P == 3 * L ? PairSrc{1, 0, 0} : (P == 3 * L + 1 ? PairSrc{2, 0, 0} : PairSrc{3, 0, 0}));
+}
+
+// (sin, cos) of pi*arg (PI) or of arg.  With pi, arg/2 is a number of
+// revolutions: removing its nearest integer is exact in float32, and the
+// hardware sine and cosine take the remaining [-1/2, 1/2] revolution.
+// Without pi the library's accurately reduced sincosf is used.
+template <bool PI>
+__device__ __forceinline__ void enc_sincos(float arg, float& s, float& c) {
+    if constexpr (PI) {
+        const float t = arg * 0.5f;
+        const float r = t - rintf(t);
+        s = __builtin_amdgcn_sinf(r);
+        c = __builtin_amdgcn_cosf(r);
+    } else {
+        sincosf(arg, &s, &c);
+    }
+}
+
+template <int KIND>
+__device__ __forceinline__ void enc_plain(const float (&x)[3], float& a, float& b) {
+    if constexpr (KIND == 1) {
+        a = x[0];
+        b = x[1];
+    } else if constexpr (KIND == 2) {
+        a = x[2];
         b = 0.0f;
     } else {
         a = 0.0f;
@@ -483,37 +513,66 @@ __device__ __forceinline__ void enc_pair_value(int P, int L, float x0, float x1,
     }
 }
 
-template <int NS>
-__device__ __forceinline__ void enc_operands(bf16x8 (&enc)[NS][2], int L, const float (&x)[2][3], bool use_pi,
-                                             int lane) {
-    const int h = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            bf16x8 v;
-#pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                float a, b;
-                enc_pair_value(8 * s + 4 * h + jp, L, x[sb][0], x[sb][1], x[sb][2], use_pi, a, b);
-                v[2 * jp] = to_bf16(a);
-                v[2 * jp + 1] = to_bf16(b);
-            }
-            enc[s][sb] = v;
-        }
+// Pair P0 for lanes of half 0, P1 for half 1 (h = lane / 32): the argument
+// is chosen per half first, so one sine/cosine serves both halves.
+template <int P0, int P1, int L, bool PI>
+__device__ __forceinline__ void enc_pair(int h, const float (&x)[3], float& a, float& b) {
+    constexpr PairSrc s0 = pair_src(P0, L), s1 = pair_src(P1, L);
+    if constexpr (s0.kind == 0 && s1.kind == 0) {
+        const float arg = h ? x[s1.ax] * (float)(1 << s1.k) : x[s0.ax] * (float)(1 << s0.k);  // exact scaling
+        enc_sincos<PI>(arg, a, b);
+    } else if constexpr (s0.kind == 0 || s1.kind == 0) {
+        constexpr PairSrc st = s0.kind == 0 ? s0 : s1, sp = s0.kind == 0 ? s1 : s0;
+        float ta, tb, pa, pb;
+        enc_sincos<PI>(x[st.ax] * (float)(1 << st.k), ta, tb);
+        enc_plain<sp.kind>(x, pa, pb);
+        const bool trig = (h != 0) == (s1.kind == 0);
+        a = trig ? ta : pa;
+        b = trig ? tb : pb;
+    } else {
+        float a0, b0, a1, b1;
+        enc_plain<s0.kind>(x, a0, b0);
+        enc_plain<s1.kind>(x, a1, b1);
+        a = h ? a1 : a0;
+        b = h ? b1 : b0;
+    }
 }
 
-template <int NS>
-__device__ __forceinline__ void enc_operands(float (&enc)[NS][1], int L, const float (&x)[1][3], bool use_pi,
-                                             int lane) {
+template <int L, bool PI, int NS>
+__device__ __forceinline__ void enc_operands_t(bf16x8 (&enc)[NS][2], const float (&x)[2][3], int lane) {
     const int h = lane >> 5;
-#pragma unroll
-    for (int p = 0; p < NS / 2; ++p) {
+    static_for<0, NS>([&](auto s) {
+        static_for<0, 2>([&](auto sb) {
+            bf16x8 v;
+            static_for<0, 4>([&](auto jp) {
+                float a, b;
+                enc_pair<8 * s.value + jp.value, 8 * s.value + 4 + jp.value, L, PI>(h, x[sb.value], a, b);
+                v[2 * jp.value] = to_bf16(a);
+                v[2 * jp.value + 1] = to_bf16(b);
+            });
+            enc[s.value][sb.value] = v;
+        });
+    });
+}
+
+template <int L, bool PI, int NS>
+__device__ __forceinline__ void enc_operands_t(float (&enc)[NS][1], const float (&x)[1][3], int lane) {
+    const int h = lane >> 5;
+    static_for<0, NS / 2>([&](auto p) {
         float a, b;
-        enc_pair_value(2 * p + h, L, x[0][0], x[0][1], x[0][2], use_pi, a, b);
-        enc[2 * p][0] = a;
-        enc[2 * p + 1][0] = b;
-    }
+        enc_pair<2 * p.value, 2 * p.value + 1, L, PI>(h, x[0], a, b);
+        enc[2 * p.value][0] = a;
+        enc[2 * p.value + 1][0] = b;
+    });
+}
+
+// Operands of the encoded input for the packer's slot order.
+template <int L, class Op, int NS, int SB>
+__device__ __forceinline__ void enc_operands(Op (&enc)[NS][SB], const float (&x)[SB][3], bool use_pi, int lane) {
+    if (use_pi)
+        enc_operands_t<L, true>(enc, x, lane);
+    else
+        enc_operands_t<L, false>(enc, x, lane);
 }
 
 // Operands of a segment read from a row-major float32 matrix (`row[sb]`

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
         for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
             for (int k = 0; k < 3; ++k) v[sb][k] = d[k] / dn;
-        enc_operands(denc, Fam::LDIR, v, a.use_pi != 0, lane);
+        enc_operands<Fam::LDIR>(denc, v, a.use_pi != 0, lane);
     }
 
     const int nc = a.n_coarse, nf = a.n_fine;
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
                 for (int k = 0; k < 3; ++k) x[sb][k] = __fadd_rn(o[k], __fmul_rn(z, d[k]));
             }
             typename T::Op enc[ES][SB];
-            enc_operands(enc, Fam::LPOS, x, a.use_pi != 0, lane);
+            enc_operands<Fam::LPOS>(enc, x, a.use_pi != 0, lane);
             f32x16 sig[SB], rgb[SB];
             const char* pk = opaque(packed);
             LdsStream<T, KIND, kRenderRing> ws(pk, lane, wave);
