@@ -186,7 +186,7 @@ def test_composite(v, N, white):
     assert max_abs(host(w), rw) <= 1e-5
 
 
-@pytest.mark.parametrize("nc,nf", [(64, 128), (16, 32), (130, 126), (3, 1)])
+@pytest.mark.parametrize("nc,nf", [(64, 128), (16, 32), (130, 126), (3, 1), (64, 192)])
 def test_sample_pdf_bit_exact(v, nc, nf):
     say(f"sample_pdf nc={nc} nf={nf}")
     torch = torch_cuda()
@@ -204,6 +204,26 @@ def test_sample_pdf_bit_exact(v, nc, nf):
     v.nerf_sample_pdf(dev(zc), dev(w), nf, 11, 1000, zf, bins, z2)
     rzf, ridx, rz2 = osamp.hierarchical_fine_samples(zc, w, nf, 11, 1000)
     assert np.array_equal(host(bins), ridx)
+    assert np.array_equal(host(zf), rzf)
+    assert np.array_equal(host(z2), rz2)
+
+
+def test_sample_pdf_unordered_coarse(v):
+    """Coarse samples given in descending or shuffled order (the merged output
+    is still the ascending union): exercises the merge's sorting of the first
+    set, which stratified samples never need."""
+    say("sample_pdf with unordered coarse samples")
+    R, nc, nf = 200, 64, 128
+    g = np.random.default_rng(7)
+    near, far = _near_far(R)
+    zc = osamp.stratified(near, far, nc, 5, True, 0)
+    zc[0::3] = zc[0::3, ::-1]
+    for i in range(1, R, 3):
+        zc[i] = zc[i, g.permutation(nc)]
+    w = g.random((R, nc)).astype(np.float32)
+    zf, bins, z2 = empty((R, nf)), torch_cuda().empty((R, nf), dtype=torch_cuda().int32, device="cuda"), empty((R, nc + nf))
+    v.nerf_sample_pdf(dev(zc), dev(w), nf, 3, 0, zf, bins, z2)
+    rzf, ridx, rz2 = osamp.hierarchical_fine_samples(zc, w, nf, 3, 0)
     assert np.array_equal(host(zf), rzf)
     assert np.array_equal(host(z2), rz2)
 

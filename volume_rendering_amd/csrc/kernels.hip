@@ -215,19 +215,7 @@ __global__ void __launch_bounds__(256) k_sample_pdf(const float* __restrict__ zc
                    bin_out ? bin_out + r * nf : nullptr);
     if (zf_out)
         for (int m = lane; m < nf; m += kWave) zf_out[r * nf + m] = L.u[nc + m];
-    if (z2_out) {
-        // rank merge straight to global memory
-        const int n2 = nc + nf;
-        for (int e = lane; e < n2; e += kWave) {
-            const float v = L.u[e];
-            int rank = 0;
-            for (int q = 0; q < n2; ++q) {
-                const float w = L.u[q];
-                rank += (w < v) || (w == v && q < e);
-            }
-            z2_out[r * n2 + rank] = v;
-        }
-    }
+    if (z2_out) merge_samples(L.u, nc, L.u + nc, nf, L.bins, z2_out + r * (nc + nf));
 }
 
 void launch_sample_pdf(const float* zc, const float* wc, int64_t n_rays, int nc, int nf, uint64_t seed,

@@ -122,19 +122,104 @@ __device__ __forceinline__ void sample_pdf_ray(const float* zc, const float* wc,
     wave_lds_sync();
 }
 
-// Ascending merge of u[0..n) into out[0..n) by rank: element e goes to
-// #{q : u_q < u_e} + #{q < e : u_q == u_e}.
-__device__ __forceinline__ void merge_rank(const float* u, int n, float* out) {
+// Ascending sort of in[0..n), n <= 64*K, into out[0..n) by a bitonic
+// network across the wave: element 64k + lane is held in v[k] (padding
+// +inf); partners closer than 64 are exchanged between lanes, farther ones
+// between registers of a lane.  min/max return one of their operands, so the
+// output is exactly the sorted input.
+template <int K>
+__device__ __forceinline__ void wave_sort(const float* in, int n, float* out) {
+    constexpr int LOG = K == 1 ? 6 : (K == 2 ? 7 : 8);
+    static_assert(64 * K == (1 << LOG), "K in {1, 2, 4}");
     const int lane = lane_id();
-    for (int e = lane; e < n; e += kWave) {
-        const float v = u[e];
-        int rank = 0;
-        for (int q = 0; q < n; ++q) {
-            const float w = u[q];
-            rank += (w < v) || (w == v && q < e);
-        }
-        out[rank] = v;
+    float v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = 64 * k + lane;
+        v[k] = i < n ? in[i] : __builtin_inff();
     }
+#pragma unroll
+    for (int st = 1; st <= LOG; ++st) {
+#pragma unroll
+        for (int t = st - 1; t >= 0; --t) {
+            const int kk = 1 << st, j = 1 << t;
+            float nv[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int i = 64 * k + lane;
+                const float p = j < kWave ? __shfl_xor(v[k], j, kWave) : v[k ^ (j / kWave)];
+                const bool take_min = ((i & kk) == 0) == ((i & j) == 0);
+                nv[k] = take_min ? fminf(v[k], p) : fmaxf(v[k], p);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = nv[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = 64 * k + lane;
+        if (i < n) out[i] = v[k];
+    }
+}
+
+__device__ __forceinline__ void wave_sort_n(const float* in, int n, float* out) {
+    if (n <= 64)
+        wave_sort<1>(in, n, out);
+    else if (n <= 128)
+        wave_sort<2>(in, n, out);
+    else
+        wave_sort<4>(in, n, out);
+}
+
+// Merge of ascending a[0..na) and b[0..nb) into out[0..na+nb): a[e] goes to
+// e + #{b < a[e]}, b[m] to m + #{a <= b[m]}, a permutation that lists the
+// union in ascending order (equal values are equal floats, so which of two
+// equal elements lands first does not change the output).
+__device__ __forceinline__ void merge_sorted(const float* a, int na, const float* b, int nb, float* out) {
+    const int lane = lane_id();
+    for (int e = lane; e < na; e += kWave) {
+        const float v = a[e];
+        int lo = 0, hi = nb;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (b[mid] < v)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        out[e + lo] = v;
+    }
+    for (int m = lane; m < nb; m += kWave) {
+        const float v = b[m];
+        int lo = 0, hi = na;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (a[mid] <= v)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        out[m + lo] = v;
+    }
+}
+
+// Ascending union of the first-pass samples zc[0..nc) and the resampled
+// zf[0..nf) into out (the input to the second pass).  Jittered stratified
+// samples are ascending already (checked; sorted here otherwise); the
+// resampled ones are sorted first.  tmp holds nc + nf floats.
+__device__ __forceinline__ void merge_samples(const float* zc, int nc, const float* zf, int nf, float* tmp,
+                                              float* out) {
+    const int lane = lane_id();
+    bool asc = true;
+    for (int e = lane; e + 1 < nc; e += kWave) asc = asc && (zc[e] <= zc[e + 1]);
+    const float* A = zc;
+    if (__ballot(!asc) != 0ull) {
+        wave_sort_n(zc, nc, tmp + nf);
+        A = tmp + nf;
+    }
+    wave_sort_n(zf, nf, tmp);
+    wave_lds_sync();
+    merge_sorted(A, nc, tmp, nf, out);
     wave_lds_sync();
 }
 

@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
             }
         } else {
             sample_pdf_ray(S.zc, S.w, nc, nf, a.seed, ray, S.bins, S.cdf, S.zc + nc, nullptr);
-            merge_rank(S.zc, nc + nf, S.z2);
+            merge_samples(S.zc, nc, S.zc + nc, nf, S.bins, S.z2);
         }
     }
 }
