@@ -129,16 +129,23 @@ struct LdsStream {
     __device__ __forceinline__ LdsStream(const char* packed, int lane_, int wave)
         : src(packed + wave * (kChunkDma * 1024) + lane_ * 16), dst(wave * (kChunkDma * 1024)), lane(lane_) {}
 
-    template <int K>
-    __device__ __forceinline__ void issue() {
+    // One copy of kilobyte I of this wave's share of chunk K.  All pieces of a
+    // chunk share one global address register and one LDS base (M0); the
+    // instruction's immediate offset, applied to both addresses, selects the
+    // piece.  (A new M0 per piece makes each copy wait for the previous one
+    // to leave the wave.)
+    template <int K, int I>
+    __device__ __forceinline__ void piece() {
+        static_assert(I * 1024 < 4096, "immediate offset range");
         if constexpr (K < NCH) {
             const char* p = src + (size_t)K * kChunkBytes;  // within the padded region
             char* slot = ring_slot<K % NBUF>() + dst;
-#pragma unroll
-            for (int i = 0; i < kChunkDma; ++i)
-                __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)(p + i * 1024),
-                                                 (NERF_AS_LDS void*)(slot + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)p, (NERF_AS_LDS void*)slot, 16, I * 1024, 0);
         }
+    }
+    template <int K>
+    __device__ __forceinline__ void issue() {
+        static_for<0, kChunkDma>([&](auto i) { piece<K, i.value>(); });
     }
 
     template <int K>
