@@ -1,12 +1,19 @@
 """Throughput of the NeRF forward-render hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload hierarchical|coarse|tiny|hash|kilo]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid]
                     [--dtype bf16|f32] [--no-cpu-baseline]
 
 A step is one ``nerf_render`` over the whole workload with rays, weights
 and tables already resident in HBM.  Default workload: the hierarchical
 render, 4 poses x 800x800 rays (focal 1110), 64 stratified + 128
 inverse-CDF samples per ray, 8x256 coarse and fine networks in bfloat16.
+
+The standalone workloads time one call of a single step against the HBM
+roofline: ``encode`` the frequency encoding (L = 10, with the input) of the
+coarse workload's 81.92M sample points, ``composite`` the compositing of its
+1.28M rays x 64 samples, ``hashgrid`` the 16-level hash-grid encoding of
+2^22 points.
 
 Prints one JSON line: rays/s (``value``), samples/s, the dominant kernel's
 achieved throughput against its roofline (timed live with HIP events on
@@ -45,7 +52,12 @@ WORKLOADS = {
     "tiny": dict(poses=1, hemi=False, H=32, W=32, focal=40.0, nc=16, nf=0, kind=2, chunk=0),
     "hash": dict(poses=1, hemi=True, H=256, W=256, focal=355.2, nc=128, nf=0, kind=4, chunk=0),
     "kilo": dict(poses=1, hemi=True, H=800, W=800, focal=1110.0, nc=192, nf=0, kind=3, chunk=0),
+    # standalone steps (kind 0): coarse workload's rays and samples, or 2^22 grid queries
+    "encode": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0),
+    "composite": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0),
+    "hashgrid": dict(points=1 << 22, kind=0),
 }
+HBM_PEAK_GBS = 8000.0
 
 
 def parse():
@@ -114,6 +126,8 @@ def main():
     from volume_rendering_amd import _binding as B
 
     wl = dict(WORKLOADS[args.workload])
+    if wl["kind"] == 0:
+        return standalone(args, wl)
     if args.poses > 0:
         wl["poses"] = args.poses
     if args.n_fine >= 0:
@@ -255,6 +269,149 @@ def main():
             base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, coarse_p, fine_p, args.cpu_seconds)
         out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
+
+
+def _timed(args, step, torch):
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_kernel = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    return ms_step, ms_kernel
+
+
+def _cpu_rate(fn, n_total, target_s, unit, what):
+    """Runs the oracle on growing evenly spaced samples until it takes about
+    target_s seconds; returns the cpu_baseline record."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = 1024
+    while True:
+        sel = np.linspace(0, n_total - 1, min(n, n_total)).astype(np.int64)
+        t = time.perf_counter()
+        fn(sel)
+        dt = time.perf_counter() - t
+        if dt >= 0.3 * target_s or len(sel) == n_total:
+            break
+        n = int(n * min(16.0, max(2.0, target_s / max(dt, 1e-3))))
+    return {"value": len(sel) / dt, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(sel)} {what} evenly spaced over the workload, float64 oracle, {dt:.1f} s"}
+
+
+def standalone(args, wl):
+    """One standalone step of the path against the HBM roofline."""
+    import torch
+    import seeded_inputs as si
+    import volume_rendering_amd as v
+
+    dev = torch.device("cuda")
+    name = args.workload
+    if name in ("encode", "composite"):
+        P = si.poses(wl["poses"], seed=0, hemisphere=wl["hemi"])
+        H, W, f = wl["H"], wl["W"], wl["focal"]
+        R, N = wl["poses"] * H * W, wl["nc"]
+        ro = torch.empty((R, 3), device=dev)
+        rd = torch.empty((R, 3), device=dev)
+        for p in range(wl["poses"]):
+            v.nerf_gen_rays(P[p], W, H, f, f, 0.5 * W, 0.5 * H, ro[p * H * W:(p + 1) * H * W],
+                            rd[p * H * W:(p + 1) * H * W])
+        near = torch.full((R,), 2.0, device=dev)
+        far = torch.full((R,), 6.0, device=dev)
+        z = torch.empty((R, N), device=dev)
+        v.nerf_sample_stratified(near, far, N, 0, 0, True, z)
+    if name == "encode":
+        x = (ro[:, None, :] + z[:, :, None] * rd[:, None, :]).reshape(-1, 3).contiguous()
+        n = x.shape[0]
+        L = 10
+        out = torch.empty((n, 3 + 6 * L), device=dev)
+
+        def step():
+            v.nerf_encode_freq(x, L, True, True, 0, out)
+
+        units, unit = n, "points/s"
+        bytes_per_unit = 12 + 4 * (3 + 6 * L)
+        kernel = "k_encode_freq"
+        config = {"workload": name, "points": n, "L": L, "include_input": True, "out": "f32",
+                  "source": "8 poses x 400x400 rays x 64 stratified samples"}
+        data = "synthetic: seeded hemisphere poses, jittered stratified depths"
+        if not args.no_cpu_baseline:
+            from oracle import encoding as oenc
+            xh = x.cpu().numpy()
+            base = _cpu_rate(lambda sel: oenc.freq_encode(xh[sel], L), n, args.cpu_seconds, "points/s", "points")
+    elif name == "composite":
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        raw = (torch.randn((R, N, 4), device=dev, generator=g) * 3.0).contiguous()
+        rgb = torch.empty((R, 3), device=dev)
+        depth = torch.empty((R,), device=dev)
+        acc = torch.empty((R,), device=dev)
+        w = torch.empty((R, N), device=dev)
+
+        def step():
+            v.nerf_composite(raw, z, rd, False, rgb, depth, acc, w)
+
+        units, unit = R * N, "samples/s"
+        bytes_per_unit = 16 + 4 + 4 + 32.0 / N  # raw, z, weights out per sample; rays_d + rgb, depth, acc per ray
+        kernel = "k_composite"
+        config = {"workload": name, "rays": R, "samples_per_ray": N, "weights_out": True,
+                  "source": "8 poses x 400x400 rays x 64 stratified samples"}
+        data = "synthetic: seeded hemisphere poses, jittered depths, raw ~ 3 N(0,1) (seeded device generator)"
+        if not args.no_cpu_baseline:
+            from oracle import composite as ocomp
+            raw_h, z_h, d_h = raw.cpu().numpy(), z.cpu().numpy(), rd.cpu().numpy()
+            base = _cpu_rate(lambda sel: ocomp.volume_render(raw_h[sel], z_h[sel], d_h[sel]), R, args.cpu_seconds,
+                             "samples/s", "rays x 64 samples")
+            base["value"] *= N
+    else:  # hashgrid
+        n = wl["points"]
+        grid = v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048)
+        tabs = si.hash_tables(list(grid.size)[:16], seed=0, scale=1e-4)
+        tdev = torch.from_numpy(np.concatenate(tabs, 0)).to(dev)
+        grid.tables = tdev.data_ptr()
+        xh = si.query_points(n, seed=0)
+        x = torch.from_numpy(xh).to(dev)
+        out = torch.empty((n, 32), device=dev)
+
+        def step():
+            v.nerf_encode_hashgrid(x, grid, out)
+
+        units, unit = n, "points/s"
+        bytes_per_unit = 12 + 128  # point in, 32 float32 features out; table gathers are cache traffic
+        kernel = "k_encode_hash"
+        config = {"workload": name, "points": n, "levels": 16, "table_size": 2 ** 19, "n_min": 16, "n_max": 2048}
+        data = "synthetic: seeded uniform points in the unit cube, tables U(-1e-4, 1e-4) float16"
+        if not args.no_cpu_baseline:
+            from oracle import encoding as oenc
+            og = oenc.hashgrid_3d()
+            base = _cpu_rate(lambda sel: og.encode(xh[sel], tabs), n, args.cpu_seconds, "points/s", "points")
+
+    ms_step, ms_kernel = _timed(args, step, torch)
+    achieved = bytes_per_unit * units / (ms_kernel * 1e-3) / 1e9
+    out_rec = {
+        "metric": {"encode": "points/s, frequency encoding (HBM GB/s %)",
+                   "composite": "samples/s, compositing (HBM GB/s %)",
+                   "hashgrid": "points/s, hash-grid encoding (HBM GB/s %)"}[name],
+        "value": units / (ms_step * 1e-3), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": data, "config": config,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": MEASURED_TRAFFIC.get((name, "f32")),
+                     "kernel": kernel, "kernel_ms": ms_kernel, "bytes_per_launch": bytes_per_unit * units},
+    }
+    if not args.no_cpu_baseline:
+        out_rec["cpu_baseline"] = base
+    print(json.dumps(out_rec), flush=True)
 
 
 if __name__ == "__main__":

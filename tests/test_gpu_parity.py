@@ -86,6 +86,11 @@ def test_encode_freq(v, L, use_pi):
     hb = host(ob.float())
     # bf16 output is the float32 value rounded to nearest even: within half a bf16 ulp of the exact value
     assert np.all(np.abs(hb - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+    # an output that is not 16-byte aligned takes the scalar stores: same values
+    big = empty(5003 * (3 + 6 * L) + 1)
+    om = big[1:].view(5003, 3 + 6 * L)
+    v.nerf_encode_freq(dev(x), L, True, use_pi, 0, om)
+    assert np.array_equal(host(om), host(out))
 
 
 def test_encode_sh16(v):
@@ -167,7 +172,8 @@ def test_mlp_standalone(v, kind, dtype):
 # Compositing and resampling
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N,white", [(64, False), (192, True), (16, False), (100, False)])
+@pytest.mark.parametrize("N,white", [(64, False), (192, True), (16, False), (100, False), (1, False), (3, True),
+                                     (257, False)])
 def test_composite(v, N, white):
     say(f"composite N={N}")
     R = 777
@@ -184,6 +190,10 @@ def test_composite(v, N, white):
     assert max_abs(host(acc), ra) <= ACC_TOL
     assert max_abs(host(depth), rd_) <= DEPTH_TOL
     assert max_abs(host(w), rw) <= 1e-5
+    # without the weights output the other outputs are unchanged
+    rgb2, depth2, acc2 = empty((R, 3)), empty(R), empty(R)
+    v.nerf_composite(dev(raw), dev(z), dev(d), white, rgb2, depth2, acc2)
+    assert np.array_equal(host(rgb2), host(rgb)) and np.array_equal(host(acc2), host(acc))
 
 
 @pytest.mark.parametrize("nc,nf", [(64, 128), (16, 32), (130, 126), (3, 1), (64, 192)])

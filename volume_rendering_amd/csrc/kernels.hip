@@ -63,58 +63,122 @@ void launch_stratified(const float* tn, const float* tf, int64_t n_rays, int n, 
 }
 
 // ===========================================================================
-// Frequency encoding: one thread per (point, frequency) writes the in_dim
-// sines and in_dim cosines of that frequency; frequency slot 0 of threads
-// with include_input also copies the input.
+// Frequency encoding.  A workgroup encodes pw consecutive points, one thread
+// per point, into a float32 stage in LDS (row stride = width, odd for the
+// usual widths, so a wave's rows fall in distinct banks); the workgroup then
+// streams the points' rows, which are contiguous in the output, with
+// aligned 16-byte stores.
 // ===========================================================================
-template <typename OutT>
-__device__ __forceinline__ void put(OutT* p, float v);
-template <>
-__device__ __forceinline__ void put<float>(float* p, float v) {
-    *p = v;
+constexpr int kEncStageBytes = 65536;
+
+// Points per workgroup: a multiple of 8 (16-byte aligned rows of the block
+// for any width and either output type) whose stage fits kEncStageBytes.
+__host__ __device__ inline int enc_points_per_block(int width) {
+    const int pw = kEncStageBytes / (4 * width);
+    return (pw >= 256 ? 256 : pw) / 8 * 8;
 }
-template <>
-__device__ __forceinline__ void put<__bf16>(__bf16* p, float v) {
-    *p = to_bf16(v);
+
+// (sin(pi t), cos(pi t)).  t = q/2 + r with q = rint(2t) and |r| <= 1/4, both
+// exact in float32; sin(pi r) and cos(pi r) from their Taylor series through
+// degree 9 and 10 (truncation below 2.5e-8 for |pi r| <= pi/4), evaluated by
+// Horner's rule; the quadrant q mod 4 rotates the pair.
+__device__ __forceinline__ void sincospi_taylor(float t, float& s, float& c) {
+    const float q = rintf(2.0f * t);
+    const float r = fmaf(-0.5f, q, t);
+    const float r2 = r * r;
+    constexpr float a1 = 3.14159265358979312f, a3 = -5.16771278004996937f, a5 = 2.55016403987734508f,
+                    a7 = -0.599264529320791883f, a9 = 0.082145886611128191f;  // pi^j (-1)^((j-1)/2) / j!
+    constexpr float b2 = -4.934802200544679f, b4 = 4.0587121264167676f, b6 = -1.33526276885458928f,
+                    b8 = 0.235330630358893123f, b10 = -0.0258068913900140508f;  // pi^j (-1)^(j/2) / j!
+    const float S = r * fmaf(fmaf(fmaf(fmaf(a9, r2, a7), r2, a5), r2, a3), r2, a1);
+    const float C = fmaf(fmaf(fmaf(fmaf(fmaf(b10, r2, b8), r2, b6), r2, b4), r2, b2), r2, 1.0f);
+    const int qi = (int)(q - 4.0f * floorf(q * 0.25f));  // q mod 4, exact for any float q
+    const float ss = (qi & 1) ? C : S, cc = (qi & 1) ? S : C;
+    s = (qi & 2) ? -ss : ss;
+    c = ((qi + 1) & 2) ? -cc : cc;
+}
+
+__device__ __forceinline__ void enc_store16(float* dst, const float* src) {
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+}
+__device__ __forceinline__ void enc_store16(__bf16* dst, const float* src) {
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = to_bf16(src[j]);
+    *reinterpret_cast<bf16x8*>(dst) = v;
+}
+__device__ __forceinline__ void enc_store1(float* dst, float v) { *dst = v; }
+__device__ __forceinline__ void enc_store1(__bf16* dst, float v) { *dst = to_bf16(v); }
+
+// One point's row: [x (inc)] then for k < L: sin(2^k x_a) for a < D, then
+// cos(2^k x_a) for a < D (times pi with use_pi).
+template <int D>
+__device__ __forceinline__ void enc_row(const float* xp, int d, int L, int inc, int use_pi, float* o) {
+    constexpr int DD = D > 0 ? D : 4;
+    const int dn = D > 0 ? D : d;
+    float xv[DD];
+#pragma unroll
+    for (int a = 0; a < DD; ++a) xv[a] = a < dn ? xp[a] : 0.0f;
+    if (inc) {
+#pragma unroll
+        for (int a = 0; a < DD; ++a)
+            if (a < dn) o[a] = xv[a];
+        o += dn;
+    }
+    for (int k = 0; k < L; ++k, o += 2 * dn) {
+#pragma unroll
+        for (int a = 0; a < DD; ++a) {
+            if (a < dn) {
+                const float arg = ldexpf(xv[a], k);  // exact
+                float sn, cs;
+                if (use_pi)
+                    sincospi_taylor(arg, sn, cs);
+                else
+                    sincosf(arg, &sn, &cs);
+                o[a] = sn;
+                o[dn + a] = cs;
+            }
+        }
+    }
 }
 
 template <typename OutT>
 __global__ void __launch_bounds__(256) k_encode_freq(const float* __restrict__ x, int64_t n, int d, int L, int inc,
-                                                     int use_pi, OutT* __restrict__ out) {
-    const int per = L + (inc ? 1 : 0);
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n * per) return;
-    const int64_t p = t / per;
-    const int q = (int)(t - p * per);
-    const int width = d * (inc + 2 * L);
-    OutT* o = out + p * width;
-    const float* xp = x + p * d;
-    if (inc && q == 0) {
-        for (int a = 0; a < d; ++a) put(o + a, xp[a]);
-        return;
-    }
-    const int k = q - (inc ? 1 : 0);
-    OutT* ok = o + d * inc + 2 * d * k;
-    for (int a = 0; a < d; ++a) {
-        const float arg = ldexpf(xp[a], k);
-        float sn, cs;
-        if (use_pi)
-            sincospif(arg, &sn, &cs);
+                                                     int use_pi, int pw, int vec, OutT* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) float enc_stage[];
+    const int width = d * ((inc ? 1 : 0) + 2 * L);
+    const int64_t p0 = (int64_t)blockIdx.x * pw;
+    const int np = (int)((n - p0) < pw ? (n - p0) : pw);
+    for (int pl = threadIdx.x; pl < np; pl += blockDim.x) {
+        const float* xp = x + (p0 + pl) * d;
+        float* o = enc_stage + pl * width;
+        if (d == 3)
+            enc_row<3>(xp, d, L, inc, use_pi, o);
         else
-            sincosf(arg, &sn, &cs);
-        put(ok + a, sn);
-        put(ok + d + a, cs);
+            enc_row<0>(xp, d, L, inc, use_pi, o);
     }
+    __syncthreads();
+    constexpr int VEC = 16 / (int)sizeof(OutT);
+    OutT* dst = out + p0 * width;  // 16-byte aligned when out is (vec): pw is a multiple of 8
+    const int total = np * width, nv = vec ? total / VEC : 0;
+    for (int i = threadIdx.x; i < nv; i += blockDim.x) enc_store16(dst + i * VEC, enc_stage + i * VEC);
+    for (int i = nv * VEC + threadIdx.x; i < total; i += blockDim.x) enc_store1(dst + i, enc_stage[i]);
 }
 
 void launch_encode_freq(const float* x, int64_t n, int d, int L, int inc, int use_pi, int bf16, void* out,
                         hipStream_t s) {
-    const int64_t tot = n * (L + (inc ? 1 : 0));
-    const dim3 g((unsigned)((tot + 255) / 256));
+    const int width = d * ((inc ? 1 : 0) + 2 * L);
+    const int pw = enc_points_per_block(width);
+    const int threads = (pw + 63) / 64 * 64;  // one thread per point
+    const dim3 g((unsigned)((n + pw - 1) / pw));
+    const size_t lds = (size_t)pw * width * sizeof(float);
+    const int vec = (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
     if (bf16)
-        hipLaunchKernelGGL(k_encode_freq<__bf16>, g, dim3(256), 0, s, x, n, d, L, inc, use_pi, (__bf16*)out);
+        hipLaunchKernelGGL(k_encode_freq<__bf16>, g, dim3(threads), lds, s, x, n, d, L, inc, use_pi, pw, vec,
+                           (__bf16*)out);
     else
-        hipLaunchKernelGGL(k_encode_freq<float>, g, dim3(256), 0, s, x, n, d, L, inc, use_pi, (float*)out);
+        hipLaunchKernelGGL(k_encode_freq<float>, g, dim3(threads), lds, s, x, n, d, L, inc, use_pi, pw, vec,
+                           (float*)out);
 }
 
 // ===========================================================================
@@ -155,32 +219,111 @@ void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out
 }
 
 // ===========================================================================
-// Standalone compositing: one wave per ray.
+// Standalone compositing ("Spatial Intelligence - Part 1: NeRF", Section 1
+// Theory, 3. Volume rendering; Section 2 Code, 5. Volume rendering): 16
+// lanes per ray (one DPP row), 4 rays per wave.  A 64-sample chunk is four
+// rounds of 16 consecutive samples, one per lane, so every access of a row
+// is contiguous; each round's exclusive product scan of the survival
+// factors over the row, times the product of all earlier rounds, gives the
+// samples' transmittance.
 // ===========================================================================
+constexpr int kCompLanes = 16;  // one DPP row
+
+// Lane i of a 16-lane row reads lane i - N of the row; the first N lanes get
+// fill.
+template <int N>
+__device__ __forceinline__ float row_shr(float v, float fill) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                                 __builtin_bit_cast(int, v), 0x110 | N, 0xF, 0xF,
+                                                                 false));
+}
+
+// e^x from the hardware base-2 exponential, and the logistic function with
+// the hardware reciprocal (relative errors near 1e-6 for the arguments met
+// here).
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float sigmoid_hw(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-x)); }
+
 __global__ void __launch_bounds__(256) k_composite(const float* __restrict__ raw, const float* __restrict__ z,
                                                    const float* __restrict__ rd, int64_t n_rays, int n, int white,
                                                    float* __restrict__ rgb, float* __restrict__ depth,
                                                    float* __restrict__ acc, float* __restrict__ wout) {
-    const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-    if (r >= n_rays) return;
+    constexpr int G = kCompLanes;
+    const int g = lane_id() & (G - 1);
+    const int64_t r0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / G;
+    const bool ray_ok = r0 < n_rays;  // past the end: repeat the last ray, store nothing
+    const int64_t r = ray_ok ? r0 : n_rays - 1;
     const float dx = rd[3 * r], dy = rd[3 * r + 1], dz = rd[3 * r + 2];
     const float dn = sqrtf(dx * dx + dy * dy + dz * dz);
-    const CompositeOut o = composite_ray(z + r * n, reinterpret_cast<const f32x4*>(raw) + r * n, n, dn,
-                                         wout ? wout + r * n : nullptr, 0.0f);
-    if (lane_id() == 0) {
-        const float bg = white ? 1.0f - o.acc : 0.0f;
-        rgb[3 * r] = o.r + bg;
-        rgb[3 * r + 1] = o.g + bg;
-        rgb[3 * r + 2] = o.b + bg;
-        depth[r] = o.depth;
-        acc[r] = o.acc;
+    const float* zr = z + r * n;
+    const f32x4* rr = reinterpret_cast<const f32x4*>(raw) + r * n;
+    float* wr = wout ? wout + r * n : nullptr;
+    float carry = 1.0f, sr = 0.f, sg = 0.f, sbl = 0.f, sd = 0.f, sa = 0.f;
+    for (int c0 = 0; c0 < n; c0 += 4 * G) {
+        // lane g takes samples c0 + 16i + g: every load and store of the row is contiguous
+        float zi[4], al[4], sv[4], incl[4], tot[4];
+        f32x4 rw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = c0 + G * i + g;
+            al[i] = 0.0f;
+            zi[i] = 0.0f;
+            rw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s < n) {
+                zi[i] = zr[s];
+                const float delta = (s + 1 < n) ? (zr[s + 1] - zi[i]) * dn : 1e10f * dn;
+                rw[i] = rr[s];
+                al[i] = 1.0f - exp_hw(-fmaxf(rw[i][3], 0.0f) * delta);
+            }
+            sv[i] = s < n ? (1.0f - al[i] + 1e-10f) : 1.0f;
+            float p = sv[i];
+            p *= row_shr<1>(p, 1.0f);
+            p *= row_shr<2>(p, 1.0f);
+            p *= row_shr<4>(p, 1.0f);
+            p *= row_shr<8>(p, 1.0f);
+            incl[i] = p;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] = __shfl(incl[i], G - 1, G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = c0 + G * i + g;
+            const float T = row_shr<1>(incl[i], 1.0f) * carry;
+            if (s < n) {
+                const float w = T * al[i];
+                if (wr && ray_ok) wr[s] = w;
+                sa += w;
+                sd += w * zi[i];
+                sr += w * sigmoid_hw(rw[i][0]);
+                sg += w * sigmoid_hw(rw[i][1]);
+                sbl += w * sigmoid_hw(rw[i][2]);
+            }
+            carry *= tot[i];
+        }
+    }
+    // row sums, complete in the row's last lane
+    sr += row_shr<1>(sr, 0.f), sg += row_shr<1>(sg, 0.f), sbl += row_shr<1>(sbl, 0.f), sd += row_shr<1>(sd, 0.f),
+        sa += row_shr<1>(sa, 0.f);
+    sr += row_shr<2>(sr, 0.f), sg += row_shr<2>(sg, 0.f), sbl += row_shr<2>(sbl, 0.f), sd += row_shr<2>(sd, 0.f),
+        sa += row_shr<2>(sa, 0.f);
+    sr += row_shr<4>(sr, 0.f), sg += row_shr<4>(sg, 0.f), sbl += row_shr<4>(sbl, 0.f), sd += row_shr<4>(sd, 0.f),
+        sa += row_shr<4>(sa, 0.f);
+    sr += row_shr<8>(sr, 0.f), sg += row_shr<8>(sg, 0.f), sbl += row_shr<8>(sbl, 0.f), sd += row_shr<8>(sd, 0.f),
+        sa += row_shr<8>(sa, 0.f);
+    if (g == G - 1 && ray_ok) {
+        const float bg = white ? 1.0f - sa : 0.0f;
+        rgb[3 * r] = sr + bg;
+        rgb[3 * r + 1] = sg + bg;
+        rgb[3 * r + 2] = sbl + bg;
+        depth[r] = sd;
+        acc[r] = sa;
     }
 }
 
 void launch_composite(const float* raw, const float* z, const float* rd, int64_t n_rays, int n, int white, float* rgb,
                       float* depth, float* acc, float* w, hipStream_t s) {
-    const int64_t waves_per_block = 4;
-    hipLaunchKernelGGL(k_composite, dim3((unsigned)((n_rays + waves_per_block - 1) / waves_per_block)), dim3(256), 0,
+    const int64_t rays_per_block = 256 / kCompLanes;
+    hipLaunchKernelGGL(k_composite, dim3((unsigned)((n_rays + rays_per_block - 1) / rays_per_block)), dim3(256), 0,
                        s, raw, z, rd, n_rays, n, white, rgb, depth, acc, w);
 }
 
