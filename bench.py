@@ -1,7 +1,7 @@
 """Throughput of the NeRF forward-render hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid]
+                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid|mlp]
                     [--dtype bf16|f32] [--no-cpu-baseline]
 
 A step is one ``nerf_render`` over the whole workload with rays, weights
@@ -13,7 +13,8 @@ The standalone workloads time one call of a single step against the HBM
 roofline: ``encode`` the frequency encoding (L = 10, with the input) of the
 coarse workload's 81.92M sample points, ``composite`` the compositing of its
 1.28M rays x 64 samples, ``hashgrid`` the 16-level hash-grid encoding of
-2^22 points.
+2^22 points (all against the HBM roofline), ``mlp`` the 8x256 network in
+bfloat16 on 2^23 encoded samples read from HBM (against the MFMA roofline).
 
 Prints one JSON line: rays/s (``value``), samples/s, the dominant kernel's
 achieved throughput against its roofline (timed live with HIP events on
@@ -43,7 +44,7 @@ MACS_CELL_2x32 = 5088
 # HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE passes scaled by a 1 GiB copy (x2.0 and x1.0), keyed by
 # (workload, dtype).  An entry is removed whenever that kernel changes.
-MEASURED_TRAFFIC = {("hierarchical", "bf16"): 513.1e6}
+MEASURED_TRAFFIC = {("hierarchical", "bf16"): 512.6e6, ("encode", "f32"): 21.627e9, ("composite", "f32"): 2.012e9}
 
 WORKLOADS = {
     # name: (poses, hemisphere, H, W, focal, n_coarse, n_fine, net kind, chunk)
@@ -56,6 +57,7 @@ WORKLOADS = {
     "encode": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0),
     "composite": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0),
     "hashgrid": dict(points=1 << 22, kind=0),
+    "mlp": dict(poses=1, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0, rays=1 << 17),
 }
 HBM_PEAK_GBS = 8000.0
 
@@ -317,7 +319,7 @@ def standalone(args, wl):
 
     dev = torch.device("cuda")
     name = args.workload
-    if name in ("encode", "composite"):
+    if name in ("encode", "composite", "mlp"):
         P = si.poses(wl["poses"], seed=0, hemisphere=wl["hemi"])
         H, W, f = wl["H"], wl["W"], wl["focal"]
         R, N = wl["poses"] * H * W, wl["nc"]
@@ -330,6 +332,45 @@ def standalone(args, wl):
         far = torch.full((R,), 6.0, device=dev)
         z = torch.empty((R, N), device=dev)
         v.nerf_sample_stratified(near, far, N, 0, 0, True, z)
+    if name == "mlp":
+        Rm = wl["rays"]
+        x = (ro[:Rm, None, :] + z[:Rm, :, None] * rd[:Rm, None, :]).reshape(-1, 3).contiguous()
+        dirs = (rd[:Rm] / rd[:Rm].norm(dim=1, keepdim=True)).contiguous()
+        n = x.shape[0]
+        enc_x = torch.empty((n, 63), device=dev)
+        enc_v = torch.empty((Rm, 27), device=dev)
+        v.nerf_encode_freq(x, 10, True, True, 0, enc_x)
+        v.nerf_encode_freq(dirs, 4, True, True, 0, enc_v)
+        params = si.nerf_params(si.NERF_8x256, seed=0, net_id=0)
+        packed = v.weights.pack_to_device(1, 1, params)
+        raw = torch.empty((n, 4), device=dev)
+
+        def step():
+            v.nerf_mlp(1, 1, packed, enc_x, enc_v, N, raw)
+
+        ms_step, ms_kernel = _timed(args, step, torch)
+        flops = 2.0 * MACS_8x256 * n
+        achieved = flops / (ms_kernel * 1e-3) / 1e12
+        out_rec = {
+            "metric": "samples/s, 8x256 network on encoded inputs (MFMA util %)",
+            "value": n / (ms_step * 1e-3), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic: coarse-workload sample points and directions, He-uniform random weights",
+            "config": {"workload": name, "samples": n, "rays": Rm, "samples_per_ray": N, "net": "8x256",
+                       "inputs": "float32 encodings in HBM (63 + 27 per ray)"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                         "frac": achieved / PEAK["bf16"], "traffic": None, "kernel": "k_mlp",
+                         "kernel_ms": ms_kernel, "flop_per_launch": flops},
+        }
+        if not args.no_cpu_baseline:
+            from oracle import mlp as omlp
+            ex_h, ev_h = enc_x.cpu().numpy(), enc_v.cpu().numpy()
+            base = _cpu_rate(lambda sel: omlp.nerf_forward(params, ex_h[sel], ev_h[sel // N]), n, args.cpu_seconds,
+                             "samples/s", "samples")
+            out_rec["cpu_baseline"] = base
+        print(json.dumps(out_rec), flush=True)
+        return
     if name == "encode":
         x = (ro[:, None, :] + z[:, :, None] * rd[:, None, :]).reshape(-1, 3).contiguous()
         n = x.shape[0]
