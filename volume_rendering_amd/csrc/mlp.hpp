@@ -83,6 +83,8 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 constexpr int kChunkBytes = NERF_CHUNK_KB * 1024;
 static_assert(kTileRegionAlign % kChunkBytes == 0, "chunks tile the padded weight region");
 constexpr int kChunkDma = kChunkBytes / 1024 / 4;  // 1 KB copies per wave per chunk
+// Buffer resource word 3 for raw byte-addressed loads (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
 
 static __shared__ __attribute__((aligned(1024))) char g_ring0[kChunkBytes];
 static __shared__ __attribute__((aligned(1024))) char g_ring1[kChunkBytes];
@@ -106,9 +108,6 @@ __device__ __forceinline__ char* ring_slot() {
     else return g_ring7;
 }
 
-#ifndef NERF_SCHED_MASK
-#define NERF_SCHED_MASK 0  // nothing crosses a step boundary
-#endif
 #ifndef NERF_LOOK
 #define NERF_LOOK 3
 #endif
@@ -120,27 +119,33 @@ struct LdsStream {
     static constexpr size_t BYTES = net_tiles_bytes(KIND, T::prec);
     static constexpr int NT = (int)(BYTES / TB);               // tiles
     static constexpr int NCH = (int)((BYTES + kChunkBytes - 1) / kChunkBytes);
-    const char* src;  // this wave's first byte of chunk 0
-    int dst;          // this wave's byte offset within a slot
+    __amdgpu_buffer_rsrc_t rsrc;  // the padded tile region; reads past it return zero
+    int voff;                     // this lane's byte offset within a chunk
+    int dst;                      // this wave's byte offset within a slot
     int lane;
-    Op buf[LOOK];     // tiles t..t+LOOK-1, read ahead of use
+    Op buf[LOOK];                 // tiles t..t+LOOK-1, read ahead of use
 
     // Each wave copies kChunkDma consecutive kilobytes of every chunk.
     __device__ __forceinline__ LdsStream(const char* packed, int lane_, int wave)
-        : src(packed + wave * (kChunkDma * 1024) + lane_ * 16), dst(wave * (kChunkDma * 1024)), lane(lane_) {}
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(packed), (short)0,
+                                                 (int)net_tiles_padded(KIND, T::prec), kBufferWord3)),
+          voff(wave * (kChunkDma * 1024) + lane_ * 16), dst(wave * (kChunkDma * 1024)), lane(lane_) {}
 
-    // One copy of kilobyte I of this wave's share of chunk K.  All pieces of a
-    // chunk share one global address register and one LDS base (M0); the
-    // instruction's immediate offset, applied to both addresses, selects the
-    // piece.  (A new M0 per piece makes each copy wait for the previous one
-    // to leave the wave.)
+    // One copy of kilobyte I of this wave's share of chunk K, as a buffer load
+    // into LDS: the chunk offset is the scalar offset, the lane's offset a
+    // VGPR fixed for the whole stream, the piece the immediate offset (which
+    // moves the LDS address too), and all pieces of a chunk share one LDS
+    // base (M0).  (A new M0 per piece makes each copy wait for the previous
+    // one to leave the wave.  The buffer form, unlike the global one, also
+    // lets the compiler keep counting LDS reads in order, so tile reads stay
+    // in flight across the copies.)
     template <int K, int I>
     __device__ __forceinline__ void piece() {
         static_assert(I * 1024 < 4096, "immediate offset range");
         if constexpr (K < NCH) {
-            const char* p = src + (size_t)K * kChunkBytes;  // within the padded region
             char* slot = ring_slot<K % NBUF>() + dst;
-            __builtin_amdgcn_global_load_lds((const NERF_AS_GLOBAL void*)p, (NERF_AS_LDS void*)slot, 16, I * 1024, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (NERF_AS_LDS void*)slot, 16, voff, K * kChunkBytes, I * 1024,
+                                                     0);
         }
     }
     template <int K>
@@ -302,33 +307,8 @@ __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
 // accumulator p.
 template <class T>
 struct Epi;
-#ifndef NERF_EPI16
-#define NERF_EPI16 0
-#endif
 template <>
 struct Epi<TBF16> {
-#if NERF_EPI16
-    // piece p writes 32-bit register c of operand (sb, q) of the next layer:
-    // two accumulators rounded to bf16 and packed, then ReLU as a packed
-    // 16-bit integer max (negative bf16 values are negative int16)
-    static constexpr int pieces = 16;
-    template <int P, bool RELU, class Out>
-    __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
-        constexpr int sb = P / 8, q = (P / 4) % 2, c = P % 4;
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef short i16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 f = {acc[sb][8 * q + 2 * c], acc[sb][8 * q + 2 * c + 1]};
-        const bf16x2 v = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32
-        i16x2 w = __builtin_bit_cast(i16x2, v);
-        if constexpr (RELU) w = __builtin_elementwise_max(w, i16x2{0, 0});
-        int bits = __builtin_bit_cast(int, w);
-        asm volatile("" : "+a"(bits));
-        i32x4 t = __builtin_bit_cast(i32x4, out[2 * ob + q][sb]);
-        t[c] = bits;
-        out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
-    }
-#else
     static constexpr int pieces = 4;
     template <int P, bool RELU, class Out>
     __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
@@ -347,8 +327,35 @@ struct Epi<TBF16> {
         asm volatile("" : "+a"(t));
         out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
     }
-#endif
+    // The same epilogue in 8 units for the slots between matrix instructions:
+    // unit 2p rounds, packs and rectifies piece p into VGPRs (8 VALU), unit
+    // 2p+1 moves it to the AGPR operand of the next layer (4 writes).
+    static constexpr int units = 8;
+    struct Tmp {
+        i32x4 t;
+    };
+    template <int U, bool RELU, class Out>
+    __device__ static __forceinline__ void unit(const f32x16 (&acc)[2], Out& out, int ob, Tmp& tmp) {
+        constexpr int P = U / 2, sb = P / 2, q = P % 2;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef short i16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        if constexpr (U % 2 == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f32x2 f = {acc[sb][8 * q + 2 * c], acc[sb][8 * q + 2 * c + 1]};
+                i16x2 w = __builtin_bit_cast(i16x2, __builtin_convertvector(f, bf16x2));
+                if constexpr (RELU) w = __builtin_elementwise_max(w, i16x2{0, 0});
+                tmp.t[c] = __builtin_bit_cast(int, w);
+            }
+        } else {
+            i32x4 t = tmp.t;
+            asm volatile("" : "+a"(t));
+            out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
+        }
+    }
 };
+
 template <>
 struct Epi<TF32> {
     static constexpr int pieces = 16;
@@ -356,32 +363,57 @@ struct Epi<TF32> {
     __device__ static __forceinline__ void piece(const f32x16 (&acc)[1], Out& out, int ob) {
         out[16 * ob + P][0] = act<RELU>(acc[0][P]);
     }
+    static constexpr int units = 16;
+    struct Tmp {};
+    template <int U, bool RELU, class Out>
+    __device__ static __forceinline__ void unit(const f32x16 (&acc)[1], Out& out, int ob, Tmp&) {
+        piece<U, RELU>(acc, out, ob);
+    }
 };
 
 // acc = W(ob) [in1, in2] + bias; the bias enters as the C operand of the
-// first step.  After step s, piece s of the previous block's epilogue runs
-// (PREV_OB >= 0), so its vector work overlaps the matrix instructions.
+// first step.  The previous block's epilogue (PREV_OB >= 0) runs in units
+// placed between matrix instructions, where the wave would otherwise wait
+// for the matrix pipe: with two sample blocks, one unit between the two
+// MFMAs of a step (a second one after them when the block has fewer steps
+// than units); with one, a unit after the MFMA.  Scheduling barriers keep
+// each step's tile read, matrix instructions and epilogue units in place, so
+// the read-ahead distance and the interleave survive scheduling.
 template <class T, int TILE0, int S1, int S2, bool RELU, int PREV_OB, class In1, class In2, class WS, class Out>
 __device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bias, const In1& in1, const In2& in2,
                                           WS& ws, const f32x16 (&prev)[T::SB], Out& out) {
     constexpr int S = S1 + S2;
+    constexpr int U = PREV_OB >= 0 ? Epi<T>::units : 0;
+    constexpr bool TWO = T::SB == 2;
+    // slot 2*st: between the MFMAs of step st (two sample blocks only); slot
+    // 2*st+1: after them.  Unit u goes to slot su(u); units past the last
+    // slot run after the block.
+    constexpr bool DENSE = !TWO || S < U;  // use both slots of a step
+    auto su = [](int u) constexpr { return TWO ? (DENSE ? u : 2 * u) : 2 * u + 1; };
+    typename Epi<T>::Tmp tmp{};
+    auto run_slot = [&](auto slot) {
+        static_for<0, U>([&](auto uc) {
+            constexpr int u = uc.value;
+            if constexpr (su(u) == decltype(slot)::value)
+                Epi<T>::template unit<u, RELU>(prev, out, PREV_OB, tmp);
+        });
+    };
     static_for<0, S>([&](auto sc) {
         constexpr int st = sc.value;
         const typename T::Op a = ws.template get<TILE0 + st>();
-#pragma unroll
-        for (int sb = 0; sb < T::SB; ++sb) {
+        static_for<0, T::SB>([&](auto sbc) {
+            constexpr int sb = sbc.value;
             const typename T::Op b = st < S1 ? in1[st < S1 ? st : 0][sb] : in2[st >= S1 ? st - S1 : 0][sb];
             acc[sb] = T::mma(a, b, st == 0 ? bias : acc[sb]);
-        }
-        if constexpr (PREV_OB >= 0 && st < Epi<T>::pieces) Epi<T>::template piece<st, RELU>(prev, out, PREV_OB);
-#if NERF_SCHED_MASK >= 0
-        // each step keeps its own tile read, matrix instructions and epilogue
-        // piece, so the read-ahead distance survives scheduling
-        __builtin_amdgcn_sched_barrier(NERF_SCHED_MASK);
-#endif
+            __builtin_amdgcn_sched_barrier(0);
+            run_slot(IntC<2 * st + (TWO ? sb : 1)>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
     });
-    if constexpr (PREV_OB >= 0)
-        static_for<S, Epi<T>::pieces>([&](auto pc) { Epi<T>::template piece<pc.value, RELU>(prev, out, PREV_OB); });
+    static_for<0, U>([&](auto uc) {
+        constexpr int u = uc.value;
+        if constexpr (su(u) >= 2 * S) Epi<T>::template unit<u, RELU>(prev, out, PREV_OB, tmp);
+    });
 }
 
 // A hidden layer: out = act(W [in1, in2] + b), kept as next-layer operands.
@@ -391,9 +423,16 @@ __device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out&
     constexpr bool RELU = I::L.relu != 0;
     const int h = lane >> 5;
     f32x16 prev[T::SB];
+    // each block's bias is read one block ahead, so the first MFMA of a block
+    // (bias as its C operand) never waits for it
+    f32x16 bnext = load_bias16(bias, I::bias, 0, h);
     static_for<0, I::OB>([&](auto obc) {
         constexpr int ob = obc.value;
-        const f32x16 b = load_bias16(bias, I::bias, ob, h);
+        const f32x16 b = bnext;
+        if constexpr (ob + 1 < I::OB) {
+            bnext = load_bias16(bias, I::bias, ob + 1, h);
+            compiler_fence();  // issue the reads here, not next to their use
+        }
         f32x16 acc[T::SB];
         mma_block<T, I::tile0 + ob * (I::S1 + I::S2), I::S1, I::S2, RELU, ob - 1>(acc, b, in1, in2, ws, prev, out);
 #pragma unroll
