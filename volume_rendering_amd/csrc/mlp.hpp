@@ -309,25 +309,8 @@ template <class T>
 struct Epi;
 template <>
 struct Epi<TBF16> {
-    static constexpr int pieces = 4;
-    template <int P, bool RELU, class Out>
-    __device__ static __forceinline__ void piece(const f32x16 (&acc)[2], Out& out, int ob) {
-        constexpr int sb = P / 2, q = P % 2;
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef short i16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        i32x4 t;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const f32x2 f = {acc[sb][8 * q + 2 * c], acc[sb][8 * q + 2 * c + 1]};
-            i16x2 w = __builtin_bit_cast(i16x2, __builtin_convertvector(f, bf16x2));
-            if constexpr (RELU) w = __builtin_elementwise_max(w, i16x2{0, 0});
-            t[c] = __builtin_bit_cast(int, w);
-        }
-        asm volatile("" : "+a"(t));
-        out[2 * ob + q][sb] = __builtin_bit_cast(bf16x8, t);
-    }
-    // The same epilogue in 8 units for the slots between matrix instructions:
+    // The epilogue in 8 units for the slots between matrix instructions: piece
+    // p = (sb, q) turns 8 accumulators into one operand of the next layer;
     // unit 2p rounds, packs and rectifies piece p into VGPRs (8 VALU), unit
     // 2p+1 moves it to the AGPR operand of the next layer (4 writes).
     static constexpr int units = 8;
@@ -371,31 +354,82 @@ struct Epi<TF32> {
     }
 };
 
+// Epilogue sources for mma_block: nothing, or a finished block whose
+// accumulators still have to become operands of the next layer (block OBP of
+// a layer with activation RELU, written into *out).
+struct NoEpi {
+    static constexpr bool active = false;
+    template <int U, class Tmp>
+    __device__ __forceinline__ void unit(Tmp&) {}
+    __device__ __forceinline__ void finish() {}
+};
+
+template <class T, bool RELU, int OBP, class Out>
+struct BlockEpi {
+    static constexpr bool active = true;
+    static constexpr int ob = OBP;
+    f32x16 acc[T::SB];
+    Out* out;
+    template <int U>
+    __device__ __forceinline__ void unit(typename Epi<T>::Tmp& tmp) {
+        Epi<T>::template unit<U, RELU>(acc, *out, OBP, tmp);
+    }
+    __device__ __forceinline__ void finish() {
+        typename Epi<T>::Tmp tmp{};
+        static_for<0, Epi<T>::units>([&](auto u) { unit<u.value>(tmp); });
+    }
+};
+
+// Slot of epilogue unit u in a block of S steps: with two sample blocks,
+// slot 2*st lies between the two MFMAs of step st and slot 2*st+1 after
+// them; units use the between-slots when there are enough steps, else every
+// slot; with one sample block, units follow the MFMAs.  Slots >= 2*S run
+// after the block.
+template <class T, int S>
+constexpr int epi_slot(int u) {
+    constexpr bool TWO = T::SB == 2;
+    constexpr bool DENSE = !TWO || S < Epi<T>::units;
+    return TWO ? (DENSE ? u : 2 * u) : 2 * u + 1;
+}
+
+// True when block OBP's epilogue, run in the first block (S steps) of the
+// layer that reads it as its first input segment, writes every operand
+// before the MFMA that reads it (program order decides which value an
+// operand read sees).  bf16: unit 2p+1 writes operand (step 2*OBP + p%2,
+// sample block p/2), read just before slot 2*step + sb.  f32: unit u writes
+// step 16*OBP + u, read before slot 2*step + 1.
+template <class T, int S, int OBP>
+constexpr bool epi_defer_ok() {
+    for (int u = 0; u < Epi<T>::units; ++u) {
+        const int slot = epi_slot<T, S>(u);
+        if (slot >= 2 * S) return false;
+        if constexpr (T::SB == 2) {
+            if (u % 2 == 0) continue;
+            const int p = u / 2, k = 2 * OBP + p % 2, sb = p / 2;
+            if (k < S && !(slot < 2 * k + sb)) return false;
+        } else {
+            const int k = 16 * OBP + u;
+            if (k < S && !(slot < 2 * k + 1)) return false;
+        }
+    }
+    return true;
+}
+
 // acc = W(ob) [in1, in2] + bias; the bias enters as the C operand of the
-// first step.  The previous block's epilogue (PREV_OB >= 0) runs in units
-// placed between matrix instructions, where the wave would otherwise wait
-// for the matrix pipe: with two sample blocks, one unit between the two
-// MFMAs of a step (a second one after them when the block has fewer steps
-// than units); with one, a unit after the MFMA.  Scheduling barriers keep
+// first step.  The epilogue units of `epi` run in the slots above, where the
+// wave would otherwise wait for the matrix pipe.  Scheduling barriers keep
 // each step's tile read, matrix instructions and epilogue units in place, so
 // the read-ahead distance and the interleave survive scheduling.
-template <class T, int TILE0, int S1, int S2, bool RELU, int PREV_OB, class In1, class In2, class WS, class Out>
+template <class T, int TILE0, int S1, int S2, class In1, class In2, class WS, class E>
 __device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bias, const In1& in1, const In2& in2,
-                                          WS& ws, const f32x16 (&prev)[T::SB], Out& out) {
+                                          WS& ws, E& epi) {
     constexpr int S = S1 + S2;
-    constexpr int U = PREV_OB >= 0 ? Epi<T>::units : 0;
+    constexpr int U = E::active ? Epi<T>::units : 0;
     constexpr bool TWO = T::SB == 2;
-    // slot 2*st: between the MFMAs of step st (two sample blocks only); slot
-    // 2*st+1: after them.  Unit u goes to slot su(u); units past the last
-    // slot run after the block.
-    constexpr bool DENSE = !TWO || S < U;  // use both slots of a step
-    auto su = [](int u) constexpr { return TWO ? (DENSE ? u : 2 * u) : 2 * u + 1; };
     typename Epi<T>::Tmp tmp{};
     auto run_slot = [&](auto slot) {
         static_for<0, U>([&](auto uc) {
-            constexpr int u = uc.value;
-            if constexpr (su(u) == decltype(slot)::value)
-                Epi<T>::template unit<u, RELU>(prev, out, PREV_OB, tmp);
+            if constexpr (epi_slot<T, S>(uc.value) == decltype(slot)::value) epi.template unit<uc.value>(tmp);
         });
     };
     static_for<0, S>([&](auto sc) {
@@ -411,45 +445,87 @@ __device__ __forceinline__ void mma_block(f32x16 (&acc)[T::SB], const f32x16& bi
         });
     });
     static_for<0, U>([&](auto uc) {
-        constexpr int u = uc.value;
-        if constexpr (su(u) >= 2 * S) Epi<T>::template unit<u, RELU>(prev, out, PREV_OB, tmp);
+        if constexpr (epi_slot<T, S>(uc.value) >= 2 * S) epi.template unit<uc.value>(tmp);
     });
 }
 
+// Runs `pin` (the previous layer's last block) inside this layer's first
+// block when that is safe (epi_defer_ok), else before it.
+template <class T, int S, class P>
+__device__ __forceinline__ auto& defer_or_finish(P& pin, NoEpi& none) {
+    if constexpr (P::active) {
+        if constexpr (epi_defer_ok<T, S, P::ob>()) {
+            return pin;
+        } else {
+            pin.finish();
+            return none;
+        }
+    } else {
+        return none;
+    }
+}
+
 // A hidden layer: out = act(W [in1, in2] + b), kept as next-layer operands.
-template <class T, int KIND, int LAYER, class In1, class In2, class Out, class WS, class BP>
-__device__ __forceinline__ void dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws, BP bias, int lane) {
+// b0 holds this layer's first bias (read ahead by the caller) and, on
+// return, the first bias of layer NEXT (NEXT < 0: none); pin is the previous
+// layer's last block, run inside this layer's first block; the return value
+// is this layer's last block, for the next layer to run.
+template <class T, int KIND, int LAYER, int NEXT, class In1, class In2, class Out, class WS, class BP, class P>
+__device__ __forceinline__ auto dense_layer(const In1& in1, const In2& in2, Out& out, WS& ws, BP bias, int lane,
+                                            f32x16& b0, P& pin) {
     using I = LayerInfo<T, KIND, LAYER>;
     constexpr bool RELU = I::L.relu != 0;
+    constexpr int S = I::S1 + I::S2;
     const int h = lane >> 5;
     f32x16 prev[T::SB];
+    NoEpi none;
+    auto& first = defer_or_finish<T, S>(pin, none);
     // each block's bias is read one block ahead, so the first MFMA of a block
     // (bias as its C operand) never waits for it
-    f32x16 bnext = load_bias16(bias, I::bias, 0, h);
+    f32x16 bnext = b0;
     static_for<0, I::OB>([&](auto obc) {
         constexpr int ob = obc.value;
         const f32x16 b = bnext;
         if constexpr (ob + 1 < I::OB) {
             bnext = load_bias16(bias, I::bias, ob + 1, h);
             compiler_fence();  // issue the reads here, not next to their use
+        } else if constexpr (NEXT >= 0) {
+            b0 = load_bias16(bias, LayerInfo<T, KIND, NEXT>::bias, 0, h);
+            compiler_fence();
         }
         f32x16 acc[T::SB];
-        mma_block<T, I::tile0 + ob * (I::S1 + I::S2), I::S1, I::S2, RELU, ob - 1>(acc, b, in1, in2, ws, prev, out);
+        if constexpr (ob == 0) {
+            mma_block<T, I::tile0, I::S1, I::S2>(acc, b, in1, in2, ws, first);
+        } else {
+            BlockEpi<T, RELU, ob - 1, Out> pe{{}, &out};
+#pragma unroll
+            for (int sb = 0; sb < T::SB; ++sb) pe.acc[sb] = prev[sb];
+            mma_block<T, I::tile0 + ob * S, I::S1, I::S2>(acc, b, in1, in2, ws, pe);
+        }
 #pragma unroll
         for (int sb = 0; sb < T::SB; ++sb) prev[sb] = acc[sb];
     });
-    static_for<0, Epi<T>::pieces>([&](auto pc) { Epi<T>::template piece<pc.value, RELU>(prev, out, I::OB - 1); });
+    BlockEpi<T, RELU, I::OB - 1, Out> last{{}, &out};
+#pragma unroll
+    for (int sb = 0; sb < T::SB; ++sb) last.acc[sb] = prev[sb];
+    return last;
 }
 
-// A head (one output block, no activation): raw accumulators.
-template <class T, int KIND, int LAYER, class In1, class In2, class WS, class BP>
+// A head (one output block, no activation): raw accumulators.  b0 and pin as
+// for dense_layer.
+template <class T, int KIND, int LAYER, int NEXT, class In1, class In2, class WS, class BP, class P>
 __device__ __forceinline__ void dense_head(const In1& in1, const In2& in2, f32x16 (&acc)[T::SB], WS& ws, BP bias,
-                                           int lane) {
+                                           int lane, f32x16& b0, P& pin) {
     using I = LayerInfo<T, KIND, LAYER>;
     static_assert(I::OB == 1, "head layers have one output block");
-    const f32x16 b = load_bias16(bias, I::bias, 0, lane >> 5);
-    f32x16 none[T::SB];
-    mma_block<T, I::tile0, I::S1, I::S2, false, -1>(acc, b, in1, in2, ws, none, acc);
+    NoEpi none;
+    auto& first = defer_or_finish<T, I::S1 + I::S2>(pin, none);
+    const f32x16 b = b0;
+    if constexpr (NEXT >= 0) {
+        b0 = load_bias16(bias, LayerInfo<T, KIND, NEXT>::bias, 0, lane >> 5);
+        compiler_fence();
+    }
+    mma_block<T, I::tile0, I::S1, I::S2>(acc, b, in1, in2, ws, first);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,12 +539,17 @@ struct NerfFamily {
     static constexpr int LDIR = net_layers(KIND)[D + 2].s1.L;
 };
 
-template <class T, int KIND, int I, int D, class H, class E, class WS, class BP>
-__device__ __forceinline__ void hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, BP bias, int lane) {
-    if constexpr (I < D) {
-        dense_layer<T, KIND, I>(cur, enc, nxt, ws, bias, lane);  // enc is read only by a skip layer (S2 > 0)
-        hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, bias, lane);
-    }
+// Hidden layers I..D-1, alternating between cur and nxt; returns the last
+// one's final block (pending epilogue).
+template <class T, int KIND, int I, int D, class H, class E, class WS, class BP, class P>
+__device__ __forceinline__ auto hidden_chain(H& cur, H& nxt, const E& enc, WS& ws, BP bias, int lane, f32x16& b0,
+                                             P& pin) {
+    // enc is read only by a skip layer (S2 > 0)
+    auto pe = dense_layer<T, KIND, I, I + 1>(cur, enc, nxt, ws, bias, lane, b0, pin);
+    if constexpr (I + 1 < D)
+        return hidden_chain<T, KIND, I + 1, D>(nxt, cur, enc, ws, bias, lane, b0, pe);
+    else
+        return pe;
 }
 
 // enc: position-encoding operands; denc: direction-encoding operands.
@@ -479,20 +560,24 @@ __device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& w
                                              f32x16 (&rgb)[T::SB], int lane) {
     using Fam = NerfFamily<KIND>;
     constexpr int D = Fam::D;
+    static_assert(D >= 2, "at least two hidden layers");
     constexpr int HS = out_steps<T, KIND, 0>();
     constexpr int GS = out_steps<T, KIND, D + 2>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
     ws.begin();
-    dense_layer<T, KIND, 0>(enc, enc, hA, ws, bias, lane);
-    hidden_chain<T, KIND, 1, D>(hA, hB, enc, ws, bias, lane);
+    f32x16 b0 = load_bias16(bias, LayerInfo<T, KIND, 0>::bias, 0, lane >> 5);
+    NoEpi none;
+    auto p0 = dense_layer<T, KIND, 0, 1>(enc, enc, hA, ws, bias, lane, b0, none);
+    auto pl = hidden_chain<T, KIND, 1, D>(hA, hB, enc, ws, bias, lane, b0, p0);
     // the last hidden layer (index D-1) wrote hB when D-1 is odd, else hA
     auto& hl = ((D - 1) % 2 == 1) ? hB : hA;
     auto& hf = ((D - 1) % 2 == 1) ? hA : hB;
-    dense_head<T, KIND, D>(hl, hl, sig, ws, bias, lane);
-    dense_layer<T, KIND, D + 1>(hl, hl, hf, ws, bias, lane);
+    dense_head<T, KIND, D, D + 1>(hl, hl, sig, ws, bias, lane, b0, pl);
+    NoEpi none2;
+    auto pf = dense_layer<T, KIND, D + 1, D + 2>(hl, hl, hf, ws, bias, lane, b0, none2);
     typename T::Op g[GS][T::SB];
-    dense_layer<T, KIND, D + 2>(hf, denc, g, ws, bias, lane);
-    dense_head<T, KIND, D + 3>(g, g, rgb, ws, bias, lane);
+    auto pg = dense_layer<T, KIND, D + 2, D + 3>(hf, denc, g, ws, bias, lane, b0, pf);
+    dense_head<T, KIND, D + 3, -1>(g, g, rgb, ws, bias, lane, b0, pg);
 }
 
 // Hash-grid field: density 0, 1; density head 2; feature 3; colour 4 (with
@@ -504,13 +589,15 @@ __device__ __forceinline__ void hash_field_forward(const FE& feats, const DE& sh
     constexpr int HS = out_steps<T, K, 0>();
     typename T::Op hA[HS][T::SB], hB[HS][T::SB];
     ws.begin();
-    dense_layer<T, K, 0>(feats, feats, hA, ws, bias, lane);
-    dense_layer<T, K, 1>(hA, hA, hB, ws, bias, lane);
-    dense_head<T, K, 2>(hB, hB, sig, ws, bias, lane);
-    dense_layer<T, K, 3>(hB, hB, hA, ws, bias, lane);
-    dense_layer<T, K, 4>(hA, sh, hB, ws, bias, lane);
-    dense_layer<T, K, 5>(hB, hB, hA, ws, bias, lane);
-    dense_head<T, K, 6>(hA, hA, rgb, ws, bias, lane);
+    f32x16 b0 = load_bias16(bias, LayerInfo<T, K, 0>::bias, 0, lane >> 5);
+    NoEpi none, none2;
+    auto p0 = dense_layer<T, K, 0, 1>(feats, feats, hA, ws, bias, lane, b0, none);
+    auto p1 = dense_layer<T, K, 1, 2>(hA, hA, hB, ws, bias, lane, b0, p0);
+    dense_head<T, K, 2, 3>(hB, hB, sig, ws, bias, lane, b0, p1);
+    auto p3 = dense_layer<T, K, 3, 4>(hB, hB, hA, ws, bias, lane, b0, none2);
+    auto p4 = dense_layer<T, K, 4, 5>(hA, sh, hB, ws, bias, lane, b0, p3);
+    auto p5 = dense_layer<T, K, 5, 6>(hB, hB, hA, ws, bias, lane, b0, p4);
+    dense_head<T, K, 6, -1>(hA, hA, rgb, ws, bias, lane, b0, p5);
 }
 
 // ---------------------------------------------------------------------------
