@@ -6,9 +6,10 @@
 // One render pass runs as a pipeline of small kernels, with no host
 // synchronisation:
 //   count     one wave per ray: stratified samples, box and occupancy test,
-//             number of live samples per ray
+//             live-sample mask and number of live samples per ray
 //   scan      exclusive prefix sum of the counts (ray start offsets)
-//   compact   one wave per ray: live samples written in (ray, sample) order
+//   compact   one wave per ray, one lane per live sample (from the mask):
+//             live samples written in (ray, sample) order
 //             with their cell id; per-cell histogram, whose running counts
 //             give each sample its slot in the cell's bucket
 //   cells     one workgroup: per-cell start offsets, tile counts, tile list
@@ -18,8 +19,8 @@
 //   mlp       persistent waves over the tile list: each tile is up to 64
 //             (bf16) or 32 (f32) samples of one cell, evaluated by that
 //             cell's network read straight from global memory
-//   composite one wave per ray: samples in order, density 0 for dead ones,
-//             stop at the first sample with transmittance below term_T
+//   composite one wave per ray over its live samples in order (dead ones
+//             change nothing), stop at the first with transmittance below term_T
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -130,10 +131,15 @@ __device__ __forceinline__ RayIn load_ray(const RenderArgs& a, int64_t r) {
     return R;
 }
 
-// Sample i of ray r (global counter ray_offset + r): z and the point.
-__device__ __forceinline__ float sample_point(const RenderArgs& a, const RayIn& R, int64_t r, int i, float (&x)[3]) {
+// Depth of sample i of ray r (global counter ray_offset + r).
+__device__ __forceinline__ float sample_z(const RenderArgs& a, const RayIn& R, int64_t r, int i) {
     const float u = a.jitter ? philox_uniform(a.seed, a.ray_offset + (uint64_t)r, (uint32_t)i, kStreamJitter) : 0.5f;
-    const float z = stratified_z(R.near, R.far, i, a.n_coarse, u);
+    return stratified_z(R.near, R.far, i, a.n_coarse, u);
+}
+
+// Sample i of ray r: z and the point.
+__device__ __forceinline__ float sample_point(const RenderArgs& a, const RayIn& R, int64_t r, int i, float (&x)[3]) {
+    const float z = sample_z(a, R, r, i);
 #pragma unroll
     for (int k = 0; k < 3; ++k) x[k] = __fadd_rn(R.o[k], __fmul_rn(z, R.d[k]));
     return z;
@@ -163,6 +169,30 @@ __device__ __forceinline__ bool classify(const KiloArgs& k, const float (&x)[3],
     return inside && occ;
 }
 
+// The cell id alone (the same arithmetic as classify).
+__device__ __forceinline__ int cell_of(const KiloArgs& k, const float (&x)[3]) {
+    int c[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) c[a] = grid_coord(__fsub_rn(x[a], k.lo), k.cscale, k.cell_res);
+    return (c[0] * k.cell_res + c[1]) * k.cell_res + c[2];
+}
+
+// Live-sample list of one ray from its mask words (bit i = sample i live):
+// the sample indices in order, written to the wave's idx[]; returns their
+// number.
+__device__ __forceinline__ int live_list(const unsigned long long* mask, int words, int* idx) {
+    const int lane = lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int c = 0;
+    for (int w = 0; w < words; ++w) {
+        const unsigned long long mw = mask[w];
+        if ((mw >> lane) & 1ull) idx[c + __popcll(mw & below)] = kWave * w + lane;
+        c += __popcll(mw);
+    }
+    wave_lds_sync();
+    return c;
+}
+
 __global__ void __launch_bounds__(256) k_kilo_count(RenderArgs a, KiloArgs k) {
     const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     if (r >= a.n_rays) return;
@@ -178,26 +208,36 @@ __global__ void __launch_bounds__(256) k_kilo_count(RenderArgs a, KiloArgs k) {
             int cell;
             live = classify(k, x, cell);
         }
-        cnt += __popcll(__ballot(live));
+        const unsigned long long m = __ballot(live);
+        if (lane == 0) k.live_mask[r * k.mask_words + base / kWave] = m;
+        cnt += __popcll(m);
     }
     if (lane == 0) k.live_count[r] = cnt;
 }
 
+constexpr int kKiloMaxSamples = 256;
+
 __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) {
-    const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    __shared__ int lists[4][kKiloMaxSamples];
+    const int wave = threadIdx.x / kWave;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= a.n_rays) return;
     const RayIn R = load_ray(a, r);
     const int lane = lane_id();
     const unsigned long long below = (1ull << lane) - 1ull;
-    uint32_t pos = k.ray_start[r];
-    for (int base = 0; base < a.n_coarse; base += kWave) {
-        const int i = base + lane;
-        bool live = false;
-        int cell = 0;
-        if (i < a.n_coarse) {
+    int* idx = lists[wave];
+    const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
+    const uint32_t pos = k.ray_start[r];
+    // one lane per live sample, in (ray, sample) order
+    for (int base = 0; base < nlive; base += kWave) {
+        const int q = base + lane;
+        const bool live = q < nlive;
+        int cell = 0, i = 0;
+        if (live) {
+            i = idx[q];
             float x[3];
             sample_point(a, R, r, i, x);
-            live = classify(k, x, cell);
+            cell = cell_of(k, x);
         }
         const unsigned long long m = __ballot(live);
         // per-cell histogram, one atomic per distinct cell of the wave (the
@@ -215,12 +255,11 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
             rem &= ~same;
         }
         if (live) {
-            const uint32_t e = pos + (uint32_t)__popcll(m & below);
+            const uint32_t e = pos + (uint32_t)q;
             k.ent_ray[e] = (uint32_t)r;
             k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
             k.ent_slot[e] = slot;
         }
-        pos += (uint32_t)__popcll(m);
     }
 }
 
@@ -321,49 +360,72 @@ __global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int 
     }
 }
 
-struct KiloLds {
-    float z[256];
-    f32x4 raw[256];
-};
-
+// One wave per ray, over its live samples only: a dead sample has density 0,
+// so its weight is 0 and its survival factor 1 - 0 + 1e-10 rounds to 1 in
+// float32 - skipping it changes no product.  A live sample's interval needs
+// the depth of the next sample, live or not (recomputed from its counter).
 __global__ void __launch_bounds__(256) k_kilo_composite(RenderArgs a, KiloArgs k) {
-    __shared__ KiloLds lds_all[4];
+    __shared__ int lists[4][kKiloMaxSamples];
     const int wave = threadIdx.x / kWave;
-    KiloLds& S = lds_all[wave];
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= a.n_rays) return;
     const RayIn R = load_ray(a, r);
     const int lane = lane_id();
-    const unsigned long long below = (1ull << lane) - 1ull;
     const int N = a.n_coarse;
-    uint32_t pos = k.ray_start[r];
-    for (int base = 0; base < N; base += kWave) {
-        const int i = base + lane;
-        bool live = false;
-        if (i < N) {
-            float x[3];
-            S.z[i] = sample_point(a, R, r, i, x);
-            int cell;
-            live = classify(k, x, cell);
-        }
-        const unsigned long long m = __ballot(live);
-        if (i < N)
-            S.raw[i] = live ? reinterpret_cast<const f32x4*>(k.raw_live)[pos + __popcll(m & below)]
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-        pos += (uint32_t)__popcll(m);
-    }
-    wave_lds_sync();
     const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
-    const CompositeOut c = composite_ray(S.z, S.raw, N, dn, nullptr, k.term_T);
     if (a.dbg_z)
-        for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = S.z[i];
+        for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = sample_z(a, R, r, i);
+    int* idx = lists[wave];
+    const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
+    const f32x4* raw = reinterpret_cast<const f32x4*>(k.raw_live) + k.ray_start[r];
+    float carry = 1.0f, sr = 0.f, sg = 0.f, sbl = 0.f, sd = 0.f, sa = 0.f;
+    bool stopped = false;
+    for (int base = 0; base < nlive; base += kWave) {
+        const int q = base + lane;
+        const bool valid = q < nlive;
+        float alpha = 0.f, zi = 0.f;
+        f32x4 rw = {0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+            const int i = idx[q];
+            zi = sample_z(a, R, r, i);
+            const float delta = (i + 1 < N) ? (sample_z(a, R, r, i + 1) - zi) * dn : 1e10f * dn;
+            rw = raw[q];
+            alpha = 1.0f - expf(-fmaxf(rw[3], 0.0f) * delta);
+        }
+        const float surv = valid ? (1.0f - alpha + 1e-10f) : 1.0f;
+        const float incl = wave_scan_mul(surv);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 1.0f;
+        const float T = carry * excl;
+        bool stop_here = false;
+        if (k.term_T > 0.0f) {
+            // the first live sample (in order) with T < term_T and all later ones are dropped
+            const unsigned long long m = __ballot(valid && T < k.term_T);
+            const int first = m ? __builtin_ctzll(m) : kWave;
+            stop_here = stopped || (lane >= first);
+            if (m) stopped = true;
+        }
+        const float w = (valid && !stop_here) ? T * alpha : 0.0f;
+        sa += w;
+        sd += w * zi;
+        sr += w * sigmoidf_(rw[0]);
+        sg += w * sigmoidf_(rw[1]);
+        sbl += w * sigmoidf_(rw[2]);
+        carry *= __shfl(incl, kWave - 1, kWave);
+        if (stopped) break;
+    }
+    sr = wave_sum(sr);
+    sg = wave_sum(sg);
+    sbl = wave_sum(sbl);
+    sd = wave_sum(sd);
+    sa = wave_sum(sa);
     if (lane == 0) {
-        const float bg = a.white ? 1.0f - c.acc : 0.0f;
-        a.rgb[3 * r] = c.r + bg;
-        a.rgb[3 * r + 1] = c.g + bg;
-        a.rgb[3 * r + 2] = c.b + bg;
-        a.depth[r] = c.depth;
-        a.acc[r] = c.acc;
+        const float bg = a.white ? 1.0f - sa : 0.0f;
+        a.rgb[3 * r] = sr + bg;
+        a.rgb[3 * r + 1] = sg + bg;
+        a.rgb[3 * r + 2] = sbl + bg;
+        a.depth[r] = sd;
+        a.acc[r] = sa;
     }
 }
 
@@ -385,6 +447,8 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
         off += (bytes + 255) / 256 * 256;
         return at;
     };
+    const int words = (n_samples + kWave - 1) / kWave;
+    const size_t o_mask = take(8 * (size_t)n_rays * words);
     const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
                  o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
                  o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
@@ -392,6 +456,8 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
                  o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
                  o_raw = take(16 * max_live);
     if (base && k) {
+        k->live_mask = (unsigned long long*)(base + o_mask);
+        k->mask_words = words;
         k->live_count = (uint32_t*)(base + o_live);
         k->ray_start = (uint32_t*)(base + o_start);
         k->block_sums = (uint32_t*)(base + o_bs);

@@ -49,6 +49,8 @@ struct KiloArgs {
     size_t cell_stride; // bytes per packed network
     int64_t* dbg_n_live;
     // workspace
+    unsigned long long* live_mask;  // [n_rays, mask_words]: bit i of word w = sample 64w+i live
+    int mask_words;
     uint32_t* live_count;  // [n_rays]
     uint32_t* ray_start;   // [n_rays + 1]
     uint32_t* block_sums;  // [scan blocks + 1]
