@@ -217,49 +217,91 @@ __global__ void __launch_bounds__(256) k_kilo_count(RenderArgs a, KiloArgs k) {
 
 constexpr int kKiloMaxSamples = 256;
 
+// Compact: a workgroup takes kCompactRays consecutive rays (each wave
+// kCompactRays/4 of them in turn), one lane per live sample.  Cell counts
+// are first aggregated in an LDS hash table (one LDS atomic per distinct
+// cell of a wave); each used entry then takes one device-scope atomic for
+// its base in the cell's bucket, and a last pass over the workgroup's
+// (contiguous) entries turns (entry, local rank) into bucket slots.  A
+// sample that finds the table full takes its global slot directly (flagged
+// in bit 31).
+constexpr int kCompactRays = 32;
+constexpr int kCellTable = 1024;  // power of two
+constexpr uint32_t kSlotFinal = 0x80000000u;
+
 __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) {
     __shared__ int lists[4][kKiloMaxSamples];
+    __shared__ int keys[kCellTable];
+    __shared__ uint32_t counts[kCellTable];
+    for (int i = threadIdx.x; i < kCellTable; i += blockDim.x) {
+        keys[i] = -1;
+        counts[i] = 0u;
+    }
+    __syncthreads();
     const int wave = threadIdx.x / kWave;
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r >= a.n_rays) return;
-    const RayIn R = load_ray(a, r);
     const int lane = lane_id();
     const unsigned long long below = (1ull << lane) - 1ull;
     int* idx = lists[wave];
-    const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
-    const uint32_t pos = k.ray_start[r];
-    // one lane per live sample, in (ray, sample) order
-    for (int base = 0; base < nlive; base += kWave) {
-        const int q = base + lane;
-        const bool live = q < nlive;
-        int cell = 0, i = 0;
-        if (live) {
-            i = idx[q];
-            float x[3];
-            sample_point(a, R, r, i, x);
-            cell = cell_of(k, x);
+    const int64_t r0 = (int64_t)blockIdx.x * kCompactRays;
+    for (int j = 0; j < kCompactRays / 4; ++j) {
+        const int64_t r = r0 + wave * (kCompactRays / 4) + j;
+        if (r >= a.n_rays) break;
+        const RayIn R = load_ray(a, r);
+        const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
+        const uint32_t pos = k.ray_start[r];
+        for (int base = 0; base < nlive; base += kWave) {
+            const int q = base + lane;
+            const bool live = q < nlive;
+            int cell = 0, i = 0;
+            if (live) {
+                i = idx[q];
+                float x[3];
+                sample_point(a, R, r, i, x);
+                cell = cell_of(k, x);
+            }
+            uint32_t slot = 0;
+            for (unsigned long long rem = __ballot(live); rem;) {
+                const int leader = __ffsll((long long)rem) - 1;
+                const int c = __shfl(cell, leader, kWave);
+                const unsigned long long same = __ballot(live && cell == c);
+                uint32_t b = 0;
+                if (lane == leader) {
+                    const uint32_t n = (uint32_t)__popcll(same);
+                    int h = (int)(((uint32_t)c * 2654435761u) >> 22) & (kCellTable - 1);
+                    int probes = 0;
+                    for (; probes < kCellTable; ++probes, h = (h + 1) & (kCellTable - 1)) {
+                        const int prev = atomicCAS(&keys[h], -1, c);
+                        if (prev == -1 || prev == c) break;
+                    }
+                    if (probes < kCellTable)
+                        b = ((uint32_t)h << 20) | atomicAdd(&counts[h], n);
+                    else
+                        b = kSlotFinal | atomicAdd(&k.cell_count[c], n);
+                }
+                b = __shfl(b, leader, kWave);
+                if ((same >> lane) & 1ull) slot = b + (uint32_t)__popcll(same & below);
+                rem &= ~same;
+            }
+            if (live) {
+                const uint32_t e = pos + (uint32_t)q;
+                k.ent_ray[e] = (uint32_t)r;
+                k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
+                k.ent_slot[e] = slot;
+            }
         }
-        const unsigned long long m = __ballot(live);
-        // per-cell histogram, one atomic per distinct cell of the wave (the
-        // samples of a ray segment fall into a few neighbouring cells); the
-        // count it returns places each live sample in its cell's bucket
-        uint32_t slot = 0;
-        for (unsigned long long rem = m; rem;) {
-            const int leader = __ffsll((long long)rem) - 1;
-            const int c = __shfl(cell, leader, kWave);
-            const unsigned long long same = __ballot(live && cell == c);
-            uint32_t b = 0;
-            if (lane == leader) b = atomicAdd(&k.cell_count[c], (uint32_t)__popcll(same));
-            b = __shfl(b, leader, kWave);
-            if ((same >> lane) & 1ull) slot = b + (uint32_t)__popcll(same & below);
-            rem &= ~same;
-        }
-        if (live) {
-            const uint32_t e = pos + (uint32_t)q;
-            k.ent_ray[e] = (uint32_t)r;
-            k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
-            k.ent_slot[e] = slot;
-        }
+    }
+    __syncthreads();
+    // one device-scope atomic per used table entry: its base in the bucket
+    for (int h = threadIdx.x; h < kCellTable; h += blockDim.x) {
+        const int c = keys[h];
+        if (c >= 0) counts[h] = atomicAdd(&k.cell_count[c], counts[h]);
+    }
+    __syncthreads();
+    const int64_t r1 = r0 + kCompactRays < a.n_rays ? r0 + kCompactRays : a.n_rays;
+    const uint32_t e0 = k.ray_start[r0], e1 = k.ray_start[r1];
+    for (uint32_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+        const uint32_t t = k.ent_slot[e];
+        k.ent_slot[e] = (t & kSlotFinal) ? (t & ~kSlotFinal) : counts[t >> 20] + (t & 0xFFFFFu);
     }
 }
 
@@ -487,7 +529,7 @@ void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int ad
     hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, k.block_sums, nb);
     hipLaunchKernelGGL(k_scan_add, dim3((unsigned)((n + 1 + 255) / 256)), dim3(256), 0, s, k.ray_start, n,
                        k.block_sums, nb);
-    hipLaunchKernelGGL(k_kilo_compact, rays4, dim3(256), 0, s, a, k);
+    hipLaunchKernelGGL(k_kilo_compact, dim3((unsigned)((n + kCompactRays - 1) / kCompactRays)), dim3(256), 0, s, a, k);
     const int tile = bf16 ? 64 : 32;
     hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells, tile);
     hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n);
