@@ -12,10 +12,10 @@
 //             live samples written in (ray, sample) order
 //             with their cell id; per-cell histogram, whose running counts
 //             give each sample its slot in the cell's bucket
-//   cells     one workgroup: per-cell start offsets, tile counts, tile list
-//   scatter   live samples into per-cell buckets (bucket order within a
-//             cell is arbitrary: each sample is its own matrix column and
-//             writes only its own entry)
+//   cells     one workgroup: per-cell start offsets and tile offsets
+//   scatter   the tile list, and live samples into per-cell buckets (bucket
+//             order within a cell is arbitrary: each sample is its own matrix
+//             column and writes only its own entry)
 //   mlp       persistent waves over the tile list: each tile is up to 64
 //             (bf16) or 32 (f32) samples of one cell, evaluated by that
 //             cell's network read straight from global memory
@@ -305,8 +305,7 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
     }
 }
 
-// One workgroup of 1024 threads: cell start offsets, tiles per cell and the
-// tile list.
+// One workgroup of 1024 threads: cell start offsets and tile offsets.
 __global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells, int tile) {
     __shared__ uint32_t lds[17];
     uint32_t carry_s = 0, carry_t = 0;
@@ -328,22 +327,31 @@ __global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells, in
         k.cell_start[n_cells] = carry_s;
         k.tile_start[n_cells] = carry_t;
     }
-    __syncthreads();
-    for (int c = threadIdx.x; c < n_cells; c += blockDim.x) {
-        const uint32_t t0 = k.tile_start[c], t1 = k.tile_start[c + 1];
-        for (uint32_t t = t0; t < t1; ++t) {
-            k.tile_cell[t] = (uint32_t)c;
-            k.tile_off[t] = (t - t0) * (uint32_t)tile;
-        }
-    }
 }
 
-__global__ void __launch_bounds__(256) k_kilo_scatter(KiloArgs k, int64_t n_rays) {
+// Grid-wide: live samples into their cells' buckets, and the tile list
+// (tile t belongs to the cell c with tile_start[c] <= t < tile_start[c+1],
+// found by binary search).
+__global__ void __launch_bounds__(256) k_kilo_scatter(KiloArgs k, int64_t n_rays, int n_cells, int tile) {
     const uint32_t total = k.ray_start[n_rays];
     const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const uint32_t t_id = blockIdx.x * blockDim.x + threadIdx.x;
+    for (uint32_t e = t_id; e < total; e += stride) {
         const uint32_t c = k.ent_meta[e] & 0xFFFFu;
         k.bucket[k.cell_start[c] + k.ent_slot[e]] = e;
+    }
+    const uint32_t n_tiles = k.tile_start[n_cells];
+    for (uint32_t t = t_id; t < n_tiles; t += stride) {
+        int lo = 0, hi = n_cells;  // largest c with tile_start[c] <= t
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (k.tile_start[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        k.tile_cell[t] = (uint32_t)lo;
+        k.tile_off[t] = (t - k.tile_start[lo]) * (uint32_t)tile;
     }
 }
 
@@ -532,7 +540,7 @@ void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int ad
     hipLaunchKernelGGL(k_kilo_compact, dim3((unsigned)((n + kCompactRays - 1) / kCompactRays)), dim3(256), 0, s, a, k);
     const int tile = bf16 ? 64 : 32;
     hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells, tile);
-    hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n);
+    hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n, n_cells, tile);
     const dim3 persist(256 * 16);  // a multiple of kXcds (the tile partition)
     if (bf16)
         hipLaunchKernelGGL(k_kilo_mlp<TBF16>, persist, dim3(256), 0, s, a, k, n_cells);
