@@ -118,8 +118,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rays shard independently; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path.  Rays are independent, so the "
+              "render would shard by contiguous pixel blocks per GPU (same counters, replicated networks) "
+              "and gather rgb/depth/acc at the end.", file=sys.stderr)
         sys.exit(2)
 
     import torch
