@@ -98,7 +98,6 @@ def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s):
             oren.render_kilo(rays_o[sel], rays_d[sel], near[sel], far[sel], occ, lambda c: cells[c], wl["nc"], seed=0,
                              term_T=1e-2)
         elif kind == 4:
-            from oracle import encoding as oenc
             grid, tabs, field = coarse
             oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0)
         else:
@@ -168,7 +167,6 @@ def main():
         nets = []
         mode = B.NERF_MODE_KILO
     elif kind == 4:
-        from oracle import encoding as _unused  # noqa: F401  (oracle only used for the cpu baseline)
         g = v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048)
         tabs = si.hash_tables(list(g.size)[:16], seed=0, scale=1.0)
         tdev = torch.from_numpy(np.concatenate(tabs, 0)).to(dev)

@@ -217,6 +217,26 @@ def occupancy_bits(res: int = 128, p: float = 0.1, seed: int = 0) -> np.ndarray:
     return np.packbits(occ.astype(np.uint8), bitorder="little").view(np.uint32).copy()
 
 
+def occupancy_words(res: int, seed: int = 0) -> np.ndarray:
+    """Occupancy of a large res^3 grid as uniformly random uint32 words
+    (each voxel occupied with probability 1/2), for grids too large to draw
+    one float per voxel.  Same bit order as :func:`occupancy_bits`."""
+    n_words = (res ** 3 + 31) // 32
+    return rng(seed, TAG_OCC, res).integers(0, 2 ** 32, size=n_words, dtype=np.uint32)
+
+
+class PackedOccupancy:
+    """Read-only view of a packed occupancy bitset that indexes like a dense
+    boolean array (``occ[vox]`` for an integer array ``vox``)."""
+
+    def __init__(self, words: np.ndarray):
+        self.words = words
+
+    def __getitem__(self, vox):
+        vox = np.asarray(vox, dtype=np.int64)
+        return ((self.words[vox >> 5] >> (vox & 31).astype(np.uint32)) & 1).astype(bool)
+
+
 def occupancy_dense(bits: np.ndarray, res: int = 128) -> np.ndarray:
     return np.unpackbits(bits.view(np.uint8), bitorder="little")[: res ** 3].astype(bool)
 

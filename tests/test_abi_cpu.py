@@ -71,7 +71,7 @@ def _unpack_layer(buf, kind, prec, li, layers, n_in):
             return (2 if prec else 16) * ob
         if kindc == "E":
             pairs = 3 * L + 2
-            return -(-pairs // 8) if prec else 2 * (-(-pairs // 2))
+            return -(-pairs // 8) if prec else 16 * (-(-pairs // 16))
         if kindc == "F":
             return -(-width // 16) if prec else -(-width // 2)
         return 0

@@ -133,3 +133,37 @@ def test_kilo_bf16_cells(scene):
     assert n_live == ref["n_live"]
     say(f"  rgb err {max_abs(rgb, ref['rgb']):.2e}")
     assert max_abs(rgb, ref["rgb"]) <= 2e-2
+
+
+def test_kilo_occupancy_resolution_near_cap(scene):
+    """A 1700^3 occupancy grid: voxel ids pass 2^32 (from 1626^3 on), so the
+    bit address must be formed in 64 bits; live samples and colours are
+    checked against the oracle's classification of the same packed bits."""
+    import volume_rendering_amd._binding as B
+    say("kilo render, occupancy resolution 1700")
+    v, torch = scene["v"], scene["torch"]
+    res = 1700
+    words = si.occupancy_words(res, seed=3)
+    occ = si.PackedOccupancy(words)
+    sel = si.subset(800 * 800, 300, seed=8)
+    o, d = scene["o"][sel], scene["d"][sel]
+    cells_dev, params = _pack_cells(v, scene["cells"], 0)
+    R = len(sel)
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    occ_dev = dev(words.view(np.int32))
+    nlive = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cfg = B.nerf_render_cfg(mode=2, n_coarse=192, use_pi=1, jitter=1, seed=0, term_T=1e-2, box_lo=-1.5,
+                            box_hi=1.5, occ_res=res, cell_res=16, occ=occ_dev.data_ptr(), dbg_n_live=nlive.data_ptr())
+    w = B.nerf_weights(net=B.nerf_mlp_desc(3, 0), cells=cells_dev.data_ptr(), n_cells=4096)
+    rgb, depth, acc = empty((R, 3)), empty(R), empty(R)
+    v.nerf_render(dev(o), dev(d), dev(near), dev(far), w, cfg, rgb, depth, acc)
+    ref = oren.render_kilo(o, d, near, far, occ, lambda c: params[c], n_samples=192, seed=0, term_T=1e-2,
+                           occ_res=res)
+    _, _, vox = oren.kilo_classify(oren.sampling.points(o, d, ref["z"]), occ, res)
+    assert vox.max() >= 2 ** 32  # the test reaches voxel ids past 32 bits
+    n_live = int(host(nlive)[0])
+    say(f"  live samples {n_live} (oracle {ref['n_live']})")
+    assert n_live == ref["n_live"]
+    assert max_abs(host(rgb), ref["rgb"]) <= RGB_TOL
+    assert max_abs(host(acc), ref["acc"]) <= ACC_TOL
+    assert max_abs(host(depth), ref["depth"]) <= DEPTH_TOL

@@ -163,9 +163,11 @@ __device__ __forceinline__ bool classify(const KiloArgs& k, const float (&x)[3],
         v[a] = grid_coord(t, k.vscale, k.occ_res);
         c[a] = grid_coord(t, k.cscale, k.cell_res);
     }
-    const uint32_t vox = ((uint32_t)v[0] * k.occ_res + v[1]) * k.occ_res + v[2];
+    // 64-bit: (occ_res)^3 passes 2^32 from occ_res = 1626 on
+    const uint64_t res = (uint64_t)k.occ_res;
+    const uint64_t vox = ((uint64_t)v[0] * res + (uint64_t)v[1]) * res + (uint64_t)v[2];
     cell = (c[0] * k.cell_res + c[1]) * k.cell_res + c[2];
-    const bool occ = (k.occ[vox >> 5] >> (vox & 31)) & 1u;
+    const bool occ = (k.occ[vox >> 5] >> (uint32_t)(vox & 31u)) & 1u;
     return inside && occ;
 }
 

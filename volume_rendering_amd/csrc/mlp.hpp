@@ -234,6 +234,9 @@ struct BiasRegion {
     static constexpr int layer_float() {
         return (int)((net_bias_offset(KIND, PREC, LAYER) - begin) / sizeof(float));
     }
+    static constexpr int layer_float_rt(int layer) {
+        return (int)((net_bias_offset(KIND, PREC, layer) - begin) / sizeof(float));
+    }
 };
 
 // Copies the bias region of a packed network to LDS; every thread of the
@@ -299,6 +302,10 @@ __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
     i32x4 bits = __builtin_bit_cast(i32x4, v);
     asm volatile("" : "+a"(bits));
     return __builtin_bit_cast(bf16x8, bits);
+}
+__device__ __forceinline__ float to_agpr(float v) {
+    asm volatile("" : "+a"(v));
+    return v;
 }
 
 // Epilogue of one output block, cut into pieces so it can run between the
@@ -578,6 +585,172 @@ __device__ __forceinline__ void nerf_forward(const E& enc, const DE& denc, WS& w
     typename T::Op g[GS][T::SB];
     auto pg = dense_layer<T, KIND, D + 2, D + 3>(hf, denc, g, ws, bias, lane, b0, pf);
     dense_head<T, KIND, D + 3, -1>(g, g, rgb, ws, bias, lane, b0, pg);
+}
+
+// ---------------------------------------------------------------------------
+// Float32 NeRF family with a runtime loop over layers.  Fully unrolling a
+// float32 chain (32x32x2 steps: ~9,300 matrix instructions for 8x256) makes
+// compile time explode, so one copy of a layer body serves every layer: up
+// to 8 output blocks, each up to 8 hidden k-groups and 2 encoding k-groups
+// of 16 steps, skipped at run time where a layer has fewer.  The hidden
+// state is read from `hin` and written to `hout`; a layer that is read again
+// by the next one copies hout to hin (density head: no copy, the feature
+// layer reads the same state).  Weight tiles stream per wave straight from
+// global memory (L2) one 16-tile group ahead of use.
+// ---------------------------------------------------------------------------
+struct LoopLayer {
+    int n_ob;        // output blocks
+    int n_hkb;       // hidden input k-groups (16 steps each)
+    int seg2;        // 0 none, 1 position encoding, 2 direction encoding
+    int relu;
+    int commit;      // copy hout to hin afterwards
+    int save;        // 0 none, 1 density head, 2 rgb head
+    int bias_float;  // first bias of the layer in the bias region
+};
+
+template <int KIND>
+struct LoopPlan {
+    using Fam = NerfFamily<KIND>;
+    static constexpr int NL = net_n_layers(KIND);
+    static constexpr LoopLayer layer(int i) {
+        const Layer L = net_layers(KIND)[i];
+        LoopLayer d{};
+        d.n_ob = out_blocks(L.n_out);
+        d.n_hkb = L.s0.kind == SEG_HIDDEN ? seg_steps(L.s0, PREC_F32) / 16 : 0;
+        const Seg e = L.s0.kind == SEG_ENC ? L.s0 : L.s1;
+        d.seg2 = e.kind != SEG_ENC ? 0 : (e.L == Fam::LPOS && i != Fam::D + 2 ? 1 : 2);
+        d.relu = L.relu;
+        d.commit = i != Fam::D;
+        d.save = i == Fam::D ? 1 : (i == Fam::D + 3 ? 2 : 0);
+        d.bias_float = BiasRegion<KIND, PREC_F32>::layer_float_rt(i);
+        return d;
+    }
+    struct Table {
+        LoopLayer l[NL];
+    };
+    static constexpr Table table() {
+        Table t{};
+        for (int i = 0; i < NL; ++i) t.l[i] = layer(i);
+        return t;
+    }
+    static constexpr bool fits() {
+        for (int i = 0; i < NL; ++i) {
+            const Layer L = net_layers(KIND)[i];
+            if (out_blocks(L.n_out) > 8 || (L.s0.kind == SEG_HIDDEN && seg_steps(L.s0, PREC_F32) > 128)) return false;
+            if (L.s0.kind == SEG_HIDDEN && seg_steps(L.s0, PREC_F32) % 16) return false;
+        }
+        return true;
+    }
+};
+
+// Weight tiles of the looped float32 network: group g = tiles 16g..16g+15
+// (one float per lane each).  cur holds the group in use, nxt the one
+// after it; next() moves on and fetches the group after that.
+struct F32Groups {
+    const NERF_AS_GLOBAL char* base;  // this lane's bytes of tile 0
+    int next_tile;                    // first tile of the group in nxt
+    int last_group_tile;              // last valid group start (reads never pass the tiles)
+    float cur[16], nxt[16];
+    __device__ __forceinline__ F32Groups(const char* packed, int lane, int n_tiles)
+        : base((const NERF_AS_GLOBAL char*)packed + lane * 4), next_tile(16), last_group_tile(n_tiles - 16) {}
+    __device__ __forceinline__ void load(float (&dst)[16], int t) const {
+        t = t < last_group_tile ? t : last_group_tile;
+        const NERF_AS_GLOBAL char* p = base + (size_t)t * 256;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[j] = *reinterpret_cast<const NERF_AS_GLOBAL float*>(p + 256 * j);
+    }
+    __device__ __forceinline__ void begin() {
+        load(cur, 0);
+        load(nxt, 16);
+    }
+    __device__ __forceinline__ void next() {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+        next_tile += 16;
+        load(nxt, next_tile);
+    }
+};
+
+template <int KIND>
+__constant__ typename LoopPlan<KIND>::Table kLoopTable = LoopPlan<KIND>::table();
+
+// Networks whose float32 form runs through the layer loop.
+template <class T, int KIND>
+constexpr bool kLoopedF32 = T::prec == PREC_F32 && KIND == NET_8x256;
+
+template <int KIND, int ES, int DS>
+__device__ __forceinline__ void nerf_forward_f32_loop(const float (&enc)[ES][1], const float (&denc)[DS][1],
+                                                      const char* packed, const NERF_AS_LDS float* bias,
+                                                      f32x16 (&sig)[1], f32x16 (&rgb)[1], int lane) {
+    using P = LoopPlan<KIND>;
+    static_assert(P::fits(), "layer shapes of the looped float32 network");
+    static_assert(ES % 16 == 0 && ES <= 32 && DS % 16 == 0 && DS <= 32, "encoding segments in whole groups");
+    constexpr int NT = (int)(net_tiles_bytes(KIND, PREC_F32) / 256);
+    const int h = lane >> 5;
+    // matrix-instruction B operands (the layer input and both encodings) sit
+    // in accumulation registers; the outputs of a layer are written by
+    // vector instructions into architectural registers
+    float hin[128], hout[128], pe[ES], de[DS];
+#pragma unroll
+    for (int i = 0; i < 128; ++i) hin[i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < ES; ++i) pe[i] = to_agpr(enc[i][0]);
+#pragma unroll
+    for (int i = 0; i < DS; ++i) de[i] = to_agpr(denc[i][0]);
+    F32Groups ws(packed, lane, NT);
+    ws.begin();
+    sig[0] = f32x16{};
+    rgb[0] = f32x16{};
+#pragma unroll 1
+    for (int li = 0; li < P::NL; ++li) {
+        const LoopLayer L = kLoopTable<KIND>.l[li];
+        static_for<0, 8>([&](auto obc) {
+            constexpr int ob = obc.value;
+            if (ob < L.n_ob) {
+                f32x16 acc = load_bias16(bias, L.bias_float, ob, h);
+                static_for<0, 8>([&](auto kbc) {
+                    constexpr int kb = kbc.value;
+                    if (kb < L.n_hkb) {
+                        static_for<0, 16>([&](auto j) {
+                            acc = TF32::mma(ws.cur[j.value], hin[16 * kb + j.value], acc);
+                        });
+                        ws.next();
+                    }
+                });
+                if (L.seg2 == 1) {
+                    static_for<0, ES / 16>([&](auto g) {
+                        static_for<0, 16>([&](auto j) {
+                            acc = TF32::mma(ws.cur[j.value], pe[16 * g.value + j.value], acc);
+                        });
+                        ws.next();
+                    });
+                } else if (L.seg2 == 2) {
+                    static_for<0, DS / 16>([&](auto g) {
+                        static_for<0, 16>([&](auto j) {
+                            acc = TF32::mma(ws.cur[j.value], de[16 * g.value + j.value], acc);
+                        });
+                        ws.next();
+                    });
+                }
+                if (ob == 0) {
+                    // element-wise selects: a conditional store of the whole
+                    // vector would be lowered through private memory
+                    const bool s1 = L.save == 1, s2 = L.save == 2;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        sig[0][r] = s1 ? acc[r] : sig[0][r];
+                        rgb[0][r] = s2 ? acc[r] : rgb[0][r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) hout[16 * ob + r] = L.relu ? fmaxf(acc[r], 0.0f) : acc[r];
+            }
+        });
+        if (L.commit) {
+#pragma unroll
+            for (int i = 0; i < 128; ++i) hin[i] = to_agpr(hout[i]);
+        }
+    }
 }
 
 // Hash-grid field: density 0, 1; density head 2; feature 3; colour 4 (with

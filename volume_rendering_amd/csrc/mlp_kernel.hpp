@@ -48,11 +48,15 @@ __global__ void __launch_bounds__(256) k_mlp(const char* __restrict__ packed, co
     __syncthreads();
     const NERF_AS_LDS float* bias = (const NERF_AS_LDS float*)bias_lds;
     f32x16 sig[T::SB], rgb[T::SB];
-    LdsStream<T, KIND, kMlpRing> ws(packed, lane, wave);
-    if constexpr (KIND == NET_HASH_FIELD)
-        hash_field_forward<T>(enc, denc, ws, bias, sig, rgb, lane);
-    else
-        nerf_forward<T, KIND>(enc, denc, ws, bias, sig, rgb, lane);
+    if constexpr (kLoopedF32<T, KIND>) {
+        nerf_forward_f32_loop<KIND>(enc, denc, packed, bias, sig, rgb, lane);
+    } else {
+        LdsStream<T, KIND, kMlpRing> ws(packed, lane, wave);
+        if constexpr (KIND == NET_HASH_FIELD)
+            hash_field_forward<T>(enc, denc, ws, bias, sig, rgb, lane);
+        else
+            nerf_forward<T, KIND>(enc, denc, ws, bias, sig, rgb, lane);
+    }
     if (lane < 32) {
 #pragma unroll
         for (int sb = 0; sb < T::SB; ++sb) {

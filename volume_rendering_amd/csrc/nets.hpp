@@ -22,6 +22,9 @@
 // Frequency-encoding inputs are supplied in (sin, cos) pairs of one
 // argument so each lane evaluates one sincospi per pair: pair P < 3L is
 // (sin, cos)(pi 2^(P/3) x[P%3]); pair 3L is (x, y); pair 3L+1 is (z, 0).
+// In float32 an encoding segment is zero-padded to a whole number of
+// 16-step groups (the unit in which the looped float32 network streams its
+// weight tiles).
 //
 // Packed buffer: all A tiles (layer order; within a layer output block
 // major, k-step minor; 64 operands per tile), zero padding to a 16 KB boundary,
@@ -64,7 +67,7 @@ NERF_HD constexpr int out_blocks(int n_out) { return ceil_div(n_out, 32); }
 NERF_HD constexpr int seg_steps(Seg s, int prec) {
     return s.kind == SEG_NONE     ? 0
            : s.kind == SEG_HIDDEN ? (prec == PREC_BF16 ? 2 : 16) * out_blocks(s.width)
-           : s.kind == SEG_ENC    ? (prec == PREC_BF16 ? ceil_div(enc_pairs(s.L), 8) : 2 * ceil_div(enc_pairs(s.L), 2))
+           : s.kind == SEG_ENC    ? (prec == PREC_BF16 ? ceil_div(enc_pairs(s.L), 8) : 16 * ceil_div(enc_pairs(s.L), 16))
                                   : (prec == PREC_BF16 ? ceil_div(s.width, 16) : ceil_div(s.width, 2));
 }
 

@@ -106,8 +106,12 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
             enc_operands<Fam::LPOS>(enc, x, a.use_pi != 0, lane);
             f32x16 sig[SB], rgb[SB];
             const char* pk = opaque(packed);
-            LdsStream<T, KIND, kRenderRing> ws(pk, lane, wave);
-            nerf_forward<T, KIND>(enc, denc, ws, (const NERF_AS_LDS float*)bias_lds[pass], sig, rgb, lane);
+            if constexpr (kLoopedF32<T, KIND>) {
+                nerf_forward_f32_loop<KIND>(enc, denc, pk, (const NERF_AS_LDS float*)bias_lds[pass], sig, rgb, lane);
+            } else {
+                LdsStream<T, KIND, kRenderRing> ws(pk, lane, wave);
+                nerf_forward<T, KIND>(enc, denc, ws, (const NERF_AS_LDS float*)bias_lds[pass], sig, rgb, lane);
+            }
             if (lane < 32) {
 #pragma unroll
                 for (int sb = 0; sb < SB; ++sb) {
