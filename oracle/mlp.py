@@ -113,3 +113,35 @@ def nerf_forward_naive(params: dict, pos_enc, dir_enc) -> np.ndarray:
         rgb = lin(g, params["rgb"], False)
         res.append(rgb + sigma)
     return np.array(res, dtype=np.float64)
+
+
+def hash_field_forward_naive(params: dict, feats, dir_enc) -> np.ndarray:
+    """The hash-grid field written as explicit loops over samples, output
+    units and inputs, in plain Python floats: density layers on the grid
+    features, density head and feature layer on the last density state, then
+    the colour layers on [feature, direction encoding] and the rgb head.  For
+    a handful of samples only."""
+
+    def lin(vec, Wb, relu):
+        W, b = Wb
+        out = []
+        for o in range(W.shape[0]):
+            s = float(b[o])
+            for i in range(W.shape[1]):
+                s += float(W[o, i]) * vec[i]
+            out.append(max(s, 0.0) if relu else s)
+        return out
+
+    res = []
+    for p in range(len(feats)):
+        h = [float(v) for v in feats[p]]
+        for Wb in params["density"]:
+            h = lin(h, Wb, True)
+        sigma = lin(h, params["sigma"], False)
+        feat = lin(h, params["feature"], False)
+        g = feat + [float(v) for v in dir_enc[p]]
+        for Wb in params["color"]:
+            g = lin(g, Wb, True)
+        rgb = lin(g, params["rgb"], False)
+        res.append(rgb + sigma)
+    return np.array(res, dtype=np.float64)

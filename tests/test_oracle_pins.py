@@ -381,6 +381,40 @@ def test_nerf_skip_concatenates_encoding_after_hidden_state():
     assert np.abs(expect).max() > 0.1
 
 
+def test_hash_field_forward_matches_naive_loops():
+    p = si.hash_field_params(seed=4)
+    g = np.random.default_rng(8)
+    feats = g.normal(size=(4, 32))
+    de = g.normal(size=(4, 16))
+    assert np.allclose(mlp.hash_field_forward(p, feats, de), mlp.hash_field_forward_naive(p, feats, de), atol=1e-10,
+                       rtol=1e-12)
+
+
+def test_hash_field_zero_weights_give_biases():
+    p = si.hash_field_params(seed=0)
+    zero = lambda Wb: (np.zeros_like(Wb[0]), Wb[1])  # noqa: E731
+    q = dict(p, density=[zero(x) for x in p["density"]], color=[zero(x) for x in p["color"]],
+             **{k: zero(p[k]) for k in ("sigma", "feature", "rgb")})
+    out = mlp.hash_field_forward(q, np.ones((3, 32)), np.ones((3, 16)))
+    assert np.allclose(out[:, :3], p["rgb"][1]) and np.allclose(out[:, 3], p["sigma"][1][0])
+
+
+def test_hash_field_density_ignores_direction_and_colour_reads_features_through_the_feature_layer():
+    p = si.hash_field_params(seed=2)
+    g = np.random.default_rng(9)
+    feats = np.repeat(g.normal(size=(1, 32)), 5, axis=0)
+    de = g.normal(size=(5, 16))
+    out = mlp.hash_field_forward(p, feats, de)
+    assert np.all(out[:, 3] == out[0, 3])            # density: grid features only
+    assert np.ptp(out[:, 0]) > 1e-3                  # colour: depends on the direction
+    # with a zero feature layer the colour no longer depends on the grid features
+    q = dict(p, feature=(np.zeros_like(p["feature"][0]), p["feature"][1]))
+    f2 = g.normal(size=(5, 32))
+    de2 = np.repeat(de[:1], 5, axis=0)
+    o2 = mlp.hash_field_forward(q, f2, de2)
+    assert np.allclose(o2[:, :3], o2[0, :3], atol=1e-14) and np.ptp(o2[:, 3]) > 1e-3
+
+
 def test_round_bf16_nearest_even():
     vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 2 ** -9, 1.0 + 3 * 2 ** -9, -2.5, 1e-3], np.float32)
     r = mlp.round_bf16(vals)
@@ -520,6 +554,67 @@ def test_sample_pdf_spike_mass():
     assert abs(frac - p_spike) < 5 * math.sqrt(p_spike * (1 - p_spike) / n) + 1e-4
 
 
+def test_midpoints_lie_between_consecutive_samples():
+    R, N = 4, 64
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    zc = sampling.stratified(near, far, N, 0, jitter=False)  # z_i = 2 + (i + 1/2) / 16
+    b = sampling.midpoints(zc)
+    assert b.shape == (R, N - 1)
+    k = np.arange(N - 1, dtype=np.float64)
+    assert np.array_equal(b.astype(np.float64), np.broadcast_to(2.0 + (k + 1.0) / 16.0, (R, N - 1)))
+    zj = sampling.stratified(near, far, N, 5)
+    bj = sampling.midpoints(zj)
+    assert np.all((bj > zj[:, :-1]) & (bj < zj[:, 1:]))
+
+
+@pytest.mark.parametrize("k", [1, 2, 31, 61, 62])
+def test_hierarchical_spike_goes_to_the_bin_around_its_coarse_sample(k):
+    """One coarse weight spike at sample k (Section 2 Code, 6. Hierarchical
+    sampling: bins are midpoints of the coarse samples, weights drop the two
+    end samples): a fraction (1 + 1e-5) / (1 + 62e-5) of the fine samples lands
+    in [b_{k-1}, b_k], the bin that contains coarse sample k."""
+    R, Nc, Nf = 256, 64, 128
+    zc = sampling.stratified(np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32), Nc, 4)
+    w = np.zeros((R, Nc), np.float32)
+    w[:, k] = 1.0
+    zf, idx, _ = sampling.hierarchical_fine_samples(zc, w, Nf, seed=7)
+    b = sampling.midpoints(zc)
+    assert np.all((b[:, k - 1] < zc[:, k]) & (zc[:, k] < b[:, k]))
+    inside = (zf >= b[:, k - 1:k]) & (zf <= b[:, k:k + 1])
+    p = (1.0 + 1e-5) / (1.0 + 62 * 1e-5)
+    n = R * Nf
+    assert abs(inside.mean() - p) < 5 * math.sqrt(p * (1 - p) / n) + 1e-4
+    assert np.all(inside == (idx == k))
+
+
+@pytest.mark.parametrize("k", [0, 63])
+def test_hierarchical_end_sample_weights_are_ignored(k):
+    """A spike on an end sample (excluded by the page's weights[1:-1]) leaves a
+    uniform pdf over the 62 bins."""
+    R, Nc, Nf = 512, 64, 128
+    zc = sampling.stratified(np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32), Nc, 0, jitter=False)
+    w = np.zeros((R, Nc), np.float32)
+    w[:, k] = 1.0
+    _, idx, _ = sampling.hierarchical_fine_samples(zc, w, Nf, seed=8)
+    counts = np.bincount(idx.reshape(-1) - 1, minlength=62)
+    chi2 = scipy.stats.chisquare(counts)
+    assert counts.size == 62 and chi2.pvalue > 1e-4
+
+
+def test_hierarchical_uniform_weights_map_u_linearly():
+    """Equal weights on evenly spaced coarse samples z_i = near + (i + 1/2) s:
+    the fine samples are near + s + u * 62 s, the linear map of the uniforms
+    onto [b_0, b_62]."""
+    R, Nc, Nf = 32, 64, 128
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    zc = sampling.stratified(near, far, Nc, 0, jitter=False)
+    zf, _, _ = sampling.hierarchical_fine_samples(zc, np.full((R, Nc), 0.25, np.float32), Nf, seed=13,
+                                                  ray_offset=77)
+    u = philox.uniforms(13, philox.STREAM_PDF, (77 + np.arange(R))[:, None], np.arange(Nf)[None, :])
+    s = 4.0 / 64
+    assert np.allclose(zf, 2.0 + s + u.astype(np.float64) * 62 * s, atol=2e-6, rtol=0)
+
+
 def test_hierarchical_merge_is_sorted_union():
     g = np.random.default_rng(6)
     R = 8
@@ -563,6 +658,68 @@ def test_render_constant_field_closed_form():
     sig = 1 / (1 + np.exp(-np.array([0.2, -0.4, 1.0])))
     assert np.allclose(out["rgb"], sig[None, :] * out["acc"][:, None], atol=1e-12)
     assert np.all(T_last > 0)
+
+
+def _zero_hash_field(rgb_raw, sigma_raw):
+    p = si.hash_field_params(seed=0)
+    zero = lambda Wb: (np.zeros_like(Wb[0]), np.zeros_like(Wb[1]))  # noqa: E731
+    q = dict(p, density=[zero(x) for x in p["density"]], color=[zero(x) for x in p["color"]],
+             feature=zero(p["feature"]))
+    q["sigma"] = (np.zeros_like(p["sigma"][0]), np.full(1, sigma_raw, np.float32))
+    q["rgb"] = (np.zeros_like(p["rgb"][0]), np.array(rgb_raw, np.float32))
+    return q
+
+
+def test_render_hash_constant_field_closed_form():
+    R = 32
+    c2w = si.poses(1, seed=1)[0]
+    o, d = rays.get_rays(4, 8, 40.0, 40.0, 4.0, 2.0, c2w)
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    grid = encoding.hashgrid_3d()
+    tabs = si.hash_tables(grid.sizes, seed=0, scale=1.0)
+    q = _zero_hash_field([0.3, -1.0, 0.6], 0.4)
+    out = render.render_hash(o, d, near, far, grid, tabs, q, n_samples=48, seed=0)
+    dn = np.linalg.norm(d.astype(np.float64), axis=1)
+    z = out["z"].astype(np.float64)
+    # 1 - sum_{j<i} w_j = T_i = exp(-sigma (z_i - z_0) |d|) up to the 1e-10 term
+    T = np.concatenate([np.ones((R, 1)), 1 - np.cumsum(out["w"], 1)[:, :-1]], 1)
+    assert np.allclose(T, np.exp(-0.4 * (z - z[:, :1]) * dn[:, None]), rtol=1e-7, atol=1e-8)
+    assert np.allclose(out["acc"], 1.0, atol=1e-9)
+    sig = 1 / (1 + np.exp(-np.array([0.3, -1.0, 0.6])))
+    assert np.allclose(out["rgb"], sig[None, :] * out["acc"][:, None], atol=1e-12)
+
+
+def test_render_hash_density_from_a_linear_coarsest_level():
+    """Level 0 (direct) holds the linear function a . v / N + c of its vertex
+    v; trilinear interpolation reproduces it, so with the density path reading
+    only that feature, sigma_raw at a sample is relu(a . u + c) with u the
+    sample point mapped from the box [-1.5, 1.5]^3 to the unit cube."""
+    R = 24
+    c2w = si.poses(1, seed=2)[0]
+    o, d = rays.get_rays(4, 6, 30.0, 30.0, 3.0, 2.0, c2w)
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    grid = encoding.hashgrid_3d()
+    tabs = [np.zeros((s, 2), np.float64) for s in grid.sizes]
+    N = grid.res[0]
+    a, c = np.array([0.9, -0.6, 0.75]), -0.2
+    v = np.stack(np.meshgrid(*[np.arange(N + 1)] * 3, indexing="ij"), -1).reshape(-1, 3)
+    tabs[0][encoding.direct_index([v[:, 0], v[:, 1], v[:, 2]], N), 0] = v @ a / N + c
+    q = _zero_hash_field([0.0, 0.0, 0.0], 0.0)
+    W0 = np.zeros_like(q["density"][0][0])
+    W0[0, 0] = 1.0  # level 0, feature 0
+    W1 = np.zeros_like(q["density"][1][0])
+    W1[0, 0] = 1.0
+    q["density"] = [(W0, q["density"][0][1]), (W1, q["density"][1][1])]
+    ws = np.zeros_like(q["sigma"][0])
+    ws[0, 0] = 1.0
+    q["sigma"] = (ws, q["sigma"][1])
+    out = render.render_hash(o, d, near, far, grid, tabs, q, n_samples=40, seed=3)
+    x = sampling.points(o, d, out["z"]).astype(np.float64)
+    u = (x + 1.5) / 3.0
+    expect = np.maximum(u @ a + c, 0.0)
+    inside = np.all((u >= 0) & (u <= 1), axis=-1)
+    assert inside.mean() > 0.3
+    assert np.allclose(out["raw"][..., 3][inside], expect[inside], atol=1e-6)
 
 
 def test_kilo_reduces_to_single_network_with_full_occupancy():
