@@ -17,7 +17,19 @@ from .philox import STREAM_JITTER, STREAM_PDF, uniforms
 f32 = np.float32
 
 
-def stratified(t_near, t_far, n: int, seed: int, jitter: bool = True, ray_offset: int = 0):
+def ray_counters(R: int, ray_offset) -> np.ndarray:
+    """Global ray index of each of R rays, the Philox counter of its random
+    numbers: ray_offset + r for an integer offset, or the given per-ray
+    indices for an integer array of length R (rays sampled from a larger
+    batch keep their place in it).  Returns uint64 [R, 1]."""
+    if np.ndim(ray_offset) == 0:
+        return (np.arange(R, dtype=np.uint64) + np.uint64(int(ray_offset)))[:, None]
+    ids = np.asarray(ray_offset, dtype=np.int64)
+    assert ids.shape == (R,) and (R == 0 or ids.min() >= 0)
+    return ids.astype(np.uint64)[:, None]
+
+
+def stratified(t_near, t_far, n: int, seed: int, jitter: bool = True, ray_offset=0):
     """Stratified samples.  The page calls ``stratified_sample`` without
     defining it; the reading here is n equal strata on [near, far] with one
     uniform draw in each (u = 1/2 without jitter).  As float32 operations:
@@ -29,8 +41,7 @@ def stratified(t_near, t_far, n: int, seed: int, jitter: bool = True, ray_offset
     step = (t_far - t_near) / f32(n)
     i = np.arange(n, dtype=np.float32)[None, :]
     if jitter:
-        ray_ids = (np.arange(R, dtype=np.uint64) + np.uint64(ray_offset))[:, None]
-        u = uniforms(seed, STREAM_JITTER, ray_ids, np.arange(n, dtype=np.uint64)[None, :])
+        u = uniforms(seed, STREAM_JITTER, ray_counters(R, ray_offset), np.arange(n, dtype=np.uint64)[None, :])
     else:
         u = np.full((R, n), f32(0.5), dtype=np.float32)
     s = i + u
@@ -59,7 +70,7 @@ def midpoints(z):
     return f32(0.5) * (z[:, 1:] + z[:, :-1])
 
 
-def sample_pdf(bins, weights, n_fine: int, seed: int, ray_offset: int = 0):
+def sample_pdf(bins, weights, n_fine: int, seed: int, ray_offset=0):
     """Inverse-CDF resampling ("6. Hierarchical sampling", ``sample_pdf``).
 
     ``bins`` float32 [R, B+1] are bin edges, ``weights`` float32 [R, B] the
@@ -84,8 +95,8 @@ def sample_pdf(bins, weights, n_fine: int, seed: int, ray_offset: int = 0):
     R, B = w.shape
     S = np.concatenate([np.zeros((R, 1)), np.cumsum(w.astype(np.float64), axis=1)], axis=1)
     cdf = S / S[:, -1:]
-    ray_ids = (np.arange(R, dtype=np.uint64) + np.uint64(ray_offset))[:, None]
-    u = uniforms(seed, STREAM_PDF, ray_ids, np.arange(n_fine, dtype=np.uint64)[None, :]).astype(np.float64)
+    u = uniforms(seed, STREAM_PDF, ray_counters(R, ray_offset), np.arange(n_fine, dtype=np.uint64)[None, :]
+                 ).astype(np.float64)
     idx = np.empty((R, n_fine), dtype=np.int64)
     for r in range(R):
         idx[r] = np.searchsorted(cdf[r], u[r], side="right")
@@ -102,7 +113,7 @@ def sample_pdf(bins, weights, n_fine: int, seed: int, ray_offset: int = 0):
     return z, idx.astype(np.int32)
 
 
-def hierarchical_fine_samples(z_coarse, w_coarse, n_fine: int, seed: int, ray_offset: int = 0):
+def hierarchical_fine_samples(z_coarse, w_coarse, n_fine: int, seed: int, ray_offset=0):
     """The page's resampling step of ``render_rays``: bins are the midpoints
     of the coarse samples, weighted by the coarse weights without the two end
     samples; the fine network sees the ascending sort of coarse and fine
