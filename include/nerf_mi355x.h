@@ -306,6 +306,30 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
  * HASH modes). */
 size_t nerf_render_workspace_size(const nerf_render_cfg* cfg, int64_t n_rays);
 
+/* ---------------------------------------------------------------------- */
+/* For callers that cannot allocate                                       */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the fixed device scratch of nerf_render_noalloc (per device). */
+#define NERF_NOALLOC_SCRATCH_MB 128
+
+/* nerf_render for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, results and validation as nerf_render, but no call to
+ * hipMalloc/hipMallocAsync/hipFree or any allocating routine.  The
+ * many-network mode (the only one with a workspace) takes its workspace from
+ * a fixed array of NERF_NOALLOC_SCRATCH_MB MiB that the library holds on
+ * each device from load to process end; cfg.workspace must be NULL, and the
+ * rays are rendered in the largest chunks whose workspace fits (cfg.chunk,
+ * if set, must fit, else NERF_ERR_WORKSPACE with the sizes in
+ * nerf_last_error()).  Every call on one device shares that device's array:
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be serialised by the caller.  Results equal nerf_render's bit for bit
+ * (they do not depend on the chunking). */
+nerf_status nerf_render_noalloc(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
+                                int64_t n_rays, const nerf_weights* w, const nerf_render_cfg* cfg, float* rgb,
+                                float* depth, float* acc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ EXPORTED = [
     "nerf_abi_version", "nerf_status_str", "nerf_last_error", "nerf_hashgrid_init", "nerf_mlp_packed_bytes",
     "nerf_pack_mlp", "nerf_gen_rays", "nerf_sample_stratified", "nerf_encode_freq", "nerf_encode_sh16",
     "nerf_encode_hashgrid", "nerf_mlp", "nerf_composite", "nerf_sample_pdf", "nerf_render",
-    "nerf_render_workspace_size",
+    "nerf_render_workspace_size", "nerf_render_noalloc",
 ]
 
 
@@ -89,6 +89,8 @@ def lib():
             "nerf_sample_pdf": (I, [P, P, I64, I, I, U64, U64, P, P, P, P]),
             "nerf_render": (I, [P, P, P, P, I64, C.POINTER(nerf_weights), C.POINTER(nerf_render_cfg), P, P, P, P]),
             "nerf_render_workspace_size": (S, [C.POINTER(nerf_render_cfg), I64]),
+            "nerf_render_noalloc": (I, [P, P, P, P, I64, C.POINTER(nerf_weights), C.POINTER(nerf_render_cfg), P, P,
+                                        P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -206,3 +208,9 @@ def nerf_render(rays_o, rays_d, t_near, t_far, weights: nerf_weights, cfg: nerf_
     _check(lib().nerf_render(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), rays_o.shape[0],
                              C.byref(weights), C.byref(cfg), _ptr(rgb), _ptr(depth), _ptr(acc), _stream()),
            "nerf_render")
+
+
+def nerf_render_noalloc(rays_o, rays_d, t_near, t_far, weights: nerf_weights, cfg: nerf_render_cfg, rgb, depth, acc):
+    _check(lib().nerf_render_noalloc(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), rays_o.shape[0],
+                                     C.byref(weights), C.byref(cfg), _ptr(rgb), _ptr(depth), _ptr(acc), _stream()),
+           "nerf_render_noalloc")

@@ -237,6 +237,31 @@ size_t nerf_render_workspace_size(const nerf_render_cfg* cfg, int64_t n_rays) {
 nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
                         int64_t n_rays, const nerf_weights* w, const nerf_render_cfg* cfg, float* rgb, float* depth,
                         float* acc, void* stream) {
+    return nerf::render_entry(rays_o, rays_d, t_near, t_far, n_rays, w, cfg, rgb, depth, acc, stream, nullptr, 0);
+}
+
+}  // extern "C"
+
+namespace nerf {
+
+// Rays per launch of the many-network mode that fit `bytes` of workspace
+// (0 if not even one ray does).
+static int64_t kilo_chunk_fitting(const nerf_render_cfg* cfg, int64_t n_rays, size_t bytes) {
+    const int n_cells = cfg->cell_res * cfg->cell_res * cfg->cell_res;
+    int64_t lo = 0, hi = n_rays;  // largest chunk whose layout fits
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (kilo_workspace_layout(mid, cfg->n_coarse, n_cells, nullptr, nullptr) <= bytes)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+nerf_status render_entry(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
+                         int64_t n_rays, const nerf_weights* w, const nerf_render_cfg* cfg, float* rgb, float* depth,
+                         float* acc, void* stream, void* fixed_ws, size_t fixed_bytes) {
     NERF_REQUIRE(w && cfg, "nerf_render: NULL weights or cfg");
     NERF_REQUIRE(n_rays >= 0, "nerf_render: n_rays %lld", (long long)n_rays);
     NERF_REQUIRE(cfg->n_coarse >= 1 && cfg->n_coarse <= 256, "nerf_render: n_coarse %d outside 1..256",
@@ -312,20 +337,38 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
     if (cfg->mode == NERF_MODE_KILO) {
         chunk = kilo_chunk(cfg, n_rays);
         const int n_cells = cfg->cell_res * cfg->cell_res * cfg->cell_res;
+        if (fixed_ws) {
+            // the library's fixed scratch: the caller's chunk must fit it;
+            // without one, the largest chunk that fits is used
+            NERF_REQUIRE(!cfg->workspace, "nerf_render_noalloc: cfg.workspace must be NULL (the call uses the "
+                                          "library's fixed scratch)");
+            const int64_t fit = kilo_chunk_fitting(cfg, chunk, fixed_bytes);
+            if (fit < 1 || (cfg->chunk > 0 && fit < chunk))
+                return nerf_fail(NERF_ERR_WORKSPACE,
+                                 "nerf_render_noalloc: a chunk of %lld rays x %d samples needs %zu workspace bytes, "
+                                 "the fixed scratch holds %zu",
+                                 (long long)chunk, cfg->n_coarse,
+                                 kilo_workspace_layout(cfg->chunk > 0 ? chunk : 1, cfg->n_coarse, n_cells, nullptr,
+                                                       nullptr),
+                                 fixed_bytes);
+            chunk = fit;
+        }
         const size_t need = kilo_workspace_layout(chunk, cfg->n_coarse, n_cells, nullptr, nullptr);
-        char* ws = static_cast<char*>(cfg->workspace);
-        if (ws) {
-            if (cfg->workspace_bytes < need)
-                return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: workspace has %zu bytes, needs %zu",
-                                 cfg->workspace_bytes, need);
-            NERF_REQUIRE(aligned16(ws), "nerf_render: workspace must be 16-byte aligned");
-        } else {
-            clear_pending();
-            const hipError_t e = hipMallocAsync(&own_ws, need, as_stream(stream));
-            if (e != hipSuccess)
-                return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: cannot allocate %zu workspace bytes: %s", need,
-                                 hipGetErrorString(e));
-            ws = static_cast<char*>(own_ws);
+        char* ws = fixed_ws ? static_cast<char*>(fixed_ws) : static_cast<char*>(cfg->workspace);
+        if (!fixed_ws) {  // (the fixed scratch fits by the choice of chunk above)
+            if (ws) {
+                if (cfg->workspace_bytes < need)
+                    return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: workspace has %zu bytes, needs %zu",
+                                     cfg->workspace_bytes, need);
+                NERF_REQUIRE(aligned16(ws), "nerf_render: workspace must be 16-byte aligned");
+            } else {
+                clear_pending();
+                const hipError_t e = hipMallocAsync(&own_ws, need, as_stream(stream));
+                if (e != hipSuccess)
+                    return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render: cannot allocate %zu workspace bytes: %s",
+                                     need, hipGetErrorString(e));
+                ws = static_cast<char*>(own_ws);
+            }
         }
         kilo_workspace_layout(chunk, cfg->n_coarse, n_cells, ws, &ka);
         ka.lo = cfg->box_lo;
@@ -377,4 +420,4 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
     return NERF_OK;
 }
 
-}  // extern "C"
+}  // namespace nerf
