@@ -41,10 +41,37 @@ MACS_4x64 = 21952
 MACS_HASH_FIELD = 19712
 MACS_CELL_2x32 = 5088
 
-# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes scaled by a 1 GiB copy (x2.0 and x1.0), keyed by
-# (workload, dtype).  An entry is removed whenever that kernel changes.
-MEASURED_TRAFFIC = {("hierarchical", "bf16"): 512.6e6, ("encode", "f32"): 21.627e9, ("composite", "f32"): 2.012e9}
+# Memory-side bytes per launch of the dominant kernel(s), from rocprofv3
+# FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy (x2.0 and x1.0),
+# keyed by (workload, dtype), with the digest of the sources that define the
+# kernel at the time the counters were taken.  A figure whose sources have
+# changed since is stale and reported as null.
+KERNEL_SOURCES = {
+    "hierarchical": ["render_common.hpp", "render_nerf_bf16.hip", "mlp.hpp", "nets.hpp", "raysteps.hpp",
+                     "common.hpp", "launch.hpp"],
+    "encode": ["kernels.hip", "common.hpp", "launch.hpp"],
+    "composite": ["kernels.hip", "common.hpp", "launch.hpp"],
+    "hashgrid": ["kernels.hip", "raysteps.hpp", "common.hpp", "launch.hpp"],
+}
+MEASURED_TRAFFIC = {
+    ("hashgrid", "f32"): (6.446e9, "a7357bfc988a821a"),
+}
+
+
+def source_digest(workload):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(workload, []):
+        with open(os.path.join(ROOT, "volume_rendering_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, dtype):
+    rec = MEASURED_TRAFFIC.get((workload, dtype))
+    if rec is None or workload not in KERNEL_SOURCES or source_digest(workload) != rec[1]:
+        return None
+    return rec[0]
 
 WORKLOADS = {
     # name: (poses, hemisphere, H, W, focal, n_coarse, n_fine, net kind, chunk)
@@ -204,13 +231,7 @@ def main():
     def step():
         v.nerf_render(ro, rd, near, far, w, cfg, rgb, depth, acc)
 
-    if args.calibrate_copy > 0:
-        src = torch.empty(args.calibrate_copy << 18, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)  # plain device copy of known size, for counter calibration
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(args, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -253,7 +274,7 @@ def main():
                    "net": {1: "8x256", 2: "4x64", 3: "4096 cells 2x32", 4: "hash-field"}[kind],
                    "chunk": wl["chunk"]},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": MEASURED_TRAFFIC.get((args.workload, dt_name)),
+                     "frac": achieved / peak, "traffic": measured_traffic(args.workload, dt_name),
                      "kernel": {1: "k_render_nerf", 2: "k_render_nerf", 3: "kilo pipeline", 4: "k_render_hash"}[kind],
                      "kernel_ms": ms_kernel,
                      "flop_per_launch": flops},
@@ -272,7 +293,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _calibration_copy(args, torch):
+    """One plain device copy of --calibrate-copy MiB, whose FETCH_SIZE and
+    WRITE_SIZE in a counter pass give the scale of those counters."""
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def _timed(args, step, torch):
+    _calibration_copy(args, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -427,8 +461,11 @@ def standalone(args, wl):
             v.nerf_encode_hashgrid(x, grid, out)
 
         units, unit = n, "points/s"
-        bytes_per_unit = 12 + 128  # point in, 32 float32 features out; table gathers are cache traffic
-        kernel = "k_encode_hash"
+        # point in (12 B) + 32 float32 features out (128 B) + 16 levels x 8
+        # corners x 4 B gathered from the tables (512 B); the gathers are
+        # served by L2 and the memory-side cache, not only by HBM
+        bytes_per_unit = 12 + 128 + 512
+        kernel = "k_encode_hash + k_encode_hash_lds"
         config = {"workload": name, "points": n, "levels": 16, "table_size": 2 ** 19, "n_min": 16, "n_max": 2048}
         data = "synthetic: seeded uniform points in the unit cube, tables U(-1e-4, 1e-4) float16"
         if not args.no_cpu_baseline:
@@ -446,7 +483,7 @@ def standalone(args, wl):
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": data, "config": config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": MEASURED_TRAFFIC.get((name, "f32")),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name, "f32"),
                      "kernel": kernel, "kernel_ms": ms_kernel, "bytes_per_launch": bytes_per_unit * units},
     }
     if not args.no_cpu_baseline:

@@ -105,7 +105,10 @@ typedef struct {
     uint32_t size[NERF_HASH_MAX_LEVELS];  /* entries of level l: min(T, (N_l+1)^3) */
     uint64_t offset[NERF_HASH_MAX_LEVELS];/* first entry of level l in `tables` */
     uint64_t total_entries;               /* sum of size[] */
-    const void* tables;                   /* device, float16 [total_entries][n_feat] */
+    const void* tables;                   /* device, float16 [total_entries][n_feat], 8-byte aligned;
+                                             read in aligned 8-byte words, so readable up to
+                                             total_entries rounded up to an even count (any
+                                             allocation rounded to 8 bytes is); at most 2^28 entries */
 } nerf_hashgrid;
 
 /* Weights handed to nerf_render.  Packed networks come from nerf_pack_mlp and

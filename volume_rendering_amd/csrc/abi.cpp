@@ -48,9 +48,12 @@ GridArgs grid_args(const nerf_hashgrid* g) {
     for (int l = 0; l < g->n_levels; ++l) {
         a.res[l] = g->res[l];
         a.direct[l] = g->direct[l];
+        a.size[l] = g->direct[l] ? (uint32_t)((uint64_t)(g->res[l] + 1) * (g->res[l] + 1) * (g->res[l] + 1))
+                                 : g->table_size;
         a.offset[l] = g->offset[l];
     }
     a.tables = g->tables;
+    a.bytes = (int)((g->total_entries + 1) / 2 * 8);
     return a;
 }
 
@@ -62,7 +65,8 @@ nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
                          g->n_levels, g->n_feat);
     if (g->table_size == 0 || (g->table_size & (g->table_size - 1)))
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: table size %u not a power of two", who, g->table_size);
-    if (!aligned4(g->tables)) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 4-byte aligned", who);
+    if ((reinterpret_cast<uintptr_t>(g->tables) & 7u) != 0)
+        return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 8-byte aligned", who);
     for (int l = 0; l < g->n_levels; ++l) {
         const int N = g->res[l];
         if (N < 1 || N > 65535) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d resolution %d", who, l, N);
@@ -74,6 +78,9 @@ nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
         if (g->offset[l] + need > g->total_entries)
             return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d overruns the tables", who, l);
     }
+    if (g->total_entries > ((uint64_t)1 << 28))
+        return nerf_fail(NERF_ERR_UNSUPPORTED, "%s: %llu table entries (at most 2^28)", who,
+                         (unsigned long long)g->total_entries);
     return NERF_OK;
 }
 

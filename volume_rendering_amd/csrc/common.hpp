@@ -10,6 +10,15 @@ namespace nerf {
 
 constexpr int kWave = 64;
 
+// Pointer into LDS (address space 3): reads through it are LDS reads.
+#define NERF_LDS_PTR __attribute__((address_space(3)))*
+
+// Buffer resource word 3 for raw byte-addressed loads (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+// A byte offset beyond any buffer this library builds: such a load returns
+// 0 without accessing memory.
+constexpr uint32_t kBufferOutOfRange = 0xFFFFFFF0u;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -200,22 +200,126 @@ void launch_sh16(const float* dirs, int64_t n, float* out, hipStream_t s) {
 }
 
 // ===========================================================================
-// Hash-grid encoding: one thread per (point, level).
+// Hash-grid encoding ("Instant-NGP - Visual Experiments", shared toolkit,
+// extended to 3D), level-major.  The coarsest direct levels whose tables fit
+// LDS together are staged there by workgroups that each take a large tile of
+// points.  The other levels run as work items (level pair, tile of points)
+// ordered by level, so the workgroups in flight at any moment gather from
+// one pair's tables, which then stay in the L2 of every die instead of all
+// 24 MB of tables competing for it; each point's two levels are written as
+// one 16-byte store.
 // ===========================================================================
-__global__ void __launch_bounds__(256) k_encode_hash(const float* __restrict__ x, int64_t n, GridArgs g,
-                                                     float* __restrict__ out, uint32_t* __restrict__ idx_dbg) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n * g.n_levels) return;
-    const int64_t p = t / g.n_levels;
-    const int l = (int)(t - p * g.n_levels);
-    float f0, f1;
-    grid_level(g, l, x[3 * p], x[3 * p + 1], x[3 * p + 2], f0, f1, idx_dbg ? idx_dbg + 8 * t : nullptr);
-    reinterpret_cast<float2*>(out)[t] = make_float2(f0, f1);
+constexpr int kHashLdsMax = 160 * 1024;  // LDS of one workgroup
+constexpr int kHashLdsTile = 16384;      // points per staged workgroup
+#ifndef NERF_HASH_LPI
+#define NERF_HASH_LPI 2
+#endif
+constexpr int kHashLpi = NERF_HASH_LPI;  // levels per work item
+constexpr int kHashPts = 2;              // points per thread of a work item
+
+// Writes the features of levels l .. l+nl-1 (nl <= 2) of point p.
+__device__ __forceinline__ void store_levels(float* out, int64_t p, int L, int l, int nl, const float (&f)[4]) {
+    float2* o = reinterpret_cast<float2*>(out) + p * L + l;
+    if (nl == 2 && ((reinterpret_cast<uintptr_t>(o) & 15u) == 0)) {
+        *reinterpret_cast<f32x4*>(o) = f32x4{f[0], f[1], f[2], f[3]};
+    } else {
+        o[0] = make_float2(f[0], f[1]);
+        if (nl == 2) o[1] = make_float2(f[2], f[3]);
+    }
+}
+
+__global__ void __launch_bounds__(1024) k_encode_hash_lds(const float* __restrict__ x, int64_t n, GridArgs g,
+                                                          int n_staged, float* __restrict__ out,
+                                                          uint32_t* __restrict__ idx_dbg) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t hash_tab[];
+    // the staged levels are consecutive in the tables: one copy brings them
+    // all (the last word's second entry, if any, is padding)
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(g.tables) + g.offset[0];
+    uint32_t m = 0;
+    for (int l = 0; l < n_staged; ++l) m += g.size[l];
+    for (uint32_t i = threadIdx.x; i < (m + 1) / 2 * 2; i += blockDim.x) hash_tab[i] = i < m ? src[i] : 0u;
+    __syncthreads();
+    const GridTabLds tab{(const uint32_t NERF_LDS_PTR)hash_tab};
+    const int64_t p0 = (int64_t)blockIdx.x * kHashLdsTile;
+    const int64_t p1 = p0 + kHashLdsTile < n ? p0 + kHashLdsTile : n;
+    const int L = g.n_levels;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+        const float ux = x[3 * p], uy = x[3 * p + 1], uz = x[3 * p + 2];
+        uint32_t lo = 0;
+        for (int l = 0; l < n_staged; l += 2) {
+            const int nl = l + 1 < n_staged ? 2 : 1;
+            float f[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < nl; ++j) {
+                grid_level_tab(tab, lo, g.res[l + j], true, g.tmask, ux, uy, uz, f[2 * j], f[2 * j + 1],
+                               idx_dbg ? idx_dbg + 8 * (p * L + l + j) : nullptr);
+                lo += g.size[l + j];
+            }
+            store_levels(out, p, L, l, nl, f);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_encode_hash(const float* __restrict__ x, int64_t n, GridArgs g, int l_first,
+                                                     int tiles, float* __restrict__ out,
+                                                     uint32_t* __restrict__ idx_dbg) {
+    const int l = l_first + (int)(blockIdx.x / tiles) * kHashLpi;
+    const int nl = g.n_levels - l < kHashLpi ? g.n_levels - l : kHashLpi;
+    const int64_t p0 = (int64_t)(blockIdx.x % tiles) * (256 * kHashPts);
+    const int L = g.n_levels;
+    const GridTabGlobal tab(g);
+    // every lookup of the thread (points past the end repeat the last point,
+    // a missing second level repeats the first) is issued before any finishes
+    // (the points are read first: a later read would wait for every lookup)
+    float u[kHashPts][3];
+#pragma unroll
+    for (int j = 0; j < kHashPts; ++j) {
+        int64_t p = p0 + j * 256 + threadIdx.x;
+        p = p < n ? p : n - 1;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) u[j][a] = x[3 * p + a];
+    }
+    GridLookup q[kHashPts][kHashLpi];
+#pragma unroll
+    for (int j = 0; j < kHashPts; ++j)
+#pragma unroll
+        for (int k = 0; k < kHashLpi; ++k) {
+            const int lk = k < nl ? l + k : l;
+            q[j][k].issue(tab, (uint32_t)g.offset[lk], g.res[lk], g.direct[lk] != 0, g.tmask, u[j][0], u[j][1],
+                          u[j][2]);
+        }
+#pragma unroll
+    for (int j = 0; j < kHashPts; ++j) {
+        const int64_t p = p0 + j * 256 + threadIdx.x;
+        if (p < n) {
+            float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < kHashLpi; ++k)
+                if (k < nl) q[j][k].finish(f[2 * k], f[2 * k + 1], idx_dbg ? idx_dbg + 8 * (p * L + l + k) : nullptr);
+            store_levels(out, p, L, l, kHashLpi < 2 ? 1 : nl, f);
+        }
+    }
 }
 
 void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out, uint32_t* idx, hipStream_t s) {
-    const int64_t tot = n * g.n_levels;
-    hipLaunchKernelGGL(k_encode_hash, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, x, n, g, out, idx);
+    // levels are in increasing resolution: the staged ones are a prefix of
+    // direct levels whose tables fit LDS together
+    int n_staged = 0;
+    size_t lds_bytes = 0;
+    while (n_staged < g.n_levels && g.direct[n_staged] &&
+           lds_bytes + (size_t)g.size[n_staged] * 4 + 8 <= (size_t)kHashLdsMax) {
+        lds_bytes += (size_t)g.size[n_staged] * 4;
+        ++n_staged;
+    }
+    lds_bytes = (lds_bytes + 7) / 8 * 8;  // whole 8-byte words
+    if (n_staged > 0)
+        hipLaunchKernelGGL(k_encode_hash_lds, dim3((unsigned)((n + kHashLdsTile - 1) / kHashLdsTile)), dim3(1024),
+                           lds_bytes, s, x, n, g, n_staged, out, idx);
+    if (n_staged < g.n_levels) {
+        const int tiles = (int)((n + 256 * kHashPts - 1) / (256 * kHashPts));
+        const int items = (g.n_levels - n_staged + kHashLpi - 1) / kHashLpi;
+        hipLaunchKernelGGL(k_encode_hash, dim3((unsigned)((int64_t)tiles * items)), dim3(256), 0, s, x, n, g,
+                           n_staged, tiles, out, idx);
+    }
 }
 
 // ===========================================================================

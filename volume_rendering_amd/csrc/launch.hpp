@@ -13,8 +13,10 @@ struct GridArgs {
     uint32_t tmask;  // T - 1 (T a power of two)
     int res[16];
     int direct[16];
+    uint32_t size[16];  // entries of each level
     uint64_t offset[16];
     const void* tables;  // float16 pairs, levels back to back
+    int bytes;           // bytes readable from tables: entries rounded up to whole 8-byte words
 };
 
 struct RenderArgs {

@@ -83,8 +83,6 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 constexpr int kChunkBytes = NERF_CHUNK_KB * 1024;
 static_assert(kTileRegionAlign % kChunkBytes == 0, "chunks tile the padded weight region");
 constexpr int kChunkDma = kChunkBytes / 1024 / 4;  // 1 KB copies per wave per chunk
-// Buffer resource word 3 for raw byte-addressed loads (32-bit data format).
-constexpr int kBufferWord3 = 0x00020000;
 
 static __shared__ __attribute__((aligned(1024))) char g_ring0[kChunkBytes];
 static __shared__ __attribute__((aligned(1024))) char g_ring1[kChunkBytes];

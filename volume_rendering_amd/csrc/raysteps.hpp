@@ -256,31 +256,123 @@ __device__ __forceinline__ uint32_t grid_index(int ix, int iy, int iz, int N, bo
     return ((uint32_t)ix ^ ((uint32_t)iy * 2654435761u) ^ ((uint32_t)iz * 805459861u)) & tmask;
 }
 
-// Interpolated features (f0, f1) of level l at unit-cube point u; corner
-// indices optionally written to idx_out[0..8).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Grid tables for the lookups, addressed by absolute entry (level offset +
+// index; entry = two float16 features in 32 bits, the first in the low
+// half), read in aligned 8-byte words.  Global tables go through a buffer
+// resource: a load whose entry is not needed gets an out-of-range offset and
+// returns 0 without touching memory, so every load issues unconditionally.
+struct GridTabGlobal {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit GridTabGlobal(const GridArgs& g)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.tables), (short)0, g.bytes, kBufferWord3)) {}
+    __device__ __forceinline__ u32x2 word(uint32_t a) const {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)(a * 4u), 0, 0));
+    }
+    __device__ __forceinline__ uint32_t entry_unless(uint32_t a, bool skip) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(skip ? kBufferOutOfRange : a * 4u), 0, 0);
+    }
+};
+
+// Tables staged in LDS (8-byte aligned, padded to whole words).
+struct GridTabLds {
+    const uint32_t NERF_LDS_PTR t;
+    __device__ __forceinline__ u32x2 word(uint32_t a) const { return *reinterpret_cast<const u32x2 NERF_LDS_PTR>(t + a); }
+    __device__ __forceinline__ uint32_t entry_unless(uint32_t a, bool) const { return t[a]; }
+};
+
+__device__ __forceinline__ float half_lo(uint32_t e) { return __half2float(__ushort_as_half((unsigned short)(e & 0xFFFFu))); }
+__device__ __forceinline__ float half_hi(uint32_t e) { return __half2float(__ushort_as_half((unsigned short)(e >> 16))); }
+
+// One level lookup (resolution N, direct or hashed, entries from absolute
+// entry `off` of `tab`) at a unit-cube point, in two phases so that the
+// loads of several lookups can be in flight together: issue() computes the
+// corner entries and starts their loads, finish() interpolates.
+//
+// The 8 corners are taken in 4 pairs along the axis whose neighbours are
+// often adjacent entries: z on direct levels (entries idx, idx + 1), x on
+// hashed levels (for even ix the entries idx and idx ^ 1).  The aligned
+// 8-byte word holding a pair's first entry is always read; the second entry
+// is read separately only when it lies in another word.
+struct GridLookup {
+    u32x2 W[4];
+    uint32_t B[4], A0[4], A1[4];
+    bool P[4];
+    float wx, wy, wz;
+    uint32_t off;
+    bool direct;
+
+    template <class Tab>
+    __device__ __forceinline__ void issue(const Tab& tab, uint32_t off_, int N, bool direct_, uint32_t tmask, float ux,
+                                          float uy, float uz) {
+        off = off_;
+        direct = direct_;
+        const float cx = __fmul_rn(ux, (float)N), cy = __fmul_rn(uy, (float)N), cz = __fmul_rn(uz, (float)N);
+        const float fx = floorf(cx), fy = floorf(cy), fz = floorf(cz);
+        wx = cx - fx;
+        wy = cy - fy;
+        wz = cz - fz;
+        const int x0 = (int)fx, y0 = (int)fy, z0 = (int)fz;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int qa = q >> 1, qb = q & 1;
+            const int dx0 = direct ? qa : 0, dx1 = direct ? qa : 1;
+            const int dy0 = direct ? qb : qa;
+            const int dz0 = direct ? 0 : qb, dz1 = direct ? 1 : qb;
+            const int iy = min(max(y0 + dy0, 0), N);
+            const int ixa = min(max(x0 + dx0, 0), N), ixb = min(max(x0 + dx1, 0), N);
+            const int iza = min(max(z0 + dz0, 0), N), izb = min(max(z0 + dz1, 0), N);
+            A0[q] = off + grid_index(ixa, iy, iza, N, direct, tmask);
+            A1[q] = off + grid_index(ixb, iy, izb, N, direct, tmask);
+            P[q] = (A0[q] >> 1) == (A1[q] >> 1);
+            W[q] = tab.word(A0[q] & ~1u);
+            B[q] = tab.entry_unless(A1[q], P[q]);
+        }
+    }
+
+    // Features (f0, f1); corner indices optionally to idx_out[0..8)
+    // (lexicographic, x most significant).
+    __device__ __forceinline__ void finish(float& f0, float& f1, uint32_t* idx_out) const {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int qa = q >> 1, qb = q & 1;
+            const int dx0 = direct ? qa : 0, dx1 = direct ? qa : 1;
+            const int dy0 = direct ? qb : qa;
+            const int dz0 = direct ? 0 : qb, dz1 = direct ? 1 : qb;
+            if (idx_out) {
+                idx_out[4 * dx0 + 2 * dy0 + dz0] = A0[q] - off;
+                idx_out[4 * dx1 + 2 * dy0 + dz1] = A1[q] - off;
+            }
+            const uint32_t e0 = (A0[q] & 1u) ? W[q].y : W[q].x;
+            const uint32_t e1 = P[q] ? ((A1[q] & 1u) ? W[q].y : W[q].x) : B[q];
+            const float wt0 = (dx0 ? wx : 1.0f - wx) * (dy0 ? wy : 1.0f - wy) * (dz0 ? wz : 1.0f - wz);
+            const float wt1 = (dx1 ? wx : 1.0f - wx) * (dy0 ? wy : 1.0f - wy) * (dz1 ? wz : 1.0f - wz);
+            a0 += wt0 * half_lo(e0);
+            a1 += wt0 * half_hi(e0);
+            a0 += wt1 * half_lo(e1);
+            a1 += wt1 * half_hi(e1);
+        }
+        f0 = a0;
+        f1 = a1;
+    }
+};
+
+template <class Tab>
+__device__ __forceinline__ void grid_level_tab(const Tab& tab, uint32_t off, int N, bool direct, uint32_t tmask,
+                                               float ux, float uy, float uz, float& f0, float& f1,
+                                               uint32_t* idx_out) {
+    GridLookup q;
+    q.issue(tab, off, N, direct, tmask, ux, uy, uz);
+    q.finish(f0, f1, idx_out);
+}
+
+// Level l of grid g, tables in global memory.
 __device__ __forceinline__ void grid_level(const GridArgs& g, int l, float ux, float uy, float uz, float& f0, float& f1,
                                            uint32_t* idx_out) {
-    const int N = g.res[l];
-    const bool direct = g.direct[l] != 0;
-    const float cx = __fmul_rn(ux, (float)N), cy = __fmul_rn(uy, (float)N), cz = __fmul_rn(uz, (float)N);
-    const float fx = floorf(cx), fy = floorf(cy), fz = floorf(cz);
-    const float wx = cx - fx, wy = cy - fy, wz = cz - fz;
-    const int x0 = (int)fx, y0 = (int)fy, z0 = (int)fz;
-    const __half2* tab = reinterpret_cast<const __half2*>(g.tables) + g.offset[l];
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int dx = (c >> 2) & 1, dy = (c >> 1) & 1, dz = c & 1;
-        const int ix = min(max(x0 + dx, 0), N), iy = min(max(y0 + dy, 0), N), iz = min(max(z0 + dz, 0), N);
-        const uint32_t idx = grid_index(ix, iy, iz, N, direct, g.tmask);
-        if (idx_out) idx_out[c] = idx;
-        const float2 v = __half22float2(tab[idx]);
-        const float wt = (dx ? wx : 1.0f - wx) * (dy ? wy : 1.0f - wy) * (dz ? wz : 1.0f - wz);
-        a0 += wt * v.x;
-        a1 += wt * v.y;
-    }
-    f0 = a0;
-    f1 = a1;
+    const GridTabGlobal tab(g);
+    grid_level_tab(tab, (uint32_t)g.offset[l], g.res[l], g.direct[l] != 0, g.tmask, ux, uy, uz, f0, f1, idx_out);
 }
 
 }  // namespace nerf
