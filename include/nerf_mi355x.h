@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define NERF_ABI_VERSION 1
+#define NERF_ABI_VERSION 2
 
 typedef enum {
     NERF_OK = 0,
@@ -92,9 +92,10 @@ typedef struct {
     float fx, fy, cx, cy;
 } nerf_intrinsics;
 
-/* Multiresolution grid over [0,1]^3 ("Instant-NGP - Visual Experiments",
- * shared toolkit ``HashGrid2D``, generalised to 3D).  Filled by
- * nerf_hashgrid_init(); `tables` is set by the caller. */
+/* Multiresolution grid over [0,1]^dim ("Instant-NGP - Visual Experiments",
+ * shared toolkit ``HashGrid2D``, and its generalisation to 3D).  Filled by
+ * nerf_hashgrid_init(); `tables` is set by the caller; `level_mask` may be
+ * changed by the caller. */
 #define NERF_HASH_MAX_LEVELS 16
 typedef struct {
     int32_t n_levels;                     /* L <= 16 */
@@ -109,6 +110,11 @@ typedef struct {
                                              read in aligned 8-byte words, so readable up to
                                              total_entries rounded up to an even count (any
                                              allocation rounded to 8 bytes is); at most 2^28 entries */
+    int32_t dim;                          /* 2 or 3 */
+    float level_mask[NERF_HASH_MAX_LEVELS];/* level l's features are multiplied by level_mask[l]
+                                             (the toolkit's level_mask: coarse-to-fine evaluation);
+                                             nerf_encode_hashgrid does not look up a level whose
+                                             mask is 0; init: 1 */
 } nerf_hashgrid;
 
 /* Weights handed to nerf_render.  Packed networks come from nerf_pack_mlp and
@@ -162,12 +168,14 @@ const char* nerf_last_error(void);
 /* Host helpers                                                           */
 /* ---------------------------------------------------------------------- */
 
-/* Fills res/direct/size/offset/total_entries of `g` (host) for L levels with
- * resolutions N_l = round(n_min * b^l), b = exp((ln n_max - ln n_min)/(L-1)),
- * direct indexing where (N_l+1)^3 <= T ("Instant-NGP - Visual Experiments",
- * shared toolkit; Experiment 1).  n_feat is set to 2, tables to NULL.
- * Errors: L outside 2..16, T not a power of two, n_min < 1, n_max < n_min. */
-nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int n_levels, uint32_t table_size, int n_min, int n_max);
+/* Fills res/direct/size/offset/total_entries of `g` (host) for a grid over
+ * [0,1]^dim with L levels of resolutions N_l = round(n_min * b^l),
+ * b = exp((ln n_max - ln n_min)/(L-1)), direct indexing where
+ * (N_l+1)^dim <= T ("Instant-NGP - Visual Experiments", shared toolkit;
+ * Experiments 1 and 4).  n_feat is set to 2, tables to NULL, every
+ * level_mask to 1.  Errors: dim not 2 or 3, L outside 2..16, T not a power
+ * of two, n_min < 1, n_max < n_min. */
+nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int dim, int n_levels, uint32_t table_size, int n_min, int n_max);
 
 /* Bytes of one packed network of this description (0 if unsupported). */
 size_t nerf_mlp_packed_bytes(const nerf_mlp_desc* net);
@@ -232,17 +240,19 @@ nerf_status nerf_encode_freq(const float* x, int64_t n, int in_dim, int n_freq, 
  * dirs: device [n, 3] (normalised inside); out: device [n, 16]. */
 nerf_status nerf_encode_sh16(const float* dirs, int64_t n, float* out, void* stream);
 
-/* Multiresolution hash-grid encoding in 3D ("Instant-NGP - Visual
- * Experiments", shared toolkit ``HashGrid2D.encode``, extended to 3D): per
- * level c = x*N_l (float32), c0 = floor(c), w = c - c0; for the 8 corners
+/* Multiresolution hash-grid encoding ("Instant-NGP - Visual Experiments",
+ * shared toolkit ``HashGrid2D.encode``, and its extension to 3D): per level
+ * c = x*N_l (float32), c0 = floor(c), w = c - c0; for the 2^dim corners
  * (lexicographic, x most significant) corner coordinates clamped to [0,N_l];
- * index ((ix*(N+1)) + iy)*(N+1) + iz on direct levels, else
- * (ix*1 ^ iy*2654435761 ^ iz*805459861) mod T; feature = sum over corners of
- * prod(w or 1-w) * table[index]; levels concatenated (level-major, then
- * feature).  x: device [n, 3] (points outside [0,1]^3 use clamped corners);
- * out: device [n, L*2]; idx_dbg: optional device uint32 [n, L, 8] corner
- * indices.  Errors: null pointers, n < 0, grid not initialised, null
- * tables. */
+ * index ix*(N+1) + iy (2D) or ((ix*(N+1)) + iy)*(N+1) + iz (3D) on direct
+ * levels, else (ix ^ iy*2654435761) mod T (2D) or
+ * (ix*1 ^ iy*2654435761 ^ iz*805459861) mod T (3D); feature = level_mask[l]
+ * * sum over corners of prod(w or 1-w) * table[index]; levels concatenated
+ * (level-major, then feature).  x: device [n, dim] (points outside the unit
+ * cube use clamped corners); out: device [n, L*2]; idx_dbg: optional device
+ * uint32 [n, L, 2^dim] corner indices (levels with mask 0 are not looked up
+ * and their indices are not written).  Errors: null pointers, n < 0, grid
+ * not initialised, null tables. */
 nerf_status nerf_encode_hashgrid(const float* x, int64_t n, const nerf_hashgrid* g, float* out, uint32_t* idx_dbg,
                                  void* stream);
 
@@ -304,6 +314,20 @@ nerf_status nerf_sample_pdf(const float* z_coarse, const float* w_coarse, int64_
 nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
                         int64_t n_rays, const nerf_weights* w, const nerf_render_cfg* cfg, float* rgb, float* depth,
                         float* acc, void* stream);
+
+/* One image per camera pose (Section 2 Code, 1. Overview: render_image and
+ * the video of a pose sweep).  For frame f: the rays of pose f and camera K
+ * (as nerf_gen_rays), t_near and t_far for every ray, then nerf_render with
+ * cfg.ray_offset + f*W*H as the ray offset, so every pixel of every frame has
+ * its own random-number counters.  poses: host [n_poses][12] row-major 3x4
+ * camera-to-world; rgb: device [n_poses, H*W, 3]; depth, acc: device
+ * [n_poses, H*W].  workspace: device, 16-byte aligned, at least 32*W*H bytes
+ * (one frame's rays and near/far), or NULL: allocated stream-ordered and
+ * freed after the work.  The debug outputs of cfg must be NULL.
+ * Errors: as nerf_gen_rays and nerf_render; workspace too small. */
+nerf_status nerf_render_poses(const float* poses, int n_poses, const nerf_intrinsics* K, float t_near, float t_far,
+                              const nerf_weights* w, const nerf_render_cfg* cfg, void* workspace,
+                              size_t workspace_bytes, float* rgb, float* depth, float* acc, void* stream);
 
 /* Device workspace nerf_render needs for this configuration (0 for NERF and
  * HASH modes). */

@@ -59,14 +59,14 @@ def render_nerf(rays_o, rays_d, t_near, t_far, coarse, fine=None, n_coarse=64, n
 
 
 def render_hash(rays_o, rays_d, t_near, t_far, grid, tables, field, n_samples=128, seed=0, jitter=True,
-                mode="f64", box=(-1.5, 1.5), white_bkgd=False, ray_offset=0):
+                mode="f64", box=(-1.5, 1.5), white_bkgd=False, ray_offset=0, level_mask=None):
     """Hash-grid field render: stratified samples, world box mapped to the
-    unit cube, grid features, spherical-harmonics direction encoding, field
-    network, compositing."""
+    unit cube, grid features (times the optional per-level mask), spherical
+    harmonics direction encoding, field network, compositing."""
     z = sampling.stratified(t_near, t_far, n_samples, seed, jitter, ray_offset)
     R, N = z.shape
     x = sampling.points(rays_o, rays_d, z).reshape(-1, 3)
-    feats = grid.encode(encoding.world_to_unit(x, *box), tables)
+    feats = grid.encode(encoding.world_to_unit(x, *box), tables, level_mask)
     de = np.repeat(encoding.sh16(sampling.view_dirs(rays_d)), N, axis=0)
     raw = mlp.hash_field_forward(field, feats, de, mode).reshape(R, N, 4)
     rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd)
@@ -94,7 +94,7 @@ def kilo_classify(x, occ_dense, occ_res=128, cells=16, box=(-1.5, 1.5)):
 
 def render_kilo(rays_o, rays_d, t_near, t_far, occ_dense, cell_nets, n_samples=192, seed=0, jitter=True,
                 term_T=1e-2, L_pos=10, L_dir=4, mode="f64", use_pi=True, occ_res=128, cells=16,
-                box=(-1.5, 1.5), ray_offset=0):
+                box=(-1.5, 1.5), ray_offset=0, white_bkgd=False):
     """Many tiny networks.  ``cell_nets(c)`` returns the parameters of cell
     c.  Dead samples (outside the box or in an empty voxel) have density 0;
     compositing stops a ray at the first sample whose transmittance is below
@@ -112,5 +112,5 @@ def render_kilo(rays_o, rays_d, t_near, t_far, occ_dense, cell_nets, n_samples=1
         r_sel, s_sel = rr[sel], ss[sel]
         pe = encoding.freq_encode(x[r_sel, s_sel], L_pos, True, use_pi)
         raw[r_sel, s_sel] = mlp.nerf_forward(cell_nets(int(c)), pe, vdir[r_sel], mode)
-    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, False, term_T)
+    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd, term_T)
     return dict(z=z, raw=raw, rgb=rgb, depth=depth, acc=acc, w=w, live=live, cell=cell, n_live=int(live.sum()))

@@ -65,6 +65,19 @@ def poses(n: int, seed: int = 0, radius: float = 4.0, hemisphere: bool = True) -
     return np.stack(out).astype(np.float32)
 
 
+def sweep_poses(n: int, elevation_deg: float = 30.0, radius: float = 4.0) -> np.ndarray:
+    """``n`` poses evenly spaced in azimuth around the scene (a 360 degree
+    sweep at a fixed elevation and radius), each looking at the origin.
+    Deterministic; returns float32 [n,3,4]."""
+    el = math.radians(elevation_deg)
+    out = []
+    for k in range(n):
+        az = 2.0 * math.pi * k / n
+        p = radius * np.array([math.cos(el) * math.cos(az), math.cos(el) * math.sin(az), math.sin(el)])
+        out.append(look_at_pose(p))
+    return np.stack(out).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------
 # Network weights (float32, row-major [out, in])
 # ----------------------------------------------------------------------------

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = v.lib()
-    assert v.nerf_abi_version() == 1
+    assert v.nerf_abi_version() == 2
     assert L.nerf_status_str(0) == b"NERF_OK"
     assert L.nerf_status_str(3) == b"NERF_ERR_WORKSPACE"
 
@@ -53,11 +53,27 @@ def test_hashgrid_init_matches_oracle_layout():
         assert list(g.offset)[:Lv] == list(np.cumsum([0] + og.sizes[:-1]))
 
 
+def test_hashgrid_init_2d_reproduces_the_printed_tables(golden_dir):
+    # Experiment 1 (T = 2^12) and Experiment 4 (T = 2^8, 2^14), 8 levels from 8 to 160
+    rows = [l.split() for l in open(os.path.join(golden_dir, "hashgrid2d_experiment1.txt")) if l[0] != "#"]
+    g = v.nerf_hashgrid_init(8, 2 ** 12, 8, 160, dim=2)
+    assert g.dim == 2 and list(g.level_mask)[:8] == [1.0] * 8
+    assert list(g.res)[:8] == [int(r[1]) for r in rows]
+    assert [bool(d) for d in list(g.direct)[:8]] == [r[3] == "direct" for r in rows]
+    assert list(g.size)[:8] == [min(int(r[2]), 2 ** 12) for r in rows]
+    for r in (l.split() for l in open(os.path.join(golden_dir, "hashgrid2d_experiment4.txt")) if l[0] != "#"):
+        T, n_hash, L = map(int, r)
+        g = v.nerf_hashgrid_init(L, T, 8, 160, dim=2)
+        assert sum(not d for d in list(g.direct)[:L]) == n_hash
+
+
 def test_hashgrid_init_rejects_bad_arguments():
     for args in ((1, 2 ** 19, 16, 2048), (17, 2 ** 19, 16, 2048), (16, 3000, 16, 2048), (16, 2 ** 19, 0, 10),
                  (16, 2 ** 19, 20, 10)):
         with pytest.raises(v.NerfError, match="INVALID_ARGUMENT"):
             v.nerf_hashgrid_init(*args)
+    with pytest.raises(v.NerfError, match="INVALID_ARGUMENT"):
+        v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048, dim=4)
 
 
 def _unpack_layer(buf, kind, prec, li, layers, n_in):
@@ -176,3 +192,34 @@ def test_validation_errors_before_any_launch():
     assert L.nerf_sample_stratified(None, None, 0, 16, 0, 0, 1, None, None) == 0
     assert L.nerf_composite(None, None, None, 0, 64, 0, None, None, None, None, None) == 0
     assert L.nerf_sample_pdf(None, None, 0, 64, 128, 0, 0, None, None, None, None) == 0
+
+
+def test_render_poses_validation():
+    L = v.lib()
+    K = B.nerf_intrinsics(8, 8, 10.0, 10.0, 4.0, 4.0)
+    cfg = B.nerf_render_cfg(mode=0, n_coarse=16)
+    w = B.nerf_weights(net=B.nerf_mlp_desc(2, 0))
+    # no poses: nothing to do
+    assert L.nerf_render_poses(None, 0, C.byref(K), 2.0, 6.0, C.byref(w), C.byref(cfg), None, 0, None, None, None,
+                               None) == 0
+    # debug outputs are refused, before anything is launched
+    cfg.dbg_z = 16
+    assert L.nerf_render_poses(None, 2, C.byref(K), 2.0, 6.0, C.byref(w), C.byref(cfg), None, 0, None, None, None,
+                               None) == 1
+    assert b"debug outputs" in L.nerf_last_error()
+    cfg.dbg_z = None
+    assert L.nerf_render_poses(None, 2, C.byref(K), 2.0, 6.0, C.byref(w), C.byref(cfg), None, 0, None, None, None,
+                               None) == 1
+    bad = B.nerf_intrinsics(0, 8, 10.0, 10.0, 4.0, 4.0)
+    assert L.nerf_render_poses(None, 2, C.byref(bad), 2.0, 6.0, C.byref(w), C.byref(cfg), None, 0, None, None, None,
+                               None) == 1
+
+
+def test_sweep_poses_look_at_the_origin():
+    P = si.sweep_poses(24, elevation_deg=30.0, radius=4.0)
+    assert P.shape == (24, 3, 4)
+    for p in P:
+        t = p[:, 3].astype(np.float64)
+        assert abs(np.linalg.norm(t) - 4.0) < 1e-5 and abs(t[2] - 2.0) < 1e-5  # 4 sin 30
+        # the camera looks down its -z axis: the third column points away from the origin
+        assert np.allclose(p[:, 2], t / 4.0, atol=1e-6)

@@ -267,12 +267,13 @@ def test_render_tiny_coarse_fp32(v):
     assert max_abs(dw, ref["coarse"]["w"]) <= 1e-5
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
-def test_render_hierarchical_stage_isolated(v, dtype):
+@pytest.mark.parametrize("dtype,white", [(0, False), (1, False), (0, True)])
+def test_render_hierarchical_stage_isolated(v, dtype, white):
     """Coarse 64 + fine 128 with 4x64 networks: coarse weights against the
     oracle, bins and merged samples bit-exact from the GPU's own coarse
-    weights, fine colour from the GPU's own merged samples."""
-    say(f"render hierarchical 4x64 dtype={dtype}")
+    weights, fine colour from the GPU's own merged samples (also on a white
+    background)."""
+    say(f"render hierarchical 4x64 dtype={dtype} white={white}")
     pose = si.poses(1, seed=3)[0]
     H = W = 24
     ro, rd = gpu_rays(H, W, 30.0, pose)
@@ -281,13 +282,13 @@ def test_render_hierarchical_stage_isolated(v, dtype):
     near, far = _near_far(R)
     pc, pf = si.nerf_params(si.NERF_4x64, seed=5, net_id=0), si.nerf_params(si.NERF_4x64, seed=5, net_id=1)
     nets = [v.weights.pack_to_device(2, dtype, pc), v.weights.pack_to_device(2, dtype, pf)]
-    rgb, depth, acc, dz, dw = _render(v, 0, 2, dtype, ro, rd, near, far, nets, 64, 128, seed=9)
+    rgb, depth, acc, dz, dw = _render(v, 0, 2, dtype, ro, rd, near, far, nets, 64, 128, seed=9, white=white)
     mode = "f64" if dtype == 0 else "bf16"
     ref_c = oren.render_nerf(o, d, near, far, pc, None, 64, 0, 6, 4, seed=9, mode=mode)
     assert max_abs(dw, ref_c["coarse"]["w"]) <= (1e-5 if dtype == 0 else 2e-2)
     _, _, z2 = osamp.hierarchical_fine_samples(ref_c["z_c"], dw, 128, 9)
     assert np.array_equal(dz, z2)
-    fine = oren.nerf_pass(pf, o, d, dz, 6, 4, "f64")
+    fine = oren.nerf_pass(pf, o, d, dz, 6, 4, "f64", white_bkgd=white)
     if dtype == 0:
         assert max_abs(rgb, fine["rgb"]) <= RGB_TOL
         assert max_abs(acc, fine["acc"]) <= ACC_TOL

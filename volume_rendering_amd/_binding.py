@@ -26,7 +26,7 @@ EXPORTED = [
     "nerf_abi_version", "nerf_status_str", "nerf_last_error", "nerf_hashgrid_init", "nerf_mlp_packed_bytes",
     "nerf_pack_mlp", "nerf_gen_rays", "nerf_sample_stratified", "nerf_encode_freq", "nerf_encode_sh16",
     "nerf_encode_hashgrid", "nerf_mlp", "nerf_composite", "nerf_sample_pdf", "nerf_render",
-    "nerf_render_workspace_size", "nerf_render_noalloc",
+    "nerf_render_workspace_size", "nerf_render_noalloc", "nerf_render_poses",
 ]
 
 
@@ -47,7 +47,8 @@ class nerf_hashgrid(C.Structure):
     _fields_ = [("n_levels", C.c_int32), ("n_feat", C.c_int32), ("table_size", C.c_uint32),
                 ("res", C.c_int32 * HASH_MAX_LEVELS), ("direct", C.c_int32 * HASH_MAX_LEVELS),
                 ("size", C.c_uint32 * HASH_MAX_LEVELS), ("offset", C.c_uint64 * HASH_MAX_LEVELS),
-                ("total_entries", C.c_uint64), ("tables", C.c_void_p)]
+                ("total_entries", C.c_uint64), ("tables", C.c_void_p), ("dim", C.c_int32),
+                ("level_mask", C.c_float * HASH_MAX_LEVELS)]
 
 
 class nerf_weights(C.Structure):
@@ -76,7 +77,7 @@ def lib():
             "nerf_abi_version": (I, []),
             "nerf_status_str": (C.c_char_p, [I]),
             "nerf_last_error": (C.c_char_p, []),
-            "nerf_hashgrid_init": (I, [C.POINTER(nerf_hashgrid), I, C.c_uint32, I, I]),
+            "nerf_hashgrid_init": (I, [C.POINTER(nerf_hashgrid), I, I, C.c_uint32, I, I]),
             "nerf_mlp_packed_bytes": (S, [C.POINTER(nerf_mlp_desc)]),
             "nerf_pack_mlp": (I, [C.POINTER(nerf_mlp_desc), C.POINTER(C.c_void_p), I, P, S]),
             "nerf_gen_rays": (I, [P, C.POINTER(nerf_intrinsics), P, P, P]),
@@ -91,6 +92,8 @@ def lib():
             "nerf_render_workspace_size": (S, [C.POINTER(nerf_render_cfg), I64]),
             "nerf_render_noalloc": (I, [P, P, P, P, I64, C.POINTER(nerf_weights), C.POINTER(nerf_render_cfg), P, P,
                                         P, P]),
+            "nerf_render_poses": (I, [P, I, C.POINTER(nerf_intrinsics), C.c_float, C.c_float, C.POINTER(nerf_weights),
+                                      C.POINTER(nerf_render_cfg), P, S, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -127,9 +130,9 @@ def nerf_abi_version() -> int:
     return lib().nerf_abi_version()
 
 
-def nerf_hashgrid_init(n_levels=16, table_size=2 ** 19, n_min=16, n_max=2048) -> nerf_hashgrid:
+def nerf_hashgrid_init(n_levels=16, table_size=2 ** 19, n_min=16, n_max=2048, dim=3) -> nerf_hashgrid:
     g = nerf_hashgrid()
-    _check(lib().nerf_hashgrid_init(C.byref(g), n_levels, table_size, n_min, n_max), "nerf_hashgrid_init")
+    _check(lib().nerf_hashgrid_init(C.byref(g), dim, n_levels, table_size, n_min, n_max), "nerf_hashgrid_init")
     return g
 
 
@@ -214,3 +217,16 @@ def nerf_render_noalloc(rays_o, rays_d, t_near, t_far, weights: nerf_weights, cf
     _check(lib().nerf_render_noalloc(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), rays_o.shape[0],
                                      C.byref(weights), C.byref(cfg), _ptr(rgb), _ptr(depth), _ptr(acc), _stream()),
            "nerf_render_noalloc")
+
+
+def nerf_render_poses(poses: np.ndarray, W, H, fx, fy, cx, cy, t_near, t_far, weights: nerf_weights,
+                      cfg: nerf_render_cfg, rgb, depth, acc, workspace=None):
+    """One image per pose: ``poses`` host float32 [n, 3, 4]; rgb [n, H*W, 3],
+    depth and acc [n, H*W] device tensors; ``workspace`` an optional device
+    uint8 tensor of at least 32*W*H bytes."""
+    K = nerf_intrinsics(W, H, fx, fy, cx, cy)
+    p = np.ascontiguousarray(poses, dtype=np.float32).reshape(-1, 12)
+    ws, wsb = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().nerf_render_poses(p.ctypes.data, p.shape[0], C.byref(K), float(t_near), float(t_far),
+                                   C.byref(weights), C.byref(cfg), ws, wsb, _ptr(rgb), _ptr(depth), _ptr(acc),
+                                   _stream()), "nerf_render_poses")

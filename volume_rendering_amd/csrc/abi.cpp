@@ -44,13 +44,15 @@ bool net_is_nerf_family(int kind) { return kind == NET_8x256 || kind == NET_4x64
 GridArgs grid_args(const nerf_hashgrid* g) {
     GridArgs a{};
     a.n_levels = g->n_levels;
+    a.dim = g->dim;
     a.tmask = g->table_size - 1;
     for (int l = 0; l < g->n_levels; ++l) {
+        const uint64_t n1 = (uint64_t)g->res[l] + 1;
         a.res[l] = g->res[l];
         a.direct[l] = g->direct[l];
-        a.size[l] = g->direct[l] ? (uint32_t)((uint64_t)(g->res[l] + 1) * (g->res[l] + 1) * (g->res[l] + 1))
-                                 : g->table_size;
+        a.size[l] = g->direct[l] ? (uint32_t)(n1 * n1 * (g->dim == 3 ? n1 : 1u)) : g->table_size;
         a.offset[l] = g->offset[l];
+        a.mask[l] = g->level_mask[l];
     }
     a.tables = g->tables;
     a.bytes = (int)((g->total_entries + 1) / 2 * 8);
@@ -67,10 +69,11 @@ nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: table size %u not a power of two", who, g->table_size);
     if ((reinterpret_cast<uintptr_t>(g->tables) & 7u) != 0)
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 8-byte aligned", who);
+    if (g->dim != 2 && g->dim != 3) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid dim %d", who, g->dim);
     for (int l = 0; l < g->n_levels; ++l) {
         const int N = g->res[l];
         if (N < 1 || N > 65535) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d resolution %d", who, l, N);
-        const uint64_t verts = (uint64_t)(N + 1) * (N + 1) * (N + 1);
+        const uint64_t verts = (uint64_t)(N + 1) * (N + 1) * (g->dim == 3 ? (uint64_t)(N + 1) : 1u);
         const uint64_t need = g->direct[l] ? verts : g->table_size;
         if (g->direct[l] && verts > g->table_size)
             return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: level %d marked direct but has %llu vertices", who, l,
@@ -247,6 +250,60 @@ nerf_status nerf_render(const float* rays_o, const float* rays_d, const float* t
     return nerf::render_entry(rays_o, rays_d, t_near, t_far, n_rays, w, cfg, rgb, depth, acc, stream, nullptr, 0);
 }
 
+nerf_status nerf_render_poses(const float* poses, int n_poses, const nerf_intrinsics* K, float t_near, float t_far,
+                              const nerf_weights* w, const nerf_render_cfg* cfg, void* workspace,
+                              size_t workspace_bytes, float* rgb, float* depth, float* acc, void* stream) {
+    NERF_REQUIRE(n_poses >= 0, "nerf_render_poses: n_poses %d", n_poses);
+    NERF_REQUIRE(K && w && cfg, "nerf_render_poses: NULL camera, weights or cfg");
+    NERF_REQUIRE(K->W >= 1 && K->H >= 1 && (int64_t)K->W * K->H <= (int64_t)1 << 31,
+                 "nerf_render_poses: image %dx%d", K->W, K->H);
+    NERF_REQUIRE(K->fx != 0.0f && K->fy != 0.0f, "nerf_render_poses: zero focal length");
+    NERF_REQUIRE(!cfg->dbg_z && !cfg->dbg_w_coarse && !cfg->dbg_n_live,
+                 "nerf_render_poses: debug outputs are per render; use nerf_render");
+    if (n_poses == 0) return NERF_OK;
+    NERF_REQUIRE(poses && rgb && depth && acc, "nerf_render_poses: NULL poses or output");
+    const int64_t R = (int64_t)K->W * K->H;
+    const size_t need = (size_t)32 * R;  // rays_o, rays_d, t_near, t_far of one frame
+    char* ws = static_cast<char*>(workspace);
+    void* own = nullptr;
+    if (ws) {
+        if (workspace_bytes < need)
+            return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render_poses: workspace has %zu bytes, needs %zu",
+                             workspace_bytes, need);
+        NERF_REQUIRE(aligned16(ws), "nerf_render_poses: workspace must be 16-byte aligned");
+    } else {
+        clear_pending();
+        const hipError_t e = hipMallocAsync(&own, need, as_stream(stream));
+        if (e != hipSuccess)
+            return nerf_fail(NERF_ERR_WORKSPACE, "nerf_render_poses: cannot allocate %zu workspace bytes: %s", need,
+                             hipGetErrorString(e));
+        ws = static_cast<char*>(own);
+    }
+    float* ro = reinterpret_cast<float*>(ws);
+    float* rd = ro + 3 * R;
+    float* tn = rd + 3 * R;
+    float* tf = tn + R;
+    clear_pending();
+    launch_fill_f32(tn, R, t_near, as_stream(stream));
+    launch_fill_f32(tf, R, t_far, as_stream(stream));
+    nerf_status st = check_launch("nerf_render_poses");
+    for (int f = 0; f < n_poses && st == NERF_OK; ++f) {
+        launch_gen_rays(poses + 12 * (int64_t)f, K->W, K->H, K->fx, K->fy, K->cx, K->cy, ro, rd, as_stream(stream));
+        st = check_launch("nerf_render_poses");
+        if (st != NERF_OK) break;
+        nerf_render_cfg c = *cfg;
+        c.ray_offset = cfg->ray_offset + (uint64_t)f * (uint64_t)R;
+        st = nerf::render_entry(ro, rd, tn, tf, R, w, &c, rgb + 3 * R * f, depth + R * f, acc + R * f, stream,
+                                nullptr, 0);
+    }
+    if (own) {
+        const hipError_t e = hipFreeAsync(own, as_stream(stream));
+        if (st == NERF_OK && e != hipSuccess)
+            return nerf_fail(NERF_ERR_HIP, "nerf_render_poses: workspace free: %s", hipGetErrorString(e));
+    }
+    return st;
+}
+
 }  // extern "C"
 
 namespace nerf {
@@ -310,8 +367,9 @@ nerf_status render_entry(const float* rays_o, const float* rays_d, const float* 
             NERF_REQUIRE(cfg->n_fine == 0, "nerf_render: hash mode has no resampling pass");
             const nerf_status gs = check_grid(w->grid, "nerf_render");
             if (gs != NERF_OK) return gs;
-            if (w->grid->n_levels != 16)
-                return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_render: the field network takes 16 levels x 2 features");
+            if (w->grid->n_levels != 16 || w->grid->dim != 3)
+                return nerf_fail(NERF_ERR_UNSUPPORTED,
+                                 "nerf_render: the field network takes a 3D grid of 16 levels x 2 features");
             NERF_REQUIRE(cfg->box_hi > cfg->box_lo, "nerf_render: empty scene box");
             ga = grid_args(w->grid);
             break;

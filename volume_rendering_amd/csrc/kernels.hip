@@ -41,6 +41,15 @@ void launch_gen_rays(const float* pose, int W, int H, float fx, float fy, float 
                        rd);
 }
 
+__global__ void __launch_bounds__(256) k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+}
+
 // ===========================================================================
 // Stratified samples: one thread per (ray, sample).
 // ===========================================================================
@@ -228,6 +237,7 @@ __device__ __forceinline__ void store_levels(float* out, int64_t p, int L, int l
     }
 }
 
+template <int DIM>
 __global__ void __launch_bounds__(1024) k_encode_hash_lds(const float* __restrict__ x, int64_t n, GridArgs g,
                                                           int n_staged, float* __restrict__ out,
                                                           uint32_t* __restrict__ idx_dbg) {
@@ -243,15 +253,21 @@ __global__ void __launch_bounds__(1024) k_encode_hash_lds(const float* __restric
     const int64_t p0 = (int64_t)blockIdx.x * kHashLdsTile;
     const int64_t p1 = p0 + kHashLdsTile < n ? p0 + kHashLdsTile : n;
     const int L = g.n_levels;
+    constexpr int NC = 1 << DIM;
     for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-        const float ux = x[3 * p], uy = x[3 * p + 1], uz = x[3 * p + 2];
+        float u[DIM];
+#pragma unroll
+        for (int a = 0; a < DIM; ++a) u[a] = x[DIM * p + a];
         uint32_t lo = 0;
         for (int l = 0; l < n_staged; l += 2) {
             const int nl = l + 1 < n_staged ? 2 : 1;
             float f[4] = {0.f, 0.f, 0.f, 0.f};
             for (int j = 0; j < nl; ++j) {
-                grid_level_tab(tab, lo, g.res[l + j], true, g.tmask, ux, uy, uz, f[2 * j], f[2 * j + 1],
-                               idx_dbg ? idx_dbg + 8 * (p * L + l + j) : nullptr);
+                if (g.mask[l + j] != 0.0f) {
+                    GridLookup<DIM> q;
+                    q.issue(tab, lo, g.res[l + j], true, g.tmask, u);
+                    q.finish(g.mask[l + j], f[2 * j], f[2 * j + 1], idx_dbg ? idx_dbg + NC * (p * L + l + j) : nullptr);
+                }
                 lo += g.size[l + j];
             }
             store_levels(out, p, L, l, nl, f);
@@ -259,6 +275,7 @@ __global__ void __launch_bounds__(1024) k_encode_hash_lds(const float* __restric
     }
 }
 
+template <int DIM>
 __global__ void __launch_bounds__(256) k_encode_hash(const float* __restrict__ x, int64_t n, GridArgs g, int l_first,
                                                      int tiles, float* __restrict__ out,
                                                      uint32_t* __restrict__ idx_dbg) {
@@ -266,26 +283,30 @@ __global__ void __launch_bounds__(256) k_encode_hash(const float* __restrict__ x
     const int nl = g.n_levels - l < kHashLpi ? g.n_levels - l : kHashLpi;
     const int64_t p0 = (int64_t)(blockIdx.x % tiles) * (256 * kHashPts);
     const int L = g.n_levels;
+    constexpr int NC = 1 << DIM;
     const GridTabGlobal tab(g);
-    // every lookup of the thread (points past the end repeat the last point,
-    // a missing second level repeats the first) is issued before any finishes
     // (the points are read first: a later read would wait for every lookup)
-    float u[kHashPts][3];
+    float u[kHashPts][DIM];
 #pragma unroll
     for (int j = 0; j < kHashPts; ++j) {
         int64_t p = p0 + j * 256 + threadIdx.x;
         p = p < n ? p : n - 1;
 #pragma unroll
-        for (int a = 0; a < 3; ++a) u[j][a] = x[3 * p + a];
+        for (int a = 0; a < DIM; ++a) u[j][a] = x[DIM * p + a];
     }
-    GridLookup q[kHashPts][kHashLpi];
+    // every lookup of the thread (points past the end repeat the last point,
+    // a missing second level repeats the first) is issued before any finishes;
+    // a level with mask 0 is skipped (the mask is uniform over the workgroup)
+    bool look[kHashLpi];
+#pragma unroll
+    for (int k = 0; k < kHashLpi; ++k) look[k] = k < nl && g.mask[l + k] != 0.0f;
+    GridLookup<DIM> q[kHashPts][kHashLpi];
 #pragma unroll
     for (int j = 0; j < kHashPts; ++j)
 #pragma unroll
         for (int k = 0; k < kHashLpi; ++k) {
             const int lk = k < nl ? l + k : l;
-            q[j][k].issue(tab, (uint32_t)g.offset[lk], g.res[lk], g.direct[lk] != 0, g.tmask, u[j][0], u[j][1],
-                          u[j][2]);
+            if (look[k]) q[j][k].issue(tab, (uint32_t)g.offset[lk], g.res[lk], g.direct[lk] != 0, g.tmask, u[j]);
         }
 #pragma unroll
     for (int j = 0; j < kHashPts; ++j) {
@@ -294,13 +315,17 @@ __global__ void __launch_bounds__(256) k_encode_hash(const float* __restrict__ x
             float f[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < kHashLpi; ++k)
-                if (k < nl) q[j][k].finish(f[2 * k], f[2 * k + 1], idx_dbg ? idx_dbg + 8 * (p * L + l + k) : nullptr);
+                if (look[k])
+                    q[j][k].finish(g.mask[l + k], f[2 * k], f[2 * k + 1],
+                                   idx_dbg ? idx_dbg + NC * (p * L + l + k) : nullptr);
             store_levels(out, p, L, l, kHashLpi < 2 ? 1 : nl, f);
         }
     }
 }
 
-void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out, uint32_t* idx, hipStream_t s) {
+template <int DIM>
+static void launch_encode_hash_t(const float* x, int64_t n, const GridArgs& g, float* out, uint32_t* idx,
+                                 hipStream_t s) {
     // levels are in increasing resolution: the staged ones are a prefix of
     // direct levels whose tables fit LDS together
     int n_staged = 0;
@@ -312,14 +337,21 @@ void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out
     }
     lds_bytes = (lds_bytes + 7) / 8 * 8;  // whole 8-byte words
     if (n_staged > 0)
-        hipLaunchKernelGGL(k_encode_hash_lds, dim3((unsigned)((n + kHashLdsTile - 1) / kHashLdsTile)), dim3(1024),
-                           lds_bytes, s, x, n, g, n_staged, out, idx);
+        hipLaunchKernelGGL(k_encode_hash_lds<DIM>, dim3((unsigned)((n + kHashLdsTile - 1) / kHashLdsTile)),
+                           dim3(1024), lds_bytes, s, x, n, g, n_staged, out, idx);
     if (n_staged < g.n_levels) {
         const int tiles = (int)((n + 256 * kHashPts - 1) / (256 * kHashPts));
         const int items = (g.n_levels - n_staged + kHashLpi - 1) / kHashLpi;
-        hipLaunchKernelGGL(k_encode_hash, dim3((unsigned)((int64_t)tiles * items)), dim3(256), 0, s, x, n, g,
+        hipLaunchKernelGGL(k_encode_hash<DIM>, dim3((unsigned)((int64_t)tiles * items)), dim3(256), 0, s, x, n, g,
                            n_staged, tiles, out, idx);
     }
+}
+
+void launch_encode_hash(const float* x, int64_t n, const GridArgs& g, float* out, uint32_t* idx, hipStream_t s) {
+    if (g.dim == 2)
+        launch_encode_hash_t<2>(x, n, g, out, idx, s);
+    else
+        launch_encode_hash_t<3>(x, n, g, out, idx, s);
 }
 
 // ===========================================================================

@@ -10,6 +10,8 @@ namespace nerf {
 
 struct GridArgs {
     int n_levels;
+    int dim;         // 2 or 3
+    float mask[16];  // per-level multiplier; 0: level not looked up
     uint32_t tmask;  // T - 1 (T a power of two)
     int res[16];
     int direct[16];
@@ -75,6 +77,7 @@ void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int ad
 
 void launch_gen_rays(const float* pose, int W, int H, float fx, float fy, float cx, float cy, float* ro, float* rd,
                      hipStream_t s);
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 void launch_stratified(const float* tn, const float* tf, int64_t n_rays, int n, uint64_t seed, uint64_t ray_offset,
                        int jitter, float* z, hipStream_t s);
 void launch_encode_freq(const float* x, int64_t n, int d, int L, int inc, int use_pi, int bf16, void* out,

@@ -28,8 +28,9 @@ bool supported_kind(int kind) {
 
 extern "C" {
 
-nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int n_levels, uint32_t table_size, int n_min, int n_max) {
+nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int dim, int n_levels, uint32_t table_size, int n_min, int n_max) {
     if (!g) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_hashgrid_init: g is NULL");
+    if (dim != 2 && dim != 3) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_hashgrid_init: dim %d", dim);
     if (n_levels < 2 || n_levels > NERF_HASH_MAX_LEVELS)
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_hashgrid_init: n_levels %d outside 2..16", n_levels);
     if (table_size == 0 || (table_size & (table_size - 1)))
@@ -38,6 +39,8 @@ nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int n_levels, uint32_t table_si
     if (n_min < 1 || n_max < n_min)
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "nerf_hashgrid_init: bad resolutions %d..%d", n_min, n_max);
     std::memset(g, 0, sizeof(*g));
+    g->dim = dim;
+    for (int l = 0; l < NERF_HASH_MAX_LEVELS; ++l) g->level_mask[l] = 1.0f;
     g->n_levels = n_levels;
     g->n_feat = 2;
     g->table_size = table_size;
@@ -46,7 +49,7 @@ nerf_status nerf_hashgrid_init(nerf_hashgrid* g, int n_levels, uint32_t table_si
     uint64_t off = 0;
     for (int l = 0; l < n_levels; ++l) {
         const int N = (int)std::nearbyint((double)n_min * std::pow(b, (double)l));
-        const uint64_t verts = (uint64_t)(N + 1) * (uint64_t)(N + 1) * (uint64_t)(N + 1);
+        const uint64_t verts = (uint64_t)(N + 1) * (uint64_t)(N + 1) * (dim == 3 ? (uint64_t)(N + 1) : 1u);
         g->res[l] = N;
         g->direct[l] = verts <= table_size ? 1 : 0;
         g->size[l] = (uint32_t)(verts <= table_size ? verts : table_size);

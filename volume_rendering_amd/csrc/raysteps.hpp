@@ -249,11 +249,15 @@ __device__ __forceinline__ void sh16_eval(float x, float y, float z, float (&o)[
 
 // ---------------------------------------------------------------------------
 // Multiresolution hash grid ("Instant-NGP - Visual Experiments", shared
-// toolkit, extended to 3D).
+// toolkit, 2D as printed and extended to 3D).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t grid_index(int ix, int iy, int iz, int N, bool direct, uint32_t tmask) {
     if (direct) return (uint32_t)((ix * (N + 1) + iy) * (N + 1) + iz);
     return ((uint32_t)ix ^ ((uint32_t)iy * 2654435761u) ^ ((uint32_t)iz * 805459861u)) & tmask;
+}
+__device__ __forceinline__ uint32_t grid_index(int ix, int iy, int N, bool direct, uint32_t tmask) {
+    if (direct) return (uint32_t)(ix * (N + 1) + iy);
+    return ((uint32_t)ix ^ ((uint32_t)iy * 2654435761u)) & tmask;
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -285,94 +289,124 @@ struct GridTabLds {
 __device__ __forceinline__ float half_lo(uint32_t e) { return __half2float(__ushort_as_half((unsigned short)(e & 0xFFFFu))); }
 __device__ __forceinline__ float half_hi(uint32_t e) { return __half2float(__ushort_as_half((unsigned short)(e >> 16))); }
 
-// One level lookup (resolution N, direct or hashed, entries from absolute
-// entry `off` of `tab`) at a unit-cube point, in two phases so that the
-// loads of several lookups can be in flight together: issue() computes the
-// corner entries and starts their loads, finish() interpolates.
+// One level lookup in DIM dimensions (resolution N, direct or hashed,
+// entries from absolute entry `off` of `tab`) at a unit-cube point, in two
+// phases so that the loads of several lookups can be in flight together:
+// issue() computes the corner entries and starts their loads, finish()
+// interpolates.
 //
-// The 8 corners are taken in 4 pairs along the axis whose neighbours are
-// often adjacent entries: z on direct levels (entries idx, idx + 1), x on
-// hashed levels (for even ix the entries idx and idx ^ 1).  The aligned
-// 8-byte word holding a pair's first entry is always read; the second entry
-// is read separately only when it lies in another word.
+// The 2^DIM corners are taken in pairs along the axis whose neighbours are
+// often adjacent entries: the last axis on direct levels (entries idx,
+// idx + 1), x on hashed levels (for even ix the entries idx and idx ^ 1).
+// The aligned 8-byte word holding a pair's first entry is always read; the
+// second entry is read separately only when it lies in another word.
+template <int DIM>
 struct GridLookup {
-    u32x2 W[4];
-    uint32_t B[4], A0[4], A1[4];
-    bool P[4];
-    float wx, wy, wz;
+    static_assert(DIM == 2 || DIM == 3, "2D or 3D grids");
+    static constexpr int NP = 1 << (DIM - 1);  // corner pairs
+    u32x2 W[NP];
+    uint32_t B[NP], A0[NP], A1[NP];
+    bool P[NP];
+    float w[DIM];
     uint32_t off;
     bool direct;
 
+    // Corner offsets of pair q: the pair axis takes 0 and 1, the bits of q
+    // (most significant first) the other axes.
+    __device__ static __forceinline__ void deltas(int q, bool direct, int (&d0)[DIM], int (&d1)[DIM]) {
+        const int ax = direct ? DIM - 1 : 0;
+        int bit = DIM - 2;
+#pragma unroll
+        for (int a = 0; a < DIM; ++a) {
+            const bool pa = a == ax;
+            const int v = pa ? 0 : (q >> bit) & 1;
+            d0[a] = v;
+            d1[a] = pa ? 1 : v;
+            bit -= pa ? 0 : 1;
+        }
+    }
+
+    __device__ static __forceinline__ uint32_t index(const int (&i)[DIM], int N, bool direct, uint32_t tmask) {
+        if constexpr (DIM == 3)
+            return grid_index(i[0], i[1], i[2], N, direct, tmask);
+        else
+            return grid_index(i[0], i[1], N, direct, tmask);
+    }
+
     template <class Tab>
-    __device__ __forceinline__ void issue(const Tab& tab, uint32_t off_, int N, bool direct_, uint32_t tmask, float ux,
-                                          float uy, float uz) {
+    __device__ __forceinline__ void issue(const Tab& tab, uint32_t off_, int N, bool direct_, uint32_t tmask,
+                                          const float (&u)[DIM]) {
         off = off_;
         direct = direct_;
-        const float cx = __fmul_rn(ux, (float)N), cy = __fmul_rn(uy, (float)N), cz = __fmul_rn(uz, (float)N);
-        const float fx = floorf(cx), fy = floorf(cy), fz = floorf(cz);
-        wx = cx - fx;
-        wy = cy - fy;
-        wz = cz - fz;
-        const int x0 = (int)fx, y0 = (int)fy, z0 = (int)fz;
+        int c0[DIM];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int qa = q >> 1, qb = q & 1;
-            const int dx0 = direct ? qa : 0, dx1 = direct ? qa : 1;
-            const int dy0 = direct ? qb : qa;
-            const int dz0 = direct ? 0 : qb, dz1 = direct ? 1 : qb;
-            const int iy = min(max(y0 + dy0, 0), N);
-            const int ixa = min(max(x0 + dx0, 0), N), ixb = min(max(x0 + dx1, 0), N);
-            const int iza = min(max(z0 + dz0, 0), N), izb = min(max(z0 + dz1, 0), N);
-            A0[q] = off + grid_index(ixa, iy, iza, N, direct, tmask);
-            A1[q] = off + grid_index(ixb, iy, izb, N, direct, tmask);
+        for (int a = 0; a < DIM; ++a) {
+            const float c = __fmul_rn(u[a], (float)N);
+            const float f = floorf(c);
+            w[a] = c - f;
+            c0[a] = (int)f;
+        }
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            int d0[DIM], d1[DIM], ia[DIM], ib[DIM];
+            deltas(q, direct, d0, d1);
+#pragma unroll
+            for (int a = 0; a < DIM; ++a) {
+                ia[a] = min(max(c0[a] + d0[a], 0), N);
+                ib[a] = min(max(c0[a] + d1[a], 0), N);
+            }
+            A0[q] = off + index(ia, N, direct, tmask);
+            A1[q] = off + index(ib, N, direct, tmask);
             P[q] = (A0[q] >> 1) == (A1[q] >> 1);
             W[q] = tab.word(A0[q] & ~1u);
             B[q] = tab.entry_unless(A1[q], P[q]);
         }
     }
 
-    // Features (f0, f1); corner indices optionally to idx_out[0..8)
-    // (lexicographic, x most significant).
-    __device__ __forceinline__ void finish(float& f0, float& f1, uint32_t* idx_out) const {
+    // Features (f0, f1) times `scale`; corner indices optionally to
+    // idx_out[0..2^DIM) (lexicographic, x most significant).
+    __device__ __forceinline__ void finish(float scale, float& f0, float& f1, uint32_t* idx_out) const {
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int qa = q >> 1, qb = q & 1;
-            const int dx0 = direct ? qa : 0, dx1 = direct ? qa : 1;
-            const int dy0 = direct ? qb : qa;
-            const int dz0 = direct ? 0 : qb, dz1 = direct ? 1 : qb;
+        for (int q = 0; q < NP; ++q) {
+            int d0[DIM], d1[DIM];
+            deltas(q, direct, d0, d1);
+            float wt0 = 1.0f, wt1 = 1.0f;
+            int k0 = 0, k1 = 0;
+#pragma unroll
+            for (int a = 0; a < DIM; ++a) {
+                wt0 *= d0[a] ? w[a] : 1.0f - w[a];
+                wt1 *= d1[a] ? w[a] : 1.0f - w[a];
+                k0 = 2 * k0 + d0[a];
+                k1 = 2 * k1 + d1[a];
+            }
             if (idx_out) {
-                idx_out[4 * dx0 + 2 * dy0 + dz0] = A0[q] - off;
-                idx_out[4 * dx1 + 2 * dy0 + dz1] = A1[q] - off;
+                idx_out[k0] = A0[q] - off;
+                idx_out[k1] = A1[q] - off;
             }
             const uint32_t e0 = (A0[q] & 1u) ? W[q].y : W[q].x;
             const uint32_t e1 = P[q] ? ((A1[q] & 1u) ? W[q].y : W[q].x) : B[q];
-            const float wt0 = (dx0 ? wx : 1.0f - wx) * (dy0 ? wy : 1.0f - wy) * (dz0 ? wz : 1.0f - wz);
-            const float wt1 = (dx1 ? wx : 1.0f - wx) * (dy0 ? wy : 1.0f - wy) * (dz1 ? wz : 1.0f - wz);
             a0 += wt0 * half_lo(e0);
             a1 += wt0 * half_hi(e0);
             a0 += wt1 * half_lo(e1);
             a1 += wt1 * half_hi(e1);
         }
-        f0 = a0;
-        f1 = a1;
+        f0 = scale * a0;
+        f1 = scale * a1;
     }
 };
 
-template <class Tab>
-__device__ __forceinline__ void grid_level_tab(const Tab& tab, uint32_t off, int N, bool direct, uint32_t tmask,
-                                               float ux, float uy, float uz, float& f0, float& f1,
-                                               uint32_t* idx_out) {
-    GridLookup q;
-    q.issue(tab, off, N, direct, tmask, ux, uy, uz);
-    q.finish(f0, f1, idx_out);
-}
-
-// Level l of grid g, tables in global memory.
+// Level l of the 3D grid g (tables in global memory), times the level's
+// mask.  Used where the level differs between lanes (the fused render), so
+// a level is looked up even when its mask is 0: skipping it there would
+// split the wave.
 __device__ __forceinline__ void grid_level(const GridArgs& g, int l, float ux, float uy, float uz, float& f0, float& f1,
                                            uint32_t* idx_out) {
     const GridTabGlobal tab(g);
-    grid_level_tab(tab, (uint32_t)g.offset[l], g.res[l], g.direct[l] != 0, g.tmask, ux, uy, uz, f0, f1, idx_out);
+    const float u[3] = {ux, uy, uz};
+    GridLookup<3> q;
+    q.issue(tab, (uint32_t)g.offset[l], g.res[l], g.direct[l] != 0, g.tmask, u);
+    q.finish(g.mask[l], f0, f1, idx_out);
 }
 
 }  // namespace nerf
