@@ -76,6 +76,9 @@ def measured_traffic(workload, dtype):
 WORKLOADS = {
     # name: (poses, hemisphere, H, W, focal, n_coarse, n_fine, net kind, chunk)
     "hierarchical": dict(poses=4, hemi=True, H=800, W=800, focal=1110.0, nc=64, nf=128, kind=1, chunk=0),
+    # the same with empty-space skipping (128^3 occupancy at 10%) and termination at T < 1e-2
+    "hierarchical_occ": dict(poses=4, hemi=True, H=800, W=800, focal=1110.0, nc=64, nf=128, kind=1, chunk=0,
+                             occ=True),
     "coarse": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=1, chunk=65536),
     "tiny": dict(poses=1, hemi=False, H=32, W=32, focal=40.0, nc=16, nf=0, kind=2, chunk=0),
     "hash": dict(poses=1, hemi=True, H=256, W=256, focal=355.2, nc=128, nf=0, kind=4, chunk=0),
@@ -105,7 +108,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s):
+def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s, occ=None):
     """The oracle (float64 definition) timed on a bounded sample of rays."""
     from oracle import render as oren
     try:
@@ -128,8 +131,9 @@ def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s):
             grid, tabs, field = coarse
             oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0)
         else:
+            extra = dict(occ=occ, term_T=1e-2) if occ is not None else {}
             oren.render_nerf(rays_o[sel], rays_d[sel], near[sel], far[sel], coarse, fine if wl["nf"] else None,
-                             wl["nc"], wl["nf"], Lp, 4, seed=0)
+                             wl["nc"], wl["nf"], Lp, 4, seed=0, ray_offset=sel, **extra)
         return time.perf_counter() - t
 
     n = 8
@@ -209,8 +213,16 @@ def main():
         fine_p = si.nerf_params(shape, seed=0, net_id=1)
         nets = [v.weights.pack_to_device(kind, dtype, coarse_p), v.weights.pack_to_device(kind, dtype, fine_p)]
         mode = B.NERF_MODE_NERF
+    skipping = kind == 3 or wl.get("occ", False)
     cfg = B.nerf_render_cfg(mode=mode, n_coarse=wl["nc"], n_fine=wl["nf"], use_pi=1, jitter=1, seed=0,
-                            chunk=wl["chunk"], box_lo=-1.5, box_hi=1.5, term_T=1e-2, occ_res=128, cell_res=16)
+                            chunk=wl["chunk"], box_lo=-1.5, box_hi=1.5, term_T=1e-2 if skipping else 0.0,
+                            occ_res=128, cell_res=16)
+    occ_keep = None
+    if wl.get("occ", False):
+        occ_bits = si.occupancy_bits(128, 0.1, seed=0)
+        occ_keep = (torch.from_numpy(occ_bits.view(np.int32)).to(dev), torch.zeros(1, dtype=torch.int64, device=dev))
+        cfg.occ = occ_keep[0].data_ptr()
+        cfg.dbg_n_live = occ_keep[1].data_ptr()
     if kilo_keep is not None:
         w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), cells=kilo_keep[0].data_ptr(), n_cells=4096)
         cfg.occ = kilo_keep[1].data_ptr()
@@ -249,6 +261,8 @@ def main():
 
     if kind == 3:
         n_mlp_samples = int(kilo_keep[2].item())  # live samples the cell networks evaluated
+    elif occ_keep is not None:
+        n_mlp_samples = int(occ_keep[1].item())  # live samples (inside the box, occupied), both passes
     else:
         n_mlp_samples = R * (wl["nc"] + (wl["nc"] + wl["nf"] if wl["nf"] else 0))
     macs = {1: MACS_8x256, 2: MACS_4x64, 3: MACS_CELL_2x32, 4: MACS_HASH_FIELD}[kind]
@@ -272,7 +286,8 @@ def main():
         "config": {"workload": args.workload, "rays": R, "poses": wl["poses"], "H": H, "W": W, "focal": f,
                    "n_coarse": wl["nc"], "n_fine": wl["nf"],
                    "net": {1: "8x256", 2: "4x64", 3: "4096 cells 2x32", 4: "hash-field"}[kind],
-                   "chunk": wl["chunk"]},
+                   "chunk": wl["chunk"],
+                   **({"occupancy": "128^3 at 10%", "term_T": 1e-2} if occ_keep is not None else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload, dt_name),
                      "kernel": {1: "k_render_nerf", 2: "k_render_nerf", 3: "kilo pipeline", 4: "k_render_hash"}[kind],
@@ -288,7 +303,8 @@ def main():
             og = oenc.hashgrid_3d()
             base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, (og, tabs, coarse_p), None, args.cpu_seconds)
         else:
-            base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, coarse_p, fine_p, args.cpu_seconds)
+            occ_d = si.occupancy_dense(si.occupancy_bits(128, 0.1, seed=0)) if occ_keep is not None else None
+            base = cpu_baseline(wl, kind, o_h, d_h, nf_h, ff_h, coarse_p, fine_p, args.cpu_seconds, occ_d)
         out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
 

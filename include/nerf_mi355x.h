@@ -141,18 +141,22 @@ typedef struct {
     uint64_t seed;         /* Philox key for jitter and inverse-CDF uniforms */
     uint64_t ray_offset;   /* global index of ray 0: the counter of ray r is ray_offset + r */
     int64_t chunk;         /* rays per launch (0: all); results do not depend on it */
-    float term_T;          /* KILO: drop sample i and later once T_i < term_T (0: never) */
-    float box_lo, box_hi;  /* HASH/KILO: scene box [lo,hi]^3 (HASH maps it to [0,1]^3) */
-    int32_t occ_res;       /* KILO: occupancy grid resolution per axis (128) */
+    float term_T;          /* drop sample i and later once T_i < term_T (0: never); NERF/HASH
+                              also stop evaluating a ray's samples there */
+    float box_lo, box_hi;  /* scene box [lo,hi]^3 of the occupancy grid (HASH also maps it to [0,1]^3) */
+    int32_t occ_res;       /* occupancy grid resolution per axis (128) */
     int32_t cell_res;      /* KILO: cells per axis (16) */
-    const uint32_t* occ;   /* KILO: device bitset, bit v%32 of word v/32 for voxel
-                              v = (vx*res + vy)*res + vz */
+    const uint32_t* occ;   /* device bitset, bit v%32 of word v/32 for voxel
+                              v = (vx*res + vy)*res + vz, vx = clamp(floor((x-lo)*res/(hi-lo)));
+                              a sample outside the box or in an empty voxel has density 0 and is
+                              not evaluated.  Required in KILO mode; NULL in NERF/HASH: no skipping */
     void* workspace;       /* device scratch (KILO); NULL: the call allocates
                               it stream-ordered and frees it after the work */
     size_t workspace_bytes;
     float* dbg_z;          /* optional device [n_rays, n_coarse + n_fine]: samples of the last pass */
     float* dbg_w_coarse;   /* optional device [n_rays, n_coarse]: first-pass weights */
-    int64_t* dbg_n_live;   /* optional device int64[1], KILO: samples evaluated by a cell network */
+    int64_t* dbg_n_live;   /* optional device int64[1]: live samples (inside the box and
+                              occupied; every sample without a grid), over both passes */
 } nerf_render_cfg;
 
 /* ---------------------------------------------------------------------- */
@@ -303,6 +307,11 @@ nerf_status nerf_sample_pdf(const float* z_coarse, const float* w_coarse, int64_
  *        fine network on the merged samples -> compositing.
  *  HASH: stratified samples -> world box to unit cube -> hash-grid features,
  *        harmonics of the view direction -> field network -> compositing.
+ *  NERF and HASH skip empty space when cfg.occ is set (Section 1 Theory,
+ *  4.2: uniform samples waste compute on empty space): only live samples
+ *  are evaluated, the others have density 0; with term_T > 0 a ray stops
+ *  evaluating once its transmittance is below term_T, and compositing drops
+ *  sample i and later once T_i < term_T.
  *  KILO: stratified samples -> occupancy and box test -> cell id -> cell
  *        network for occupied samples (density 0 elsewhere) -> compositing
  *        that stops at the first sample with T < term_T.

@@ -28,49 +28,74 @@ def _encode_points(x, L_pos, use_pi):
     return encoding.freq_encode(x.reshape(-1, 3), L_pos, True, use_pi)
 
 
-def nerf_pass(params, rays_o, rays_d, z, L_pos=10, L_dir=4, mode="f64", use_pi=True, white_bkgd=False):
+def occupied(x, occ, occ_res=128, box=(-1.5, 1.5)):
+    """Empty-space test of sample points (the same voxel arithmetic as the
+    many-network render): inside the closed box and in an occupied voxel.
+    ``occ`` None: every sample is live.  Returns bool [...]."""
+    if occ is None:
+        return np.ones(np.asarray(x).shape[:-1], dtype=bool)
+    live, _, _ = kilo_classify(x, occ, occ_res, 1, box)
+    return live
+
+
+def nerf_pass(params, rays_o, rays_d, z, L_pos=10, L_dir=4, mode="f64", use_pi=True, white_bkgd=False, occ=None,
+              occ_res=128, box=(-1.5, 1.5), term_T=0.0):
     """One network pass over given samples ``z`` [R, N] (float32): points,
-    encodings, network, compositing.  Returns dict(raw, rgb, depth, acc, w)."""
+    encodings, network, compositing.  With an occupancy grid ``occ``, samples
+    outside the box or in empty voxels have density 0 (empty-space skipping:
+    "Spatial Intelligence - Part 1: NeRF", Section 1 Theory, 4.2, uniform
+    samples waste compute on empty space); ``term_T`` > 0 drops sample i and
+    later once T_i < term_T.  Returns dict(raw, rgb, depth, acc, w, n_live)."""
     z = np.asarray(z, dtype=np.float32)
     R, N = z.shape
     x = sampling.points(rays_o, rays_d, z)
+    live = occupied(x, occ, occ_res, box)
     pe = _encode_points(x, L_pos, use_pi)
     de = encoding.freq_encode(sampling.view_dirs(rays_d), L_dir, True, use_pi)
     de = np.repeat(de, N, axis=0)
     raw = mlp.nerf_forward(params, pe, de, mode).reshape(R, N, 4)
-    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd)
-    return dict(raw=raw, rgb=rgb, depth=depth, acc=acc, w=w)
+    raw[~live] = 0.0
+    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd, term_T)
+    return dict(raw=raw, rgb=rgb, depth=depth, acc=acc, w=w, n_live=int(live.sum()))
 
 
 def render_nerf(rays_o, rays_d, t_near, t_far, coarse, fine=None, n_coarse=64, n_fine=128, L_pos=10, L_dir=4,
-                seed=0, jitter=True, mode="f64", use_pi=True, white_bkgd=False, ray_offset=0):
+                seed=0, jitter=True, mode="f64", use_pi=True, white_bkgd=False, ray_offset=0, occ=None, occ_res=128,
+                box=(-1.5, 1.5), term_T=0.0):
     """Coarse pass, then (if ``fine`` is given and n_fine > 0) resampling and
-    the fine pass.  The coarse weights enter the sampler as float32, the
-    precision of the page's tensors."""
+    the fine pass; both passes skip empty space and stop early as
+    ``nerf_pass`` describes.  The coarse weights enter the sampler as float32,
+    the precision of the page's tensors."""
     z_c = sampling.stratified(t_near, t_far, n_coarse, seed, jitter, ray_offset)
-    c = nerf_pass(coarse, rays_o, rays_d, z_c, L_pos, L_dir, mode, use_pi, white_bkgd)
-    out = dict(z_c=z_c, coarse=c, rgb=c["rgb"], depth=c["depth"], acc=c["acc"])
+    c = nerf_pass(coarse, rays_o, rays_d, z_c, L_pos, L_dir, mode, use_pi, white_bkgd, occ, occ_res, box, term_T)
+    out = dict(z_c=z_c, coarse=c, rgb=c["rgb"], depth=c["depth"], acc=c["acc"], n_live=c["n_live"])
     if fine is not None and n_fine > 0:
         w32 = c["w"].astype(np.float32)
         z_f, idx, z2 = sampling.hierarchical_fine_samples(z_c, w32, n_fine, seed, ray_offset)
-        f = nerf_pass(fine, rays_o, rays_d, z2, L_pos, L_dir, mode, use_pi, white_bkgd)
-        out.update(z_f=z_f, bin_idx=idx, z2=z2, fine=f, rgb=f["rgb"], depth=f["depth"], acc=f["acc"])
+        f = nerf_pass(fine, rays_o, rays_d, z2, L_pos, L_dir, mode, use_pi, white_bkgd, occ, occ_res, box, term_T)
+        out.update(z_f=z_f, bin_idx=idx, z2=z2, fine=f, rgb=f["rgb"], depth=f["depth"], acc=f["acc"],
+                   n_live=c["n_live"] + f["n_live"])
     return out
 
 
 def render_hash(rays_o, rays_d, t_near, t_far, grid, tables, field, n_samples=128, seed=0, jitter=True,
-                mode="f64", box=(-1.5, 1.5), white_bkgd=False, ray_offset=0, level_mask=None):
+                mode="f64", box=(-1.5, 1.5), white_bkgd=False, ray_offset=0, level_mask=None, occ=None, occ_res=128,
+                term_T=0.0):
     """Hash-grid field render: stratified samples, world box mapped to the
     unit cube, grid features (times the optional per-level mask), spherical
-    harmonics direction encoding, field network, compositing."""
+    harmonics direction encoding, field network, compositing; empty space and
+    early termination as ``nerf_pass``."""
     z = sampling.stratified(t_near, t_far, n_samples, seed, jitter, ray_offset)
     R, N = z.shape
-    x = sampling.points(rays_o, rays_d, z).reshape(-1, 3)
+    x3 = sampling.points(rays_o, rays_d, z)
+    live = occupied(x3, occ, occ_res, box)
+    x = x3.reshape(-1, 3)
     feats = grid.encode(encoding.world_to_unit(x, *box), tables, level_mask)
     de = np.repeat(encoding.sh16(sampling.view_dirs(rays_d)), N, axis=0)
     raw = mlp.hash_field_forward(field, feats, de, mode).reshape(R, N, 4)
-    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd)
-    return dict(z=z, raw=raw, rgb=rgb, depth=depth, acc=acc, w=w)
+    raw[~live] = 0.0
+    rgb, depth, acc, w = composite.volume_render(raw, z, rays_d, white_bkgd, term_T)
+    return dict(z=z, raw=raw, rgb=rgb, depth=depth, acc=acc, w=w, n_live=int(live.sum()))
 
 
 def kilo_classify(x, occ_dense, occ_res=128, cells=16, box=(-1.5, 1.5)):

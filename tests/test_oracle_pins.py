@@ -722,6 +722,60 @@ def test_render_hash_density_from_a_linear_coarsest_level():
     assert np.allclose(out["raw"][..., 3][inside], expect[inside], atol=1e-6)
 
 
+def test_empty_space_skipping_full_and_empty_occupancy():
+    """Full occupancy with every sample inside the box reproduces the render
+    without skipping; empty occupancy renders nothing (white background: 1)."""
+    R = 24
+    c2w = si.poses(1, seed=3)[0]
+    o, d = rays.get_rays(4, 6, 20.0, 20.0, 3.0, 2.0, c2w)
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    pc, pf = si.nerf_params(si.NERF_4x64, seed=2, net_id=0), si.nerf_params(si.NERF_4x64, seed=2, net_id=1)
+    base = render.render_nerf(o, d, near, far, pc, pf, 16, 32, 6, 4, seed=1)
+    full = render.render_nerf(o, d, near, far, pc, pf, 16, 32, 6, 4, seed=1, occ=np.ones(32 ** 3, bool), occ_res=32,
+                              box=(-10.0, 10.0))
+    for k in ("rgb", "acc", "depth", "z2"):
+        assert np.array_equal(base[k], full[k]), k
+    assert full["n_live"] == R * (16 + 48)
+    empty = render.render_nerf(o, d, near, far, pc, pf, 16, 32, 6, 4, seed=1, occ=np.zeros(32 ** 3, bool),
+                               occ_res=32, white_bkgd=True)
+    assert np.all(empty["acc"] == 0) and np.all(empty["depth"] == 0) and np.all(empty["rgb"] == 1.0)
+    assert empty["n_live"] == 0
+    grid = encoding.hashgrid_3d()
+    tabs = si.hash_tables(grid.sizes, seed=0, scale=1.0)
+    field = si.hash_field_params(seed=0)
+    hb = render.render_hash(o, d, near, far, grid, tabs, field, 24, seed=0)
+    hf = render.render_hash(o, d, near, far, grid, tabs, field, 24, seed=0, occ=np.ones(16 ** 3, bool), occ_res=16,
+                            box=(-1.5, 1.5))
+    inside = np.all(np.abs(sampling.points(o, d, hb["z"])) <= 1.5, axis=-1)
+    assert hf["n_live"] == int(inside.sum())
+    # the hash render's box also maps to the unit cube, so only the dead samples change
+    assert np.array_equal(hf["raw"][inside], hb["raw"][inside]) and np.all(hf["raw"][~inside] == 0)
+
+
+def test_skipped_samples_are_transparent():
+    """A skipped sample has alpha 0: the render equals compositing the
+    network outputs with those samples' densities set to 0 by hand."""
+    R = 16
+    c2w = si.poses(1, seed=4)[0]
+    o, d = rays.get_rays(4, 4, 12.0, 12.0, 2.0, 2.0, c2w)
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    p = si.nerf_params(si.NERF_4x64, seed=3)
+    occ = np.random.default_rng(1).random(8 ** 3) < 0.4
+    out = render.render_nerf(o, d, near, far, p, None, 32, 0, 6, 4, seed=2, occ=occ, occ_res=8, term_T=1e-2)
+    z = out["z_c"]
+    x = sampling.points(o, d, z)
+    ref = render.nerf_pass(p, o, d, z, 6, 4)
+    raw = ref["raw"].copy()
+    t = (x - np.float32(-1.5)) * np.float32(8 / 3.0)
+    v = np.clip(np.floor(t), 0, 7).astype(np.int64)
+    inside = np.all((x >= np.float32(-1.5)) & (x <= np.float32(1.5)), axis=-1)
+    live = inside & occ[(v[..., 0] * 8 + v[..., 1]) * 8 + v[..., 2]]
+    raw[~live] = 0.0
+    rgb, depth, acc, _ = composite.volume_render(raw, z, d, False, 1e-2)
+    assert np.allclose(out["rgb"], rgb, atol=1e-12) and np.allclose(out["acc"], acc, atol=1e-12)
+    assert out["n_live"] == int(live.sum()) and 0 < out["n_live"] < R * 32
+
+
 def test_kilo_reduces_to_single_network_with_full_occupancy():
     R = 64
     c2w = si.poses(1, seed=0)[0]

@@ -345,6 +345,20 @@ nerf_status render_entry(const float* rays_o, const float* rays_d, const float* 
     a.seed = cfg->seed;
     a.box_lo = cfg->box_lo;
     a.box_hi = cfg->box_hi;
+    if (cfg->mode != NERF_MODE_KILO) {
+        // empty-space skipping (occupancy grid over the box) and early termination
+        NERF_REQUIRE(cfg->term_T >= 0.0f, "nerf_render: term_T %g < 0", (double)cfg->term_T);
+        a.term_T = cfg->term_T;
+        a.n_live = cfg->dbg_n_live;
+        if (cfg->occ) {
+            NERF_REQUIRE(cfg->occ_res >= 1 && cfg->occ_res <= 2048, "nerf_render: occ_res %d outside 1..2048",
+                         cfg->occ_res);
+            NERF_REQUIRE(cfg->box_hi > cfg->box_lo, "nerf_render: empty scene box");
+            a.occ = cfg->occ;
+            a.occ_res = cfg->occ_res;
+            a.vscale = (float)((double)cfg->occ_res / ((double)cfg->box_hi - (double)cfg->box_lo));
+        }
+    }
     GridArgs ga{};
     switch (cfg->mode) {
         case NERF_MODE_NERF:
@@ -450,6 +464,8 @@ nerf_status render_entry(const float* rays_o, const float* rays_d, const float* 
         ka.dbg_n_live = cfg->dbg_n_live;
     }
     clear_pending();
+    if (cfg->mode != NERF_MODE_KILO && cfg->dbg_n_live)  // (added to by every ray of every chunk)
+        launch_fill_f32(reinterpret_cast<float*>(cfg->dbg_n_live), 2, 0.0f, as_stream(stream));
     for (int64_t r0 = 0; r0 < n_rays; r0 += chunk) {
         const int64_t nr = (n_rays - r0) < chunk ? (n_rays - r0) : chunk;
         RenderArgs c = a;

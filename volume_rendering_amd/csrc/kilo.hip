@@ -145,11 +145,6 @@ __device__ __forceinline__ float sample_point(const RenderArgs& a, const RayIn& 
     return z;
 }
 
-__device__ __forceinline__ int grid_coord(float t, float scale, int res) {
-    const float f = floorf(__fmul_rn(t, scale));
-    return (int)fminf(fmaxf(f, 0.0f), (float)(res - 1));  // NaN -> 0
-}
-
 // Live = inside the closed box and in an occupied voxel; also the cell id.
 // Coordinates are floor((x - lo) * scale) of rounded float32 operations,
 // clamped to the grid; ids are x-major.

@@ -38,6 +38,12 @@ struct RenderArgs {
     float* acc;
     float* dbg_z;
     float* dbg_w;
+    // empty-space skipping and early termination (NeRF and hash modes)
+    const uint32_t* occ;  // occupancy bitset over the box, or NULL (every sample live)
+    int occ_res;
+    float vscale;         // occ_res / (hi - lo), rounded to float32 once
+    float term_T;         // drop sample i and later once T_i < term_T (0: never)
+    int64_t* n_live;      // optional: live samples evaluated, added
 };
 
 // Many-tiny-networks render: scene box, occupancy grid, cell networks and

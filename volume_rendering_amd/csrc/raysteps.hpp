@@ -224,6 +224,31 @@ __device__ __forceinline__ void merge_samples(const float* zc, int nc, const flo
 }
 
 // ---------------------------------------------------------------------------
+// Voxels of a regular grid over the scene box: floor((x - lo) * scale) of
+// rounded float32 operations, clamped to the grid.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int grid_coord(float t, float scale, int res) {
+    const float f = floorf(__fmul_rn(t, scale));
+    return (int)fminf(fmaxf(f, 0.0f), (float)(res - 1));  // NaN -> 0
+}
+
+// Inside the closed box [lo, hi]^3 and in an occupied voxel of the bitset
+// (bit v%32 of word v/32, v = (vx*res + vy)*res + vz, formed in 64 bits).
+__device__ __forceinline__ bool box_occupied(const uint32_t* occ, int res, float scale, float lo, float hi,
+                                             const float (&x)[3]) {
+    bool inside = true;
+    int v[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        inside = inside && (x[a] >= lo) && (x[a] <= hi);
+        v[a] = grid_coord(__fsub_rn(x[a], lo), scale, res);
+    }
+    const uint64_t r = (uint64_t)res;
+    const uint64_t vox = ((uint64_t)v[0] * r + (uint64_t)v[1]) * r + (uint64_t)v[2];
+    return inside && ((occ[vox >> 5] >> (uint32_t)(vox & 31u)) & 1u);
+}
+
+// ---------------------------------------------------------------------------
 // Real spherical harmonics, degrees 0..3, orthonormal, no Condon-Shortley
 // phase; order: l, then m = -l..l.
 // ---------------------------------------------------------------------------

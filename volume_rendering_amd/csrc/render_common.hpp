@@ -33,9 +33,78 @@ struct RenderLds {
     float z2[kMaxRaySamples];  // merged samples of the second pass
     f32x4 raw[kMaxRaySamples];
     float w[kMaxRaySamples];
-    double cdf[kMaxRaySamples];
+    union {
+        double cdf[kMaxRaySamples];  // resampling (between the passes)
+        int live[kMaxRaySamples];    // live samples of the pass being evaluated
+    };
     float bins[kMaxRaySamples];
 };
+
+// ---------------------------------------------------------------------------
+// Empty-space skipping and early termination ("Spatial Intelligence - Part
+// 1: NeRF", Section 1 Theory, 4.2: uniform samples waste compute on empty
+// space).  A ray's live samples (inside the box, in an occupied voxel) are
+// listed in order and evaluated in dense blocks; a skipped sample has
+// density 0, i.e. alpha 0 and a survival factor 1 - 0 + 1e-10 that rounds
+// to 1 in float32, so leaving it out changes no product.  After each block
+// the transmittance so far is updated, and the ray stops evaluating once it
+// is below term_T (with a 1e-4 relative margin, so every sample the
+// compositor keeps has been evaluated).
+// ---------------------------------------------------------------------------
+
+// Ascending indices of the live samples among zp[0..N) into list; returns
+// their number.
+__device__ __forceinline__ int live_samples(const RenderArgs& a, const float* zp, int N, const float (&o)[3],
+                                            const float (&d)[3], int* list) {
+    const int lane = lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int n = 0;
+    for (int base = 0; base < N; base += kWave) {
+        const int i = base + lane;
+        bool lv = false;
+        if (i < N) {
+            float x[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) x[k] = __fadd_rn(o[k], __fmul_rn(zp[i], d[k]));
+            lv = box_occupied(a.occ, a.occ_res, a.vscale, a.box_lo, a.box_hi, x);
+        }
+        const unsigned long long m = __ballot(lv);
+        if (lv) list[n + __popcll(m & below)] = i;
+        n += __popcll(m);
+    }
+    wave_lds_sync();
+    return n;
+}
+
+// Every wave of the workgroup calls this once per block iteration `it` (the
+// weight ring makes the waves run the same number of network passes); true
+// while any wave still has a block to evaluate.  One workgroup barrier; the
+// flags alternate between two rows so a fast wave's next write cannot meet
+// a slow wave's read.
+__device__ __forceinline__ bool workgroup_busy(bool busy, int it, int wave, int (&flags)[2][4]) {
+    if (lane_id() == 0) flags[it & 1][wave] = busy ? 1 : 0;
+    __syncthreads();
+    const int* f = flags[it & 1];
+    return (f[0] | f[1] | f[2] | f[3]) != 0;
+}
+
+// Product of (1 - alpha + 1e-10) over the evaluated samples j0 .. j0+M-1 of
+// the pass (sample indices from list, or j itself when list is NULL).
+__device__ __forceinline__ float block_survival(const float* zp, const f32x4* raw, const int* list, int j0, int M,
+                                                int n_eval, int N, float dn) {
+    const int lane = lane_id();
+    const int j = j0 + lane;
+    float surv = 1.0f;
+    if (lane < M && j < n_eval) {
+        const int i = list ? list[j] : j;
+        const float delta = (i + 1 < N) ? (zp[i + 1] - zp[i]) * dn : 1e10f * dn;
+        const float alpha = 1.0f - expf(-fmaxf(raw[i][3], 0.0f) * delta);
+        surv = 1.0f - alpha + 1e-10f;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) surv *= __shfl_xor(surv, off, kWave);
+    return surv;
+}
 
 template <class T, int KIND>
 __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
@@ -78,27 +147,53 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
     const int npass = nf > 0 ? 2 : 1;
     constexpr int NBF = BiasRegion<KIND, T::prec>::floats;
     __shared__ __attribute__((aligned(16))) float bias_lds[2][NBF];
+    __shared__ int busy_flags[2][4];
     bias_to_lds<KIND, T::prec>((NERF_AS_LDS float*)bias_lds[0], (const char*)a.coarse, threadIdx.x, blockDim.x);
     if (npass == 2)
         bias_to_lds<KIND, T::prec>((NERF_AS_LDS float*)bias_lds[1], (const char*)a.fine, threadIdx.x, blockDim.x);
     __syncthreads();
+    // skipping or termination: rays evaluate different numbers of blocks
+    const bool dynamic = a.occ != nullptr || a.term_T > 0.0f;
+    int it = 0;
     for (int pass = 0; pass < npass; ++pass) {
         const int N = pass ? nc + nf : nc;
         const char* packed = pass ? (const char*)a.fine : (const char*)a.coarse;
-        for (int blk = 0; blk < N; blk += M) {
+        float* zp = pass ? S.z2 : S.zc;
+        if (pass == 0) {
+            for (int i = lane; i < nc; i += kWave) {
+                const float u = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)i, kStreamJitter) : 0.5f;
+                S.zc[i] = stratified_z(near, far, i, nc, u);
+            }
+            wave_lds_sync();
+        }
+        int n_eval = N;
+        if (a.occ) {
+            n_eval = live_samples(a, zp, N, o, d, S.live);
+            if (a.n_live && live && lane == 0) atomicAdd((unsigned long long*)a.n_live, (unsigned long long)n_eval);
+        }
+        if (dynamic) {
+            for (int i = lane; i < N; i += kWave) S.raw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            wave_lds_sync();
+        }
+        const int nb = (n_eval + M - 1) / M;
+        float T_run = 1.0f;
+        bool stop = false;
+        for (int b = 0;; ++b) {
+            if (dynamic) {
+                if (!workgroup_busy(!stop && b < nb, it++, wave, busy_flags)) break;
+            } else if (b >= nb) {
+                break;
+            }
+            const bool idle = stop || b >= nb;  // an idle wave evaluates sample 0 and stores nothing
             float x[SB][3];
+            int si[SB];
+            bool valid[SB];
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb) {
-                const int s = blk + sb * 32 + (lane & 31);
-                const int sv = s < N ? s : N - 1;
-                float z;
-                if (pass) {
-                    z = S.z2[sv];
-                } else {
-                    const float u = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)sv, kStreamJitter) : 0.5f;
-                    z = stratified_z(near, far, sv, nc, u);
-                    if (h == 0 && s < N) S.zc[s] = z;
-                }
+                const int j = b * M + sb * 32 + (lane & 31);
+                valid[sb] = !idle && j < n_eval;
+                si[sb] = valid[sb] ? (a.occ ? S.live[j] : j) : 0;
+                const float z = zp[si[sb]];
 #pragma unroll
                 for (int k = 0; k < 3; ++k) x[sb][k] = __fadd_rn(o[k], __fmul_rn(z, d[k]));
             }
@@ -114,15 +209,17 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
             }
             if (lane < 32) {
 #pragma unroll
-                for (int sb = 0; sb < SB; ++sb) {
-                    const int s = blk + sb * 32 + lane;
-                    if (s < N) S.raw[s] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
-                }
+                for (int sb = 0; sb < SB; ++sb)
+                    if (valid[sb]) S.raw[si[sb]] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
+            }
+            if (a.term_T > 0.0f && !idle) {
+                wave_lds_sync();
+                T_run *= block_survival(zp, S.raw, a.occ ? S.live : nullptr, b * M, M, n_eval, N, dn);
+                stop = T_run < a.term_T * 0.9999f;
             }
         }
         wave_lds_sync();
-        const float* zp = pass ? S.z2 : S.zc;
-        const CompositeOut c = composite_ray(zp, S.raw, N, dn, pass == 0 ? S.w : nullptr, 0.0f);
+        const CompositeOut c = composite_ray(zp, S.raw, N, dn, pass == 0 ? S.w : nullptr, a.term_T);
         wave_lds_sync();
         if (pass == 0 && a.dbg_w && live)
             for (int i = lane; i < nc; i += kWave) a.dbg_w[r * nc + i] = S.w[i];
@@ -233,18 +330,44 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         sh_operands(shop, sh, lane);
     }
     __shared__ __attribute__((aligned(16))) float bias_lds[BiasRegion<NET_HASH_FIELD, T::prec>::floats];
+    __shared__ int busy_flags[2][4];
     bias_to_lds<NET_HASH_FIELD, T::prec>((NERF_AS_LDS float*)bias_lds, (const char*)a.coarse, threadIdx.x, blockDim.x);
     __syncthreads();
     const int N = a.n_coarse;
-    for (int blk = 0; blk < N; blk += M) {
+    for (int i = lane; i < N; i += kWave) {
+        const float uj = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)i, kStreamJitter) : 0.5f;
+        S.zc[i] = stratified_z(near, far, i, N, uj);
+    }
+    wave_lds_sync();
+    const bool dynamic = a.occ != nullptr || a.term_T > 0.0f;
+    int n_eval = N;
+    if (a.occ) {
+        n_eval = live_samples(a, S.zc, N, o, d, S.live);
+        if (a.n_live && live && lane == 0) atomicAdd((unsigned long long*)a.n_live, (unsigned long long)n_eval);
+    }
+    if (dynamic) {
+        for (int i = lane; i < N; i += kWave) S.raw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wave_lds_sync();
+    }
+    const int nb = (n_eval + M - 1) / M;
+    float T_run = 1.0f;
+    bool stop = false;
+    for (int b = 0;; ++b) {
+        if (dynamic) {
+            if (!workgroup_busy(!stop && b < nb, b, wave, busy_flags)) break;
+        } else if (b >= nb) {
+            break;
+        }
+        const bool idle = stop || b >= nb;
         float u[SB][3];
+        int si[SB];
+        bool valid[SB];
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            const int s = blk + sb * 32 + (lane & 31);
-            const int sv = s < N ? s : N - 1;
-            const float uj = a.jitter ? philox_uniform(a.seed, ray, (uint32_t)sv, kStreamJitter) : 0.5f;
-            const float z = stratified_z(near, far, sv, N, uj);
-            if (h == 0 && s < N) S.zc[s] = z;
+            const int j = b * M + sb * 32 + (lane & 31);
+            valid[sb] = !idle && j < n_eval;
+            si[sb] = valid[sb] ? (a.occ ? S.live[j] : j) : 0;
+            const float z = S.zc[si[sb]];
 #pragma unroll
             for (int k = 0; k < 3; ++k)
                 u[sb][k] = __fdiv_rn(__fsub_rn(__fadd_rn(o[k], __fmul_rn(z, d[k])), lo), span);
@@ -257,14 +380,17 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         hash_field_forward<T>(feats, shop, ws, (const NERF_AS_LDS float*)bias_lds, sig, rgb, lane);
         if (lane < 32) {
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                const int s = blk + sb * 32 + lane;
-                if (s < N) S.raw[s] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
-            }
+            for (int sb = 0; sb < SB; ++sb)
+                if (valid[sb]) S.raw[si[sb]] = f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
+        }
+        if (a.term_T > 0.0f && !idle) {
+            wave_lds_sync();
+            T_run *= block_survival(S.zc, S.raw, a.occ ? S.live : nullptr, b * M, M, n_eval, N, dn);
+            stop = T_run < a.term_T * 0.9999f;
         }
     }
     wave_lds_sync();
-    const CompositeOut c = composite_ray(S.zc, S.raw, N, dn, nullptr, 0.0f);
+    const CompositeOut c = composite_ray(S.zc, S.raw, N, dn, nullptr, a.term_T);
     if (a.dbg_z && live)
         for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = S.zc[i];
     if (lane == 0 && live) {
