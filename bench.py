@@ -100,7 +100,7 @@ def parse():
     ap.add_argument("--workload", default="hierarchical", choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time (all threads)")
     ap.add_argument("--poses", type=int, default=0, help="override the workload's pose count")
     ap.add_argument("--n-fine", type=int, default=-1, help="override the workload's inverse-CDF samples")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -108,14 +108,35 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s, occ=None):
-    """The oracle (float64 definition) timed on a bounded sample of rays."""
-    from oracle import render as oren
+def host_threads():
+    """(BLAS threads the oracle uses, nproc, CPUs in this process's affinity mask)."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    return int(threads), os.cpu_count() or 1, len(os.sched_getaffinity(0))
+
+
+def with_single_thread(measure, record):
+    """Adds the oracle's rate on one thread (BLAS limited to 1) and the host
+    core counts to a cpu_baseline record measured on all threads."""
+    _, nproc, affinity = host_threads()
+    record["nproc"], record["affinity_cpus"] = nproc, affinity
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = measure()
+        record["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+    except Exception as e:  # pragma: no cover
+        record["single_thread"] = {"error": str(e)}
+    return record
+
+
+def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s, occ=None):
+    """The oracle (float64 definition) timed on a bounded sample of rays."""
+    from oracle import render as oren
+    threads = host_threads()[0]
     Lp = 6 if kind == 2 else 10
     if kind == 3:
         target_s = min(target_s, 6.0)
@@ -124,24 +145,29 @@ def cpu_baseline(wl, kind, rays_o, rays_d, near, far, coarse, fine, target_s, oc
         sel = np.linspace(0, rays_o.shape[0] - 1, n).astype(np.int64)
         t = time.perf_counter()
         if kind == 3:
-            cells, occ = coarse
-            oren.render_kilo(rays_o[sel], rays_d[sel], near[sel], far[sel], occ, lambda c: cells[c], wl["nc"], seed=0,
-                             term_T=1e-2)
+            cells, occ_k = coarse
+            oren.render_kilo(rays_o[sel], rays_d[sel], near[sel], far[sel], occ_k, lambda c: cells[c], wl["nc"],
+                             seed=0, term_T=1e-2, ray_offset=sel)
         elif kind == 4:
             grid, tabs, field = coarse
-            oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0)
+            oren.render_hash(rays_o[sel], rays_d[sel], near[sel], far[sel], grid, tabs, field, wl["nc"], seed=0,
+                             ray_offset=sel)
         else:
             extra = dict(occ=occ, term_T=1e-2) if occ is not None else {}
             oren.render_nerf(rays_o[sel], rays_d[sel], near[sel], far[sel], coarse, fine if wl["nf"] else None,
                              wl["nc"], wl["nf"], Lp, 4, seed=0, ray_offset=sel, **extra)
         return time.perf_counter() - t
 
-    n = 8
-    dt = run(n)
-    n2 = int(min(rays_o.shape[0], max(n, n * target_s / max(dt, 1e-3))))
-    dt2 = run(n2)
-    return {"value": n2 / dt2, "unit": "rays/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n2} rays evenly spaced over the workload, float64 oracle, {dt2:.1f} s"}
+    def measure(t_s):
+        n = 8
+        dt = run(n)
+        n2 = int(min(rays_o.shape[0], max(n, n * t_s / max(dt, 1e-3))))
+        dt2 = run(n2)
+        return {"value": n2 / dt2, "unit": "rays/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{n2} rays evenly spaced over the workload, float64 oracle, {dt2:.1f} s"}
+
+    rec = measure(target_s)
+    return with_single_thread(lambda: dict(measure(target_s / 2), cores=1), rec)
 
 
 def main():
@@ -341,23 +367,24 @@ def _timed(args, step, torch):
 
 def _cpu_rate(fn, n_total, target_s, unit, what):
     """Runs the oracle on growing evenly spaced samples until it takes about
-    target_s seconds; returns the cpu_baseline record."""
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    n = 1024
-    while True:
-        sel = np.linspace(0, n_total - 1, min(n, n_total)).astype(np.int64)
-        t = time.perf_counter()
-        fn(sel)
-        dt = time.perf_counter() - t
-        if dt >= 0.3 * target_s or len(sel) == n_total:
-            break
-        n = int(n * min(16.0, max(2.0, target_s / max(dt, 1e-3))))
-    return {"value": len(sel) / dt, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(sel)} {what} evenly spaced over the workload, float64 oracle, {dt:.1f} s"}
+    target_s seconds; returns the cpu_baseline record (all threads, plus one
+    thread)."""
+    threads = host_threads()[0]
+
+    def measure(t_s, cores):
+        n = 1024
+        while True:
+            sel = np.linspace(0, n_total - 1, min(n, n_total)).astype(np.int64)
+            t = time.perf_counter()
+            fn(sel)
+            dt = time.perf_counter() - t
+            if dt >= 0.3 * t_s or len(sel) == n_total:
+                break
+            n = int(n * min(16.0, max(2.0, t_s / max(dt, 1e-3))))
+        return {"value": len(sel) / dt, "unit": unit, "cores": cores, "kind": "oracle",
+                "sample": f"{len(sel)} {what} evenly spaced over the workload, float64 oracle, {dt:.1f} s"}
+
+    return with_single_thread(lambda: measure(target_s / 2, 1), measure(target_s, int(threads)))
 
 
 def standalone(args, wl):
@@ -463,6 +490,8 @@ def standalone(args, wl):
             base = _cpu_rate(lambda sel: ocomp.volume_render(raw_h[sel], z_h[sel], d_h[sel]), R, args.cpu_seconds,
                              "samples/s", "rays x 64 samples")
             base["value"] *= N
+            if "value" in base.get("single_thread", {}):
+                base["single_thread"]["value"] *= N
     else:  # hashgrid
         n = wl["points"]
         grid = v.nerf_hashgrid_init(16, 2 ** 19, 16, 2048)
