@@ -1,0 +1,120 @@
+"""Pins of the backward/training oracle (oracle/backward.py) against central
+finite differences of the forward oracle, closed forms of Adam and PSNR, and
+the parameter order the C ABI documents."""
+import math
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import backward, composite, rays
+
+TINY = si.NerfNetShape(depth=3, width=8, skip=1, pos_ch=9, dir_ch=9, dir_width=4)
+
+
+def _tiny_batch(R=3, N=6, seed=0):
+    o, d = rays.get_rays(1, R, 5.0, 5.0, 0.5 * R, 0.5, si.poses(1, seed=seed)[0])
+    near, far = np.full(R, 2.0, np.float32), np.full(R, 6.0, np.float32)
+    target = np.random.default_rng(seed).random((R, 3))
+    return o, d, near, far, target
+
+
+@pytest.mark.parametrize("white", [False, True])
+def test_gradients_match_central_differences(white):
+    p = si.nerf_params(TINY, seed=3)
+    # larger densities so that transmittance and every path of the network matter
+    p = dict(p, sigma=(p["sigma"][0] * 4.0, p["sigma"][1] + np.float32(0.5)))
+    o, d, near, far, target = _tiny_batch()
+    kw = dict(n_samples=6, L_pos=1, L_dir=1, seed=2, white_bkgd=white)
+    loss, _, grads = backward.train_loss_and_grads(p, o, d, near, far, target, **kw)
+    g = backward.flatten(grads)
+    flat = backward.flatten(p)
+    h = 1e-6
+    num = np.empty_like(flat)
+    for k in range(flat.size):
+        fp, fm = flat.copy(), flat.copy()
+        fp[k] += h
+        fm[k] -= h
+        lp = backward.train_loss_and_grads(backward_unflat(fp, p), o, d, near, far, target, **kw)[0]
+        lm = backward.train_loss_and_grads(backward_unflat(fm, p), o, d, near, far, target, **kw)[0]
+        num[k] = (lp - lm) / (2 * h)
+    scale = np.abs(num).max()
+    assert scale > 1e-3
+    assert np.max(np.abs(g - num)) <= 1e-6 * scale + 1e-9
+    assert np.count_nonzero(np.abs(num) > 1e-6 * scale) > 0.5 * flat.size
+
+
+def backward_unflat(flat, like):
+    """Float64 parameters (no float32 rounding, so finite differences see the
+    exact function)."""
+    out = {"shape": like["shape"]}
+    pos = 0
+
+    def take(a):
+        nonlocal pos
+        n = np.asarray(a).size
+        v = flat[pos:pos + n].reshape(np.asarray(a).shape)
+        pos += n
+        return v
+
+    out["layers"] = [(take(W), take(b)) for W, b in like["layers"]]
+    for k in ("sigma", "feature", "dir", "rgb"):
+        out[k] = (take(like[k][0]), take(like[k][1]))
+    return out
+
+
+@pytest.mark.parametrize("white", [False, True])
+def test_composite_backward_matches_central_differences(white):
+    g = np.random.default_rng(5)
+    R, N = 4, 9
+    raw = g.normal(size=(R, N, 4)) * 1.5
+    raw[0, :, 3] = np.abs(raw[0, :, 3]) + 0.1  # every density positive on one ray
+    z = np.sort(g.uniform(2, 6, size=(R, N)), axis=1).astype(np.float32)
+    d = g.normal(size=(R, 3)).astype(np.float32)
+    d_rgb = g.normal(size=(R, 3))
+
+    def L(r):
+        rgb = composite.volume_render(r, z, d, white)[0]
+        return float(np.sum(rgb * d_rgb))
+
+    ana = backward.composite_backward(raw, z, d, d_rgb, white)
+    h = 1e-6
+    num = np.zeros_like(raw)
+    for idx in np.ndindex(raw.shape):
+        rp, rm = raw.copy(), raw.copy()
+        rp[idx] += h
+        rm[idx] -= h
+        num[idx] = (L(rp) - L(rm)) / (2 * h)
+    assert np.max(np.abs(ana - num)) <= 1e-7 * max(1.0, np.abs(num).max())
+    assert np.abs(num[..., 3]).max() > 1e-3
+
+
+def test_adam_constant_gradient_closed_form():
+    """With a constant gradient g the bias-corrected moments are exactly g
+    and g^2, so after t steps p = p0 - t lr g / (|g| + eps)."""
+    g = np.array([0.3, -2.0, 1e-3, 0.0])
+    p = np.array([1.0, -1.0, 0.5, 2.0])
+    m = np.zeros(4)
+    v = np.zeros(4)
+    q = p.copy()
+    for t in range(1, 8):
+        q, m, v = backward.adam(q, g, m, v, t, lr=1e-2)
+    expect = p - 7 * 1e-2 * g / (np.abs(g) + 1e-8)
+    assert np.allclose(q, expect, rtol=0, atol=1e-12)
+
+
+def test_psnr_and_mse():
+    assert backward.psnr(1e-3) == pytest.approx(30.0)
+    assert backward.psnr(0.01) == pytest.approx(20.0)
+    assert backward.mse(np.ones((2, 3)), np.zeros((2, 3))) == 1.0
+
+
+def test_flat_order_is_the_packing_order():
+    import volume_rendering_amd as v
+    p = si.nerf_params(si.NERF_4x64, seed=1)
+    flat = backward.flatten(p)
+    ref = np.concatenate([a.ravel() for a in v.weights.forward_order(p)]).astype(np.float64)
+    assert np.array_equal(flat, ref)
+    assert flat.size == si.NERF_4x64.n_params()
+    back = backward.unflatten(flat, p)
+    assert all(np.array_equal(a, b) for a, b in zip(v.weights.forward_order(back), v.weights.forward_order(p)))
