@@ -343,6 +343,58 @@ nerf_status nerf_render_poses(const float* poses, int n_poses, const nerf_intrin
 size_t nerf_render_workspace_size(const nerf_render_cfg* cfg, int64_t n_rays);
 
 /* ---------------------------------------------------------------------- */
+/* Training step (device)                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Configuration of one training step of a NeRF-family network. */
+typedef struct {
+    nerf_mlp_desc net;     /* NERF_NET_8x256, NERF_NET_4x64 or NERF_NET_CELL_2x32; dtype: operand
+                              precision of every matrix product, forward and backward
+                              (NERF_BF16: bfloat16 operands, float32 accumulation) */
+    int32_t n_samples;     /* stratified samples per ray: 1..256 */
+    int32_t use_pi;        /* as nerf_render_cfg */
+    int32_t white_bkgd;
+    int32_t jitter;
+    uint64_t seed;         /* Philox key of the stratified jitter (as nerf_sample_stratified) */
+    uint64_t ray_offset;   /* global index of ray 0 */
+    float lr, beta1, beta2, eps; /* Adam */
+} nerf_train_cfg;
+
+/* Flat parameter count of a network kind: the weights and biases in the
+ * order nerf_pack_mlp takes them, each row-major, back to back (0 if the
+ * kind cannot be trained here). */
+int64_t nerf_train_param_count(int kind);
+
+/* Device workspace of nerf_train_step for n_rays rays (0 if unsupported). */
+size_t nerf_train_workspace_size(const nerf_train_cfg* cfg, int64_t n_rays);
+
+/* One training step ("Spatial Intelligence - Part 1: NeRF", Section 1
+ * Theory, 5. Training; Section 2 Code, 7. Training loop, one network pass):
+ * stratified samples (as nerf_sample_stratified), position and direction
+ * encodings (as nerf_encode_freq), the network (as nerf_mlp), compositing
+ * (as nerf_composite), loss = mean over rays and channels of
+ * (rgb - target)^2, the gradient of the loss with respect to every
+ * parameter, then (adam_m and adam_v given) one Adam step (Kingma and Ba,
+ * Algorithm 1, bias-corrected with step t):
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * rays_o, rays_d, target_rgb: device [n_rays, 3]; t_near, t_far: device
+ * [n_rays]; params, adam_m, adam_v: device float32 [nerf_train_param_count]
+ * (updated in place; params is read before it is updated); grad: optional
+ * device float32 [nerf_train_param_count], the gradient before the update;
+ * loss: device float32 [1]; rgb: optional device [n_rays, 3], the rendered
+ * colours.  Weight gradients are sums over samples in a fixed order: a
+ * step is deterministic.  workspace: device, 256-byte aligned, at least
+ * nerf_train_workspace_size bytes, or NULL (allocated stream-ordered and
+ * freed after the work).  Errors: null pointers, unsupported network,
+ * n_samples outside 1..256, n_rays * n_samples above 2^28, step < 1 with
+ * Adam, one of adam_m/adam_v missing, workspace too small. */
+nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
+                            const float* target_rgb, int64_t n_rays, const nerf_train_cfg* cfg, float* params,
+                            float* adam_m, float* adam_v, int64_t step, float* grad, float* loss, float* rgb,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* For callers that cannot allocate                                       */
 /* ---------------------------------------------------------------------- */
 

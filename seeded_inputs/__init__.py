@@ -25,6 +25,7 @@ TAG_HASH = 4
 TAG_OCC = 5
 TAG_SUBSET = 6
 TAG_QUERY = 7
+TAG_TARGET = 8
 
 
 def rng(seed: int, tag: int, *extra: int) -> np.random.Generator:
@@ -264,3 +265,17 @@ def subset(n_total: int, k: int, seed: int = 0) -> np.ndarray:
     if k >= n_total:
         return np.arange(n_total, dtype=np.int64)
     return np.sort(rng(seed, TAG_SUBSET).choice(n_total, size=k, replace=False)).astype(np.int64)
+
+
+def target_colors(n: int, seed: int = 0) -> np.ndarray:
+    """``n`` colours uniform in [0,1)^3, float32 [n,3] (training targets)."""
+    return rng(seed, TAG_TARGET).random((n, 3)).astype(np.float32)
+
+
+def flat_params(params: dict) -> np.ndarray:
+    """The weights and biases of a NeRF-family parameter dict back to back,
+    float32, in the C ABI's order: each hidden layer (W row-major, then b),
+    then the density head, the feature layer, the direction layer and the rgb
+    head."""
+    seq = list(params["layers"]) + [params[k] for k in ("sigma", "feature", "dir", "rgb")]
+    return np.concatenate([np.asarray(a, np.float32).ravel() for Wb in seq for a in Wb])

@@ -223,3 +223,33 @@ def test_sweep_poses_look_at_the_origin():
         assert abs(np.linalg.norm(t) - 4.0) < 1e-5 and abs(t[2] - 2.0) < 1e-5  # 4 sin 30
         # the camera looks down its -z axis: the third column points away from the origin
         assert np.allclose(p[:, 2], t / 4.0, atol=1e-6)
+
+
+def test_train_param_count_and_validation():
+    L = v.lib()
+    for kind, shape in [(1, si.NERF_8x256), (2, si.NERF_4x64), (3, si.NERF_CELL_2x32)]:
+        assert B.nerf_train_param_count(kind) == shape.n_params()
+        assert si.flat_params(si.nerf_params(shape)).size == shape.n_params()
+    assert B.nerf_train_param_count(4) == 0  # the hash field is not trained here
+    cfg = B.nerf_train_cfg(net=B.nerf_mlp_desc(2, 0), n_samples=32, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    need = B.nerf_train_workspace_size(cfg, 1000)
+    assert need > 1000 * 32 * 4
+    assert B.nerf_train_workspace_size(cfg, 2000) > need
+    P = C.c_void_p(256)  # never dereferenced: every call below fails validation first
+    args = [P] * 5
+
+    def call(n_rays, c, m=P, vv=P, step=1, ws=None, wsb=0, params=P, loss=P):
+        return L.nerf_train_step(*args, n_rays, C.byref(c), params, m, vv, step, None, loss, None, ws, wsb, None)
+
+    assert call(0, cfg) == 0  # no rays: nothing to do
+    assert call(1000, cfg, ws=P, wsb=need - 1) == 3
+    assert b"workspace" in L.nerf_last_error()
+    assert call(1000, cfg, m=None) == 1  # one Adam moment without the other
+    assert call(1000, cfg, step=0) == 1
+    assert call(1000, cfg, params=None) == 1
+    bad = B.nerf_train_cfg(net=B.nerf_mlp_desc(2, 0), n_samples=300)
+    assert call(1000, bad) == 1 and b"n_samples" in L.nerf_last_error()
+    hashnet = B.nerf_train_cfg(net=B.nerf_mlp_desc(4, 0), n_samples=32)
+    assert call(1000, hashnet) == 2
+    assert call(1 << 24, cfg) == 2  # 2^28 samples at most
+    assert B.nerf_train_workspace_size(hashnet, 10) == 0

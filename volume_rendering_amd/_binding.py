@@ -26,7 +26,8 @@ EXPORTED = [
     "nerf_abi_version", "nerf_status_str", "nerf_last_error", "nerf_hashgrid_init", "nerf_mlp_packed_bytes",
     "nerf_pack_mlp", "nerf_gen_rays", "nerf_sample_stratified", "nerf_encode_freq", "nerf_encode_sh16",
     "nerf_encode_hashgrid", "nerf_mlp", "nerf_composite", "nerf_sample_pdf", "nerf_render",
-    "nerf_render_workspace_size", "nerf_render_noalloc", "nerf_render_poses",
+    "nerf_render_workspace_size", "nerf_render_noalloc", "nerf_render_poses", "nerf_train_param_count",
+    "nerf_train_workspace_size", "nerf_train_step",
 ]
 
 
@@ -65,6 +66,12 @@ class nerf_render_cfg(C.Structure):
                 ("dbg_n_live", C.c_void_p)]
 
 
+class nerf_train_cfg(C.Structure):
+    _fields_ = [("net", nerf_mlp_desc), ("n_samples", C.c_int32), ("use_pi", C.c_int32), ("white_bkgd", C.c_int32),
+                ("jitter", C.c_int32), ("seed", C.c_uint64), ("ray_offset", C.c_uint64), ("lr", C.c_float),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float)]
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -94,6 +101,9 @@ def lib():
                                         P, P]),
             "nerf_render_poses": (I, [P, I, C.POINTER(nerf_intrinsics), C.c_float, C.c_float, C.POINTER(nerf_weights),
                                       C.POINTER(nerf_render_cfg), P, S, P, P, P, P]),
+            "nerf_train_param_count": (I64, [I]),
+            "nerf_train_workspace_size": (S, [C.POINTER(nerf_train_cfg), I64]),
+            "nerf_train_step": (I, [P, P, P, P, P, I64, C.POINTER(nerf_train_cfg), P, P, P, I64, P, P, P, P, S, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -230,3 +240,26 @@ def nerf_render_poses(poses: np.ndarray, W, H, fx, fy, cx, cy, t_near, t_far, we
     _check(lib().nerf_render_poses(p.ctypes.data, p.shape[0], C.byref(K), float(t_near), float(t_far),
                                    C.byref(weights), C.byref(cfg), ws, wsb, _ptr(rgb), _ptr(depth), _ptr(acc),
                                    _stream()), "nerf_render_poses")
+
+
+# ----------------------------------------------------------------------------
+# Training step
+# ----------------------------------------------------------------------------
+
+def nerf_train_param_count(kind: int) -> int:
+    return lib().nerf_train_param_count(kind)
+
+
+def nerf_train_workspace_size(cfg: nerf_train_cfg, n_rays: int) -> int:
+    return lib().nerf_train_workspace_size(C.byref(cfg), n_rays)
+
+
+def nerf_train_step(rays_o, rays_d, t_near, t_far, target_rgb, cfg: nerf_train_cfg, params, loss, adam_m=None,
+                    adam_v=None, step=0, grad=None, rgb=None, workspace=None):
+    """One training step; ``params`` (and the Adam moments) are float32
+    device tensors updated in place, ``loss`` a float32 device tensor [1],
+    ``workspace`` an optional device uint8 tensor."""
+    ws, wsb = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().nerf_train_step(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), _ptr(target_rgb),
+                                 rays_o.shape[0], C.byref(cfg), _ptr(params), _ptr(adam_m), _ptr(adam_v), int(step),
+                                 _ptr(grad), _ptr(loss), _ptr(rgb), ws, wsb, _stream()), "nerf_train_step")

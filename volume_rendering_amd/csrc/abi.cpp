@@ -304,6 +304,94 @@ nerf_status nerf_render_poses(const float* poses, int n_poses, const nerf_intrin
     return st;
 }
 
+int64_t nerf_train_param_count(int kind) { return net_is_nerf_family(kind) ? train_param_count(kind) : 0; }
+
+size_t nerf_train_workspace_size(const nerf_train_cfg* cfg, int64_t n_rays) {
+    if (!cfg || !net_is_nerf_family(cfg->net.kind) || (cfg->net.dtype != NERF_F32 && cfg->net.dtype != NERF_BF16))
+        return 0;
+    if (cfg->n_samples < 1 || cfg->n_samples > 256 || n_rays < 0) return 0;
+    return train_workspace_layout(cfg->net.kind, cfg->net.dtype == NERF_BF16, n_rays, cfg->n_samples, nullptr,
+                                  nullptr);
+}
+
+nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
+                            const float* target_rgb, int64_t n_rays, const nerf_train_cfg* cfg, float* params,
+                            float* adam_m, float* adam_v, int64_t step, float* grad, float* loss, float* rgb,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    NERF_REQUIRE(cfg, "nerf_train_step: cfg is NULL");
+    NERF_REQUIRE(n_rays >= 0, "nerf_train_step: n_rays %lld", (long long)n_rays);
+    if (!net_is_nerf_family(cfg->net.kind))
+        return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_train_step: network kind %d is not a NeRF-family network",
+                         cfg->net.kind);
+    NERF_REQUIRE(cfg->net.dtype == NERF_F32 || cfg->net.dtype == NERF_BF16, "nerf_train_step: dtype %d",
+                 cfg->net.dtype);
+    NERF_REQUIRE(cfg->n_samples >= 1 && cfg->n_samples <= 256, "nerf_train_step: n_samples %d outside 1..256",
+                 cfg->n_samples);
+    if (n_rays * (int64_t)cfg->n_samples > ((int64_t)1 << 28))
+        return nerf_fail(NERF_ERR_UNSUPPORTED, "nerf_train_step: %lld samples (at most 2^28)",
+                         (long long)(n_rays * cfg->n_samples));
+    NERF_REQUIRE(!adam_m == !adam_v, "nerf_train_step: give both Adam moments or neither");
+    NERF_REQUIRE(!adam_m || step >= 1, "nerf_train_step: Adam step %lld < 1", (long long)step);
+    if (n_rays == 0) return NERF_OK;
+    NERF_REQUIRE(rays_o && rays_d && t_near && t_far && target_rgb && params && loss,
+                 "nerf_train_step: NULL input or output");
+    NERF_REQUIRE(aligned4(rays_o) && aligned4(rays_d) && aligned4(t_near) && aligned4(t_far) &&
+                     aligned4(target_rgb) && aligned4(params) && aligned4(loss) && (!grad || aligned4(grad)) &&
+                     (!rgb || aligned4(rgb)) && (!adam_m || (aligned4(adam_m) && aligned4(adam_v))),
+                 "nerf_train_step: misaligned pointer");
+    const int bf16 = cfg->net.dtype == NERF_BF16;
+    const size_t need = train_workspace_layout(cfg->net.kind, bf16, n_rays, cfg->n_samples, nullptr, nullptr);
+    void* own = nullptr;
+    if (workspace) {
+        if (workspace_bytes < need)
+            return nerf_fail(NERF_ERR_WORKSPACE, "nerf_train_step: workspace has %zu bytes, needs %zu",
+                             workspace_bytes, need);
+        NERF_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+                     "nerf_train_step: workspace must be 256-byte aligned");
+    } else {
+        clear_pending();
+        const hipError_t e = hipMallocAsync(&own, need, as_stream(stream));
+        if (e != hipSuccess)
+            return nerf_fail(NERF_ERR_WORKSPACE, "nerf_train_step: cannot allocate %zu workspace bytes: %s", need,
+                             hipGetErrorString(e));
+        workspace = own;
+    }
+    TrainArgs t{};
+    t.ro = rays_o;
+    t.rd = rays_d;
+    t.tn = t_near;
+    t.tf = t_far;
+    t.target = target_rgb;
+    t.n_rays = n_rays;
+    t.n_samples = cfg->n_samples;
+    t.use_pi = cfg->use_pi;
+    t.white = cfg->white_bkgd;
+    t.jitter = cfg->jitter;
+    t.seed = cfg->seed;
+    t.ray_offset = cfg->ray_offset;
+    t.params = params;
+    t.adam_m = adam_m;
+    t.adam_v = adam_v;
+    t.grad = grad;
+    t.step = step;
+    t.lr = cfg->lr;
+    t.beta1 = cfg->beta1;
+    t.beta2 = cfg->beta2;
+    t.eps = cfg->eps;
+    t.loss = loss;
+    t.rgb_out = rgb;
+    t.workspace = workspace;
+    clear_pending();
+    launch_train_step(cfg->net.kind, bf16, t, as_stream(stream));
+    nerf_status st = check_launch("nerf_train_step");
+    if (own) {
+        const hipError_t e = hipFreeAsync(own, as_stream(stream));
+        if (st == NERF_OK && e != hipSuccess)
+            st = nerf_fail(NERF_ERR_HIP, "nerf_train_step: workspace free: %s", hipGetErrorString(e));
+    }
+    return st;
+}
+
 }  // extern "C"
 
 namespace nerf {

@@ -87,26 +87,6 @@ __host__ __device__ inline int enc_points_per_block(int width) {
     return (pw >= 256 ? 256 : pw) / 8 * 8;
 }
 
-// (sin(pi t), cos(pi t)).  t = q/2 + r with q = rint(2t) and |r| <= 1/4, both
-// exact in float32; sin(pi r) and cos(pi r) from their Taylor series through
-// degree 9 and 10 (truncation below 2.5e-8 for |pi r| <= pi/4), evaluated by
-// Horner's rule; the quadrant q mod 4 rotates the pair.
-__device__ __forceinline__ void sincospi_taylor(float t, float& s, float& c) {
-    const float q = rintf(2.0f * t);
-    const float r = fmaf(-0.5f, q, t);
-    const float r2 = r * r;
-    constexpr float a1 = 3.14159265358979312f, a3 = -5.16771278004996937f, a5 = 2.55016403987734508f,
-                    a7 = -0.599264529320791883f, a9 = 0.082145886611128191f;  // pi^j (-1)^((j-1)/2) / j!
-    constexpr float b2 = -4.934802200544679f, b4 = 4.0587121264167676f, b6 = -1.33526276885458928f,
-                    b8 = 0.235330630358893123f, b10 = -0.0258068913900140508f;  // pi^j (-1)^(j/2) / j!
-    const float S = r * fmaf(fmaf(fmaf(fmaf(a9, r2, a7), r2, a5), r2, a3), r2, a1);
-    const float C = fmaf(fmaf(fmaf(fmaf(fmaf(b10, r2, b8), r2, b6), r2, b4), r2, b2), r2, 1.0f);
-    const int qi = (int)(q - 4.0f * floorf(q * 0.25f));  // q mod 4, exact for any float q
-    const float ss = (qi & 1) ? C : S, cc = (qi & 1) ? S : C;
-    s = (qi & 2) ? -ss : ss;
-    c = ((qi + 1) & 2) ? -cc : cc;
-}
-
 __device__ __forceinline__ void enc_store16(float* dst, const float* src) {
     *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
 }

@@ -76,6 +76,33 @@ struct KiloArgs {
     float* raw_live;       // [max_live, 4]
 };
 
+// One training step of a NeRF-family network (frequency encodings): samples,
+// network, compositing, mean squared error, gradients, Adam.
+struct TrainArgs {
+    const float* ro;
+    const float* rd;
+    const float* tn;
+    const float* tf;
+    const float* target;  // [n_rays, 3]
+    int64_t n_rays;
+    int n_samples;
+    int use_pi, white, jitter;
+    uint64_t seed, ray_offset;
+    float* params;  // flat float32 weights and biases, updated in place by Adam
+    float* adam_m;  // NULL: no Adam step
+    float* adam_v;
+    float* grad;    // flat gradient out, or NULL (kept in the workspace)
+    int64_t step;   // Adam step t >= 1
+    float lr, beta1, beta2, eps;
+    float* loss;     // [1]
+    float* rgb_out;  // [n_rays, 3] or NULL
+    void* workspace;
+};
+
+size_t train_workspace_layout(int kind, int bf16, int64_t n_rays, int n_samples, char* base, void* bufs_out);
+int64_t train_param_count(int kind);
+void launch_train_step(int kind, int bf16, const TrainArgs& t, hipStream_t s);
+
 // Workspace layout of the many-tiny-networks render for n_rays x n_samples.
 size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k);
 

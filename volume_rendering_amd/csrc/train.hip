@@ -1,0 +1,862 @@
+// One training step of a NeRF-family network for gfx950 ("Spatial
+// Intelligence - Part 1: NeRF", Section 1 Theory, 5. Training: the squared
+// error between rendered and true colours; Section 2 Code, 7. Training loop:
+// MSE of the rendered rgb, Adam).  One network pass: stratified samples ->
+// encodings -> network -> compositing -> loss -> gradients of every weight
+// and bias -> Adam.
+//
+// Unlike the fused render, a training step keeps every layer's input in HBM
+// (the weight gradients need them): the network runs layer by layer as
+// matrix products on the matrix cores (bfloat16 operands with float32
+// accumulation, or float32 throughout), with
+//   forward and input gradients   C[m][n] = sum_k A[m][k] B[n][k]  (k contiguous;
+//                                 A may be two segments, e.g. [hidden, encoding])
+//   weight gradients               C[m][n] = sum_k A[k][m] B[k][n]  (k = samples,
+//                                 split over workgroups, partial sums added in a
+//                                 fixed order, so results are deterministic)
+// Activation rows are padded with zero columns to multiples of 32, the k step
+// of a tile.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <initializer_list>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "nets.hpp"
+
+namespace nerf {
+
+namespace {
+
+constexpr int kGT = 64;  // output tile (rows and columns) of a workgroup
+constexpr int kGK = 32;  // k per tile step
+
+__device__ __forceinline__ float elt_f(float v) { return v; }
+__device__ __forceinline__ float elt_f(__bf16 v) { return (float)v; }
+template <class T>
+__device__ __forceinline__ T elt_from(float v);
+template <>
+__device__ __forceinline__ float elt_from<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ __bf16 elt_from<__bf16>(float v) { return (__bf16)v; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Matrix products
+// ---------------------------------------------------------------------------
+struct SegA {
+    const void* p;
+    int ld;       // elements per row
+    int kpad;     // columns (k) of this segment, a multiple of 32
+    int row_div;  // row of product row m is m / row_div
+};
+
+struct GemmNT {
+    SegA a0, a1;        // a1.kpad == 0: one segment
+    const void* b;      // [N][ldb], ldb >= a0.kpad + a1.kpad
+    int ldb;
+    int M, N;           // product rows, columns (N a multiple of 32)
+    const float* bias;  // [N] or NULL
+    int relu;
+    const void* mask;   // keep C[m][n] only where mask[m*ldm + n] > 0, or NULL
+    int ldm;
+    void* c;
+    int ldc, c_col0, n_store, c_f32;  // stores columns n < n_store at c[m*ldc + c_col0 + n]
+};
+
+struct GemmTN {
+    const void* a;  // [K][lda], m contiguous
+    int lda, M;
+    const void* b;  // [K / b_row_div][ldb], n contiguous
+    int ldb, N, b_row_div;
+    int K, k_chunk;  // samples, samples per split (a multiple of 32)
+    float* part;     // [splits][M][N]
+};
+
+// 64 rows x 32 k of a row-major (k contiguous) matrix into LDS.
+template <class T, int LDS_LD>
+__device__ __forceinline__ void tile_rows(T (*dst)[LDS_LD], const T* src, int ld, int row_div, int r0, int R, int k0,
+                                          int tid) {
+    constexpr int PER = 16 / (int)sizeof(T);       // elements per 16-byte piece
+    constexpr int PIECES = kGT * kGK / PER / 256;  // pieces per thread
+#pragma unroll
+    for (int q = 0; q < PIECES; ++q) {
+        const int e = (tid + 256 * q) * PER;
+        const int row = e / kGK, kc = e % kGK;
+        const int r = r0 + row;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < R) v = *reinterpret_cast<const u32x4*>(src + (size_t)(r / row_div) * ld + k0 + kc);
+        *reinterpret_cast<u32x4*>(&dst[row][kc]) = v;
+    }
+}
+
+// 32 k x 64 columns of a k-major (columns contiguous) matrix, transposed into
+// LDS as [column][k].
+template <class T, int LDS_LD>
+__device__ __forceinline__ void tile_cols(T (*dst)[LDS_LD], const T* src, int ld, int row_div, int c0, int C, int k0,
+                                          int k_end, int tid) {
+    constexpr int PER = 16 / (int)sizeof(T);
+    constexpr int PIECES = kGT * kGK / PER / 256;
+#pragma unroll
+    for (int q = 0; q < PIECES; ++q) {
+        const int e = (tid + 256 * q) * PER;
+        const int kk = e / kGT, cc = e % kGT;
+        const int k = k0 + kk;
+        T v[PER];
+        if (k < k_end && c0 + cc < C) {
+            *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src + (size_t)(k / row_div) * ld + c0 + cc);
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) v[j] = elt_from<T>(0.0f);
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) dst[cc + j][kk] = v[j];
+    }
+}
+
+// acc += A-tile x B-tile over 32 k; the wave's 32x32 block is (wm, wn).
+template <class T, int LDS_LD>
+__device__ __forceinline__ void tile_mma(f32x16& acc, const T (*As)[LDS_LD], const T (*Bs)[LDS_LD], int wm, int wn,
+                                         int lane) {
+    const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31), h = lane >> 5;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[ra][16 * ks + 8 * h]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&Bs[rb][16 * ks + 8 * h]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < kGK / 2; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[ra][2 * ks + h], Bs[rb][2 * ks + h], acc, 0, 0, 0);
+    }
+}
+
+// Row (m) of accumulator r of a lane in its wave's 32x32 block.
+__device__ __forceinline__ int acc_m(int r, int lane) { return 8 * (r / 4) + 4 * (lane >> 5) + (r % 4); }
+
+template <class T>
+__global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
+    constexpr int LD = kGK + 16 / (int)sizeof(T);  // padded LDS rows (fewer bank conflicts)
+    __shared__ __attribute__((aligned(16))) T As[kGT][LD];
+    __shared__ __attribute__((aligned(16))) T Bs[kGT][LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
+    f32x16 acc = {};
+    const int K = g.a0.kpad + g.a1.kpad;
+    for (int k0 = 0; k0 < K; k0 += kGK) {
+        const bool first = k0 < g.a0.kpad;  // a k step never straddles the segments
+        const SegA sa = first ? g.a0 : g.a1;
+        tile_rows<T, LD>(As, (const T*)sa.p, sa.ld, sa.row_div, m0, g.M, first ? k0 : k0 - g.a0.kpad, tid);
+        tile_rows<T, LD>(Bs, (const T*)g.b, g.ldb, 1, n0, g.N, k0, tid);
+        __syncthreads();
+        tile_mma<T, LD>(acc, As, Bs, wm, wn, lane);
+        __syncthreads();
+    }
+    const int n = n0 + wn * 32 + (lane & 31);
+    if (n >= g.n_store) return;
+    const float bias = g.bias ? g.bias[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 32 + acc_m(r, lane);
+        if (m >= g.M) continue;
+        float v = acc[r] + bias;
+        if (g.relu) v = fmaxf(v, 0.0f);
+        if (g.mask && !(elt_f(((const T*)g.mask)[(size_t)m * g.ldm + n]) > 0.0f)) v = 0.0f;
+        const size_t at = (size_t)m * g.ldc + g.c_col0 + n;
+        if (g.c_f32)
+            ((float*)g.c)[at] = v;
+        else
+            ((T*)g.c)[at] = elt_from<T>(v);
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
+    constexpr int LD = kGK + 16 / (int)sizeof(T);
+    __shared__ __attribute__((aligned(16))) T As[kGT][LD];
+    __shared__ __attribute__((aligned(16))) T Bs[kGT][LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
+    const int kb = blockIdx.z * g.k_chunk;
+    const int ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
+    f32x16 acc = {};
+    for (int k0 = kb; k0 < ke; k0 += kGK) {
+        tile_cols<T, LD>(As, (const T*)g.a, g.lda, 1, m0, g.M, k0, ke, tid);
+        tile_cols<T, LD>(Bs, (const T*)g.b, g.ldb, g.b_row_div, n0, g.N, k0, ke, tid);
+        __syncthreads();
+        tile_mma<T, LD>(acc, As, Bs, wm, wn, lane);
+        __syncthreads();
+    }
+    const int n = n0 + wn * 32 + (lane & 31);
+    if (n >= g.N) return;
+    float* out = g.part + (size_t)blockIdx.z * g.M * g.N;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 32 + acc_m(r, lane);
+        if (m < g.M) out[(size_t)m * g.N + n] = acc[r];
+    }
+}
+
+// Column sums of a k-major [K][lda] matrix over each split: part[split][m].
+template <class T>
+__global__ void __launch_bounds__(256) k_colsum(const T* a, int lda, int M, int K, int k_chunk, float* part) {
+    const int kb = blockIdx.x * k_chunk;
+    const int ke = kb + k_chunk < K ? kb + k_chunk : K;
+    for (int m = threadIdx.x; m < M; m += blockDim.x) {
+        float s = 0.0f;
+        for (int k = kb; k < ke; ++k) s += elt_f(a[(size_t)k * lda + m]);
+        part[(size_t)blockIdx.x * M + m] = s;
+    }
+}
+
+// grad[off + m*ld + col0 + n] = sum over splits (in order) of part[s][m][n],
+// for m < rows, n < cols.
+__global__ void __launch_bounds__(256) k_reduce(const float* part, int splits, int M, int N, int rows, int cols,
+                                                float* grad, int64_t off, int ld, int col0) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)rows * cols) return;
+    const int m = (int)(t / cols), n = (int)(t % cols);
+    float s = 0.0f;
+    for (int q = 0; q < splits; ++q) s += part[((size_t)q * M + m) * N + n];
+    grad[off + (int64_t)m * ld + col0 + n] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Weights: flat float32 parameters (nerf_pack_mlp order, row-major) into
+// padded matrices of the product element type
+// ---------------------------------------------------------------------------
+struct AsmBlock {
+    int r0, c0, nr, nc;
+    int64_t src;  // flat offset of element (0, 0)
+    int src_ld;
+    int transpose;  // dst[r0+i][c0+j] = flat[src + j*src_ld + i] instead of flat[src + i*src_ld + j]
+};
+struct AsmArgs {
+    void* dst;
+    int rows, ld, f32, nblocks;
+    AsmBlock b[2];
+};
+
+template <class T>
+__global__ void __launch_bounds__(256) k_assemble(AsmArgs a, const float* flat) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)a.rows * a.ld) return;
+    const int r = (int)(t / a.ld), c = (int)(t % a.ld);
+    float v = 0.0f;
+    for (int q = 0; q < a.nblocks; ++q) {
+        const AsmBlock& k = a.b[q];
+        const int i = r - k.r0, j = c - k.c0;
+        if (i >= 0 && i < k.nr && j >= 0 && j < k.nc)
+            v = flat[k.src + (k.transpose ? (int64_t)j * k.src_ld + i : (int64_t)i * k.src_ld + j)];
+    }
+    if (a.f32)
+        ((float*)a.dst)[t] = v;
+    else
+        ((T*)a.dst)[t] = elt_from<T>(v);
+}
+
+// ---------------------------------------------------------------------------
+// Samples, encodings, compositing with its gradient, loss, Adam
+// ---------------------------------------------------------------------------
+
+// Frequency encoding of a 3-vector into a padded row: [x, sin(2^k pi x) x3,
+// cos(2^k pi x) x3 for k < L], zero padding to `ld`.
+template <class T>
+__device__ __forceinline__ void encode_row(const float (&x)[3], int L, int use_pi, T* row, int ld) {
+    int c = 0;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) row[c++] = elt_from<T>(x[a]);
+    for (int k = 0; k < L; ++k) {
+        float sn[3], cs[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const float arg = ldexpf(x[a], k);  // exact
+            if (use_pi)
+                sincospi_taylor(arg, sn[a], cs[a]);
+            else
+                sincosf(arg, &sn[a], &cs[a]);
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a) row[c++] = elt_from<T>(sn[a]);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) row[c++] = elt_from<T>(cs[a]);
+    }
+    for (; c < ld; ++c) row[c] = elt_from<T>(0.0f);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_train_samples(const float* __restrict__ ro, const float* __restrict__ rd,
+                                                       const float* __restrict__ tn, const float* __restrict__ tf,
+                                                       int64_t R, int N, uint64_t seed, uint64_t ray_offset,
+                                                       int jitter, int L, int use_pi, float* __restrict__ z, T* E,
+                                                       int ldE) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= R * N) return;
+    const int64_t r = s / N;
+    const int i = (int)(s - r * N);
+    const float u = jitter ? philox_uniform(seed, ray_offset + (uint64_t)r, (uint32_t)i, kStreamJitter) : 0.5f;
+    const float zi = stratified_z(tn[r], tf[r], i, N, u);
+    z[s] = zi;
+    float x[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) x[k] = __fadd_rn(ro[3 * r + k], __fmul_rn(zi, rd[3 * r + k]));
+    encode_row<T>(x, L, use_pi, E + s * ldE, ldE);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_train_dirs(const float* __restrict__ rd, int64_t R, int L, int use_pi, T* V,
+                                                    int ldV) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R) return;
+    const float d[3] = {rd[3 * r], rd[3 * r + 1], rd[3 * r + 2]};
+    const float dn = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    const float v[3] = {d[0] / dn, d[1] / dn, d[2] / dn};
+    encode_row<T>(v, L, use_pi, V + r * ldV, ldV);
+}
+
+constexpr int kTrainMaxSamples = 256;
+
+// One wave per ray: compositing ("Spatial Intelligence - Part 1: NeRF",
+// Section 2 Code, 5. Volume rendering in code), the ray's squared error and
+// the gradient of the mean squared error with respect to raw = (rgb_raw,
+// sigma_raw) of every sample.  With c = sigmoid(rgb_raw), s_i = 1 - alpha_i
+// + 1e-10, T_i the exclusive product of s, w_i = T_i alpha_i and
+// e_i = dL/drgb . c_i (white background: . (c_i - 1)):
+//   dL/drgb_raw_i   = w_i dL/drgb * c_i (1 - c_i)
+//   dL/dalpha_i     = T_i (e_i - R_i),  R_i = e_{i+1} alpha_{i+1} + s_{i+1} R_{i+1}
+//   dL/dsigma_raw_i = dL/dalpha_i delta_i (1 - alpha_i) [sigma_raw_i > 0].
+// R is a suffix recursion: affine maps x -> a + b x composed across the wave.
+template <class T>
+__global__ void __launch_bounds__(256) k_composite_train(const float* __restrict__ raw, const float* __restrict__ z,
+                                                         const float* __restrict__ rd,
+                                                         const float* __restrict__ target, int64_t R, int N,
+                                                         int white, float inv_count, T* d_rgb, T* d_sig,
+                                                         float* __restrict__ rgb_out, float* __restrict__ sq_err) {
+    struct Lds {
+        float alpha[kTrainMaxSamples], s[kTrainMaxSamples], trans[kTrainMaxSamples], w[kTrainMaxSamples];
+        float delta[kTrainMaxSamples], c[kTrainMaxSamples][3];
+    };
+    __shared__ Lds lds_all[4];
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= R) return;
+    Lds& S = lds_all[wave];
+    const float* zr = z + r * N;
+    const float4* rr = reinterpret_cast<const float4*>(raw) + r * N;
+    const float dx = rd[3 * r], dy = rd[3 * r + 1], dz = rd[3 * r + 2];
+    const float dn = sqrtf(dx * dx + dy * dy + dz * dz);
+    float carry = 1.0f, sr = 0.f, sg = 0.f, sb = 0.f, sa = 0.f;
+    for (int base = 0; base < N; base += kWave) {
+        const int i = base + lane;
+        const bool valid = i < N;
+        float alpha = 0.0f, delta = 0.0f;
+        float4 rw = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) {
+            delta = (i + 1 < N) ? (zr[i + 1] - zr[i]) * dn : 1e10f * dn;
+            rw = rr[i];
+            alpha = 1.0f - expf(-fmaxf(rw.w, 0.0f) * delta);
+        }
+        const float s = valid ? 1.0f - alpha + 1e-10f : 1.0f;
+        const float incl = wave_scan_mul(s);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 1.0f;
+        const float Ti = carry * excl;
+        const float w = valid ? Ti * alpha : 0.0f;
+        const float c0 = sigmoidf_(rw.x), c1 = sigmoidf_(rw.y), c2 = sigmoidf_(rw.z);
+        if (valid) {
+            S.alpha[i] = alpha;
+            S.s[i] = s;
+            S.trans[i] = Ti;
+            S.w[i] = w;
+            S.delta[i] = delta;
+            S.c[i][0] = c0;
+            S.c[i][1] = c1;
+            S.c[i][2] = c2;
+            sr += w * c0;
+            sg += w * c1;
+            sb += w * c2;
+            sa += w;
+        }
+        carry *= __shfl(incl, kWave - 1, kWave);
+    }
+    sr = wave_sum(sr);
+    sg = wave_sum(sg);
+    sb = wave_sum(sb);
+    sa = wave_sum(sa);
+    const float bg = white ? 1.0f - sa : 0.0f;
+    const float rgb[3] = {sr + bg, sg + bg, sb + bg};
+    float g[3], sq = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float e = rgb[k] - target[3 * r + k];
+        g[k] = 2.0f * e * inv_count;
+        sq += e * e;
+    }
+    if (lane == 0) {
+        sq_err[r] = sq;
+        if (rgb_out)
+            for (int k = 0; k < 3; ++k) rgb_out[3 * r + k] = rgb[k];
+    }
+    wave_lds_sync();
+    const float cw = white ? 1.0f : 0.0f;
+    float carry_R = 0.0f;  // R at the last sample of the chunk after the current one
+    const int last_base = (N - 1) / kWave * kWave;
+    for (int base = last_base; base >= 0; base -= kWave) {
+        const int i = base + lane;
+        const bool valid = i < N;
+        float e = 0.0f, a = 0.0f, b = 1.0f;
+        if (valid) {
+            e = g[0] * (S.c[i][0] - cw) + g[1] * (S.c[i][1] - cw) + g[2] * (S.c[i][2] - cw);
+            a = e * S.alpha[i];
+            b = S.s[i];
+        }
+        // inclusive suffix composition h_i = f_i o f_{i+1} o ... o f_63, f(x) = a + b x
+        float A = a, B = b;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float A2 = __shfl_down(A, off, kWave), B2 = __shfl_down(B, off, kWave);
+            if (lane + off < kWave) {
+                A = A + B * A2;
+                B = B * B2;
+            }
+        }
+        float An = __shfl_down(A, 1, kWave), Bn = __shfl_down(B, 1, kWave);
+        if (lane == kWave - 1) {
+            An = 0.0f;
+            Bn = 1.0f;
+        }
+        const float Ri = An + Bn * carry_R;
+        carry_R = __shfl(A, 0, kWave) + __shfl(B, 0, kWave) * carry_R;
+        if (valid) {
+            const int64_t sidx = r * N + i;
+            const float d_alpha = S.trans[i] * (e - Ri);
+            const float d_sigma = rr[i].w > 0.0f ? d_alpha * S.delta[i] * (1.0f - S.alpha[i]) : 0.0f;
+            T* dr = d_rgb + sidx * 32;
+            T* ds = d_sig + sidx * 32;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) dr[k] = elt_from<T>(S.w[i] * g[k] * S.c[i][k] * (1.0f - S.c[i][k]));
+            for (int k = 3; k < 32; ++k) dr[k] = elt_from<T>(0.0f);
+            ds[0] = elt_from<T>(d_sigma);
+            for (int k = 1; k < 32; ++k) ds[k] = elt_from<T>(0.0f);
+        }
+    }
+}
+
+// loss = inv_count * sum of the rays' squared errors, summed in a fixed order.
+__global__ void __launch_bounds__(256) k_train_loss(const float* __restrict__ sq_err, int64_t R, float inv_count,
+                                                    float* __restrict__ loss) {
+    __shared__ double part[256];
+    double s = 0.0;
+    for (int64_t r = threadIdx.x; r < R; r += blockDim.x) s += (double)sq_err[r];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int h = 128; h >= 1; h >>= 1) {
+        if ((int)threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = (float)(part[0] * (double)inv_count);
+}
+
+// Adam (Kingma and Ba, Algorithm 1) with bias correction: c1 = 1/(1-b1^t),
+// c2 = 1/(1-b2^t).
+__global__ void __launch_bounds__(256) k_adam(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+                                              const float* __restrict__ g, int64_t P, float lr, float b1, float b2,
+                                              float eps, float c1, float c2) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= P) return;
+    const float gi = g[i];
+    const float mi = b1 * m[i] + (1.0f - b1) * gi;
+    const float vi = b2 * v[i] + (1.0f - b2) * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    p[i] -= lr * (mi * c1) / (sqrtf(vi * c2) + eps);
+}
+
+// ---------------------------------------------------------------------------
+// Network plan
+// ---------------------------------------------------------------------------
+int pad32(int n) { return (n + 31) / 32 * 32; }
+
+// Buffers of a step (ids into TrainBufs::ptr).
+enum : int { BZ = 0, BE, BV, BF, BG, BRAW, BDRGB, BDSIG, BDG, BDF, BDH0, BDH1, BSQ, BGRAD, BPART, BBPART, BH0 };
+
+struct NetPlan {
+    int D, W, skip, Lpos, Ldir, DW;
+    int pe, de, ldE, ldV, ldG;
+    // flat offsets of each layer's weights and biases, and its input width
+    int64_t w_off[16], b_off[16];
+    int in_total[16];
+    int64_t P;  // parameters
+};
+
+NetPlan make_plan(int kind) {
+    NetPlan p{};
+    const Layer* L = net_layers(kind);
+    const int nl = net_n_layers(kind);
+    p.D = nl - 4;
+    p.W = L[0].n_out;
+    p.skip = -1;
+    for (int l = 1; l < p.D; ++l)
+        if (L[l].s1.kind == SEG_ENC) p.skip = l - 1;
+    p.Lpos = L[0].s0.L;
+    p.Ldir = L[p.D + 2].s1.L;
+    p.DW = L[p.D + 2].n_out;
+    p.pe = 3 + 6 * p.Lpos;
+    p.de = 3 + 6 * p.Ldir;
+    p.ldE = pad32(p.pe);
+    p.ldV = pad32(p.de);
+    p.ldG = pad32(p.DW);
+    int64_t off = 0;
+    for (int l = 0; l < nl; ++l) {
+        p.in_total[l] = L[l].s0.width + L[l].s1.width;
+        p.w_off[l] = off;
+        off += (int64_t)L[l].n_out * p.in_total[l];
+        p.b_off[l] = off;
+        off += L[l].n_out;
+    }
+    p.P = off;
+    return p;
+}
+
+struct TrainBufs {
+    void* ptr[BH0 + 16];
+    int splits, k_chunk;
+    // weights: forward matrices, transposed matrices, biases (per layer), the
+    // combined feature+density transpose
+    void* wf[16];
+    void* wt[16];
+    float* bias[16];
+    void* wt_head;
+};
+
+}  // namespace
+
+// Workspace of one step (bytes), laid out into b when base is given.
+size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, void* bufs_out) {
+    const NetPlan p = make_plan(kind);
+    const int64_t S = R * N;
+    const size_t es = bf16 ? 2 : 4;
+    TrainBufs b{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> void* {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return base ? base + at : nullptr;
+    };
+    b.k_chunk = 4096;
+    b.splits = (int)((S + b.k_chunk - 1) / b.k_chunk);
+    b.ptr[BZ] = take(4 * (size_t)S);
+    b.ptr[BE] = take(es * (size_t)S * p.ldE);
+    b.ptr[BV] = take(es * (size_t)R * p.ldV);
+    for (int l = 0; l < p.D; ++l) b.ptr[BH0 + l] = take(es * (size_t)S * p.W);
+    b.ptr[BF] = take(es * (size_t)S * p.W);
+    b.ptr[BG] = take(es * (size_t)S * p.ldG);
+    b.ptr[BRAW] = take(16 * (size_t)S);
+    b.ptr[BDRGB] = take(es * (size_t)S * 32);
+    b.ptr[BDSIG] = take(es * (size_t)S * 32);
+    b.ptr[BDG] = take(es * (size_t)S * p.ldG);
+    b.ptr[BDF] = take(es * (size_t)S * p.W);
+    b.ptr[BDH0] = take(es * (size_t)S * p.W);
+    b.ptr[BDH1] = take(es * (size_t)S * p.W);
+    b.ptr[BSQ] = take(4 * (size_t)R);
+    b.ptr[BGRAD] = take(4 * (size_t)p.P);
+    const int maxk = p.ldE > p.W ? p.ldE : p.W;
+    b.ptr[BPART] = take(4 * (size_t)b.splits * pad32(p.W + 32) * pad32(maxk + 32));
+    b.ptr[BBPART] = take(4 * (size_t)b.splits * pad32(p.W + 32));
+    const int nl = p.D + 4;
+    const Layer* L = net_layers(kind);
+    for (int l = 0; l < nl; ++l) {
+        const int no = pad32(L[l].n_out);
+        const int k1 = L[l].s0.kind == SEG_HIDDEN ? pad32(L[l].s0.width) : p.ldE;
+        const int k2 = L[l].s1.kind == SEG_NONE ? 0 : (l == p.D + 2 ? p.ldV : p.ldE);
+        b.wf[l] = take(es * (size_t)no * (k1 + k2));
+        b.wt[l] = take(es * (size_t)k1 * no);
+        b.bias[l] = (float*)take(4 * (size_t)no);
+    }
+    b.wt_head = take(es * (size_t)p.W * (p.W + 32));
+    if (bufs_out) *static_cast<TrainBufs*>(bufs_out) = b;
+    return off;
+}
+
+int64_t train_param_count(int kind) { return make_plan(kind).P; }
+
+namespace {
+
+template <class T>
+void gemm_nt(const GemmNT& g, hipStream_t s) {
+    hipLaunchKernelGGL(k_gemm_nt<T>, dim3((unsigned)((g.M + kGT - 1) / kGT), (unsigned)((g.N + kGT - 1) / kGT)),
+                       dim3(256), 0, s, g);
+}
+
+// Weight gradient of one input segment: part = A^T B over the samples, then
+// the ordered reduction into the flat gradient.
+template <class T>
+void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int rows_pad, const void* in, int ld_in,
+            int cols, int cols_pad, int row_div, int64_t S, float* grad, int64_t w_off, int in_total, int col0,
+            hipStream_t s) {
+    GemmTN g{};
+    g.a = dpre;
+    g.lda = ld_dpre;
+    g.M = rows_pad;
+    g.b = in;
+    g.ldb = ld_in;
+    g.N = cols_pad;
+    g.b_row_div = row_div;
+    g.K = (int)S;
+    g.k_chunk = b.k_chunk;
+    g.part = (float*)b.ptr[BPART];
+    hipLaunchKernelGGL(k_gemm_tn<T>, dim3((unsigned)((rows_pad + kGT - 1) / kGT), (unsigned)((cols_pad + kGT - 1) / kGT),
+                                          (unsigned)b.splits),
+                       dim3(256), 0, s, g);
+    const int64_t n = (int64_t)rows * cols;
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BPART],
+                       b.splits, rows_pad, cols_pad, rows, cols, grad, w_off, in_total, col0);
+}
+
+template <class T>
+void grad_b(const TrainBufs& b, const void* dpre, int ld, int rows, int64_t S, float* grad, int64_t b_off,
+            hipStream_t s) {
+    hipLaunchKernelGGL(k_colsum<T>, dim3((unsigned)b.splits), dim3(256), 0, s, (const T*)dpre, ld, rows, (int)S,
+                       b.k_chunk, (float*)b.ptr[BBPART]);
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BBPART],
+                       b.splits, rows, 1, rows, 1, grad, b_off, 1, 0);
+}
+
+template <class T>
+void assemble(void* dst, int rows, int ld, int f32, std::initializer_list<AsmBlock> blocks, const float* flat,
+              hipStream_t s) {
+    AsmArgs a{};
+    a.dst = dst;
+    a.rows = rows;
+    a.ld = ld;
+    a.f32 = f32;
+    a.nblocks = 0;
+    for (const AsmBlock& k : blocks) a.b[a.nblocks++] = k;
+    const int64_t n = (int64_t)rows * ld;
+    hipLaunchKernelGGL(k_assemble<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, flat);
+}
+
+template <class T>
+void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
+    const NetPlan p = make_plan(kind);
+    const Layer* L = net_layers(kind);
+    TrainBufs b{};
+    train_workspace_layout(kind, sizeof(T) == 2, t.n_rays, t.n_samples, (char*)t.workspace, &b);
+    const int64_t R = t.n_rays, S = R * t.n_samples;
+    const int N = t.n_samples, W = p.W, D = p.D;
+    const int nl = D + 4;
+    const int SIG = D, FEAT = D + 1, DIR = D + 2, RGB = D + 3;
+    float* grad = t.grad ? t.grad : (float*)b.ptr[BGRAD];
+
+    // --- weights of this step ------------------------------------------------
+    for (int l = 0; l < nl; ++l) {
+        const int no = pad32(L[l].n_out);
+        const int w1 = L[l].s0.width, w2 = L[l].s1.width;
+        const int k1 = L[l].s0.kind == SEG_HIDDEN ? pad32(w1) : p.ldE;
+        const int k2 = L[l].s1.kind == SEG_NONE ? 0 : (l == DIR ? p.ldV : p.ldE);
+        const int it = p.in_total[l];
+        if (k2)
+            assemble<T>(b.wf[l], no, k1 + k2, 0,
+                        {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0},
+                         AsmBlock{0, k1, L[l].n_out, w2, p.w_off[l] + w1, it, 0}},
+                        t.params, s);
+        else
+            assemble<T>(b.wf[l], no, k1, 0, {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0}}, t.params, s);
+        assemble<T>(b.wt[l], k1, no, 0, {AsmBlock{0, 0, w1, L[l].n_out, p.w_off[l], it, 1}}, t.params, s);
+        assemble<T>(b.bias[l], 1, no, 1, {AsmBlock{0, 0, 1, L[l].n_out, p.b_off[l], 0, 0}}, t.params, s);
+    }
+    // d(last hidden) = [dF, dSIG] [W_feature^T ; W_sigma^T]
+    assemble<T>(b.wt_head, W, W + 32, 0,
+                {AsmBlock{0, 0, W, W, p.w_off[FEAT], W, 1}, AsmBlock{0, W, W, 1, p.w_off[SIG], W, 1}}, t.params, s);
+
+    // --- samples and encodings -----------------------------------------------
+    hipLaunchKernelGGL(k_train_samples<T>, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, s, t.ro, t.rd, t.tn, t.tf,
+                       R, N, t.seed, t.ray_offset, t.jitter, p.Lpos, t.use_pi, (float*)b.ptr[BZ], (T*)b.ptr[BE],
+                       p.ldE);
+    hipLaunchKernelGGL(k_train_dirs<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, t.rd, R, p.Ldir, t.use_pi,
+                       (T*)b.ptr[BV], p.ldV);
+
+    // --- forward -------------------------------------------------------------
+    auto H = [&](int l) { return b.ptr[BH0 + l]; };
+    for (int l = 0; l < D; ++l) {
+        GemmNT g{};
+        g.a0 = l == 0 ? SegA{b.ptr[BE], p.ldE, p.ldE, 1} : SegA{H(l - 1), W, W, 1};
+        if (L[l].s1.kind == SEG_ENC) g.a1 = SegA{b.ptr[BE], p.ldE, p.ldE, 1};
+        g.b = b.wf[l];
+        g.ldb = g.a0.kpad + g.a1.kpad;
+        g.M = (int)S;
+        g.N = W;
+        g.bias = b.bias[l];
+        g.relu = 1;
+        g.c = H(l);
+        g.ldc = W;
+        g.n_store = W;
+        gemm_nt<T>(g, s);
+    }
+    {
+        GemmNT g{};  // density head -> raw column 3 (float32)
+        g.a0 = SegA{H(D - 1), W, W, 1};
+        g.b = b.wf[SIG];
+        g.ldb = W;
+        g.M = (int)S;
+        g.N = 32;
+        g.bias = b.bias[SIG];
+        g.c = b.ptr[BRAW];
+        g.ldc = 4;
+        g.c_col0 = 3;
+        g.n_store = 1;
+        g.c_f32 = 1;
+        gemm_nt<T>(g, s);
+        g.b = b.wf[FEAT];  // feature (no activation)
+        g.N = W;
+        g.bias = b.bias[FEAT];
+        g.c = b.ptr[BF];
+        g.ldc = W;
+        g.c_col0 = 0;
+        g.n_store = W;
+        g.c_f32 = 0;
+        gemm_nt<T>(g, s);
+        g.a0 = SegA{b.ptr[BF], W, W, 1};  // direction layer on [feature, direction encoding of the ray]
+        g.a1 = SegA{b.ptr[BV], p.ldV, p.ldV, N};
+        g.b = b.wf[DIR];
+        g.ldb = W + p.ldV;
+        g.N = p.ldG;
+        g.bias = b.bias[DIR];
+        g.relu = 1;
+        g.c = b.ptr[BG];
+        g.ldc = p.ldG;
+        g.n_store = p.ldG;
+        gemm_nt<T>(g, s);
+        g.a0 = SegA{b.ptr[BG], p.ldG, p.ldG, 1};  // rgb head -> raw columns 0..2
+        g.a1 = SegA{};
+        g.b = b.wf[RGB];
+        g.ldb = p.ldG;
+        g.N = 32;
+        g.bias = b.bias[RGB];
+        g.relu = 0;
+        g.c = b.ptr[BRAW];
+        g.ldc = 4;
+        g.n_store = 3;
+        g.c_f32 = 1;
+        gemm_nt<T>(g, s);
+    }
+
+    // --- compositing, loss and d raw -------------------------------------------
+    const float inv_count = (float)(1.0 / (3.0 * (double)R));
+    hipLaunchKernelGGL(k_composite_train<T>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
+                       (const float*)b.ptr[BRAW], (const float*)b.ptr[BZ], t.rd, t.target, R, N, t.white, inv_count,
+                       (T*)b.ptr[BDRGB], (T*)b.ptr[BDSIG], t.rgb_out, (float*)b.ptr[BSQ]);
+    hipLaunchKernelGGL(k_train_loss, dim3(1), dim3(256), 0, s, (const float*)b.ptr[BSQ], R, inv_count, t.loss);
+
+    // --- backward ----------------------------------------------------------------
+    // rgb head
+    grad_w<T>(b, b.ptr[BDRGB], 32, 3, 32, b.ptr[BG], p.ldG, p.DW, p.ldG, 1, S, grad, p.w_off[RGB], p.in_total[RGB], 0,
+              s);
+    grad_b<T>(b, b.ptr[BDRGB], 32, 3, S, grad, p.b_off[RGB], s);
+    {
+        GemmNT g{};  // dG = dRGB W_rgb, masked by G > 0
+        g.a0 = SegA{b.ptr[BDRGB], 32, 32, 1};
+        g.b = b.wt[RGB];
+        g.ldb = 32;
+        g.M = (int)S;
+        g.N = p.ldG;
+        g.mask = b.ptr[BG];
+        g.ldm = p.ldG;
+        g.c = b.ptr[BDG];
+        g.ldc = p.ldG;
+        g.n_store = p.ldG;
+        gemm_nt<T>(g, s);
+    }
+    // direction layer: weights over [feature, direction encoding]
+    grad_w<T>(b, b.ptr[BDG], p.ldG, p.DW, p.ldG, b.ptr[BF], W, W, W, 1, S, grad, p.w_off[DIR], p.in_total[DIR], 0, s);
+    grad_w<T>(b, b.ptr[BDG], p.ldG, p.DW, p.ldG, b.ptr[BV], p.ldV, p.de, p.ldV, N, S, grad, p.w_off[DIR],
+              p.in_total[DIR], W, s);
+    grad_b<T>(b, b.ptr[BDG], p.ldG, p.DW, S, grad, p.b_off[DIR], s);
+    {
+        GemmNT g{};  // dF = dG W_dir[:, :W]
+        g.a0 = SegA{b.ptr[BDG], p.ldG, p.ldG, 1};
+        g.b = b.wt[DIR];
+        g.ldb = pad32(p.DW);
+        g.M = (int)S;
+        g.N = W;
+        g.c = b.ptr[BDF];
+        g.ldc = W;
+        g.n_store = W;
+        gemm_nt<T>(g, s);
+    }
+    // feature and density heads
+    grad_w<T>(b, b.ptr[BDF], W, W, W, H(D - 1), W, W, W, 1, S, grad, p.w_off[FEAT], W, 0, s);
+    grad_b<T>(b, b.ptr[BDF], W, W, S, grad, p.b_off[FEAT], s);
+    grad_w<T>(b, b.ptr[BDSIG], 32, 1, 32, H(D - 1), W, W, W, 1, S, grad, p.w_off[SIG], W, 0, s);
+    grad_b<T>(b, b.ptr[BDSIG], 32, 1, S, grad, p.b_off[SIG], s);
+    void* dh = b.ptr[BDH0];
+    void* dh_next = b.ptr[BDH1];
+    {
+        GemmNT g{};  // d(last hidden) = [dF, dSIG] [W_feature ; W_sigma], masked
+        g.a0 = SegA{b.ptr[BDF], W, W, 1};
+        g.a1 = SegA{b.ptr[BDSIG], 32, 32, 1};
+        g.b = b.wt_head;
+        g.ldb = W + 32;
+        g.M = (int)S;
+        g.N = W;
+        g.mask = H(D - 1);
+        g.ldm = W;
+        g.c = dh;
+        g.ldc = W;
+        g.n_store = W;
+        gemm_nt<T>(g, s);
+    }
+    // hidden layers, last to first
+    for (int l = D - 1; l >= 0; --l) {
+        if (l == 0) {
+            grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[0], p.in_total[0], 0, s);
+        } else {
+            grad_w<T>(b, dh, W, W, W, H(l - 1), W, W, W, 1, S, grad, p.w_off[l], p.in_total[l], 0, s);
+            if (L[l].s1.kind == SEG_ENC)
+                grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[l], p.in_total[l], W, s);
+        }
+        grad_b<T>(b, dh, W, W, S, grad, p.b_off[l], s);
+        if (l > 0) {
+            GemmNT g{};  // d(previous hidden) = d_pre W_l[:, :W], masked by that layer's output
+            g.a0 = SegA{dh, W, W, 1};
+            g.b = b.wt[l];
+            g.ldb = W;
+            g.M = (int)S;
+            g.N = W;
+            g.mask = H(l - 1);
+            g.ldm = W;
+            g.c = dh_next;
+            g.ldc = W;
+            g.n_store = W;
+            gemm_nt<T>(g, s);
+            void* tmp = dh;
+            dh = dh_next;
+            dh_next = tmp;
+        }
+    }
+
+    // --- Adam ------------------------------------------------------------------
+    if (t.adam_m && t.adam_v && t.step >= 1) {
+        const double c1 = 1.0 / (1.0 - std::pow((double)t.beta1, (double)t.step));
+        const double c2 = 1.0 / (1.0 - std::pow((double)t.beta2, (double)t.step));
+        hipLaunchKernelGGL(k_adam, dim3((unsigned)((p.P + 255) / 256)), dim3(256), 0, s, t.params, t.adam_m, t.adam_v,
+                           (const float*)grad, p.P, t.lr, t.beta1, t.beta2, t.eps, (float)c1, (float)c2);
+    }
+}
+
+}  // namespace
+
+void launch_train_step(int kind, int bf16, const TrainArgs& t, hipStream_t s) {
+    if (bf16)
+        train_step_t<__bf16>(kind, t, s);
+    else
+        train_step_t<float>(kind, t, s);
+}
+
+}  // namespace nerf
