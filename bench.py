@@ -1,7 +1,7 @@
 """Throughput of the NeRF forward-render hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid|mlp]
+                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid|mlp|train]
                     [--dtype bf16|f32] [--no-cpu-baseline]
 
 A step is one ``nerf_render`` over the whole workload with rays, weights
@@ -14,7 +14,10 @@ roofline: ``encode`` the frequency encoding (L = 10, with the input) of the
 coarse workload's 81.92M sample points, ``composite`` the compositing of its
 1.28M rays x 64 samples, ``hashgrid`` the 16-level hash-grid encoding of
 2^22 points (all against the HBM roofline), ``mlp`` the 8x256 network in
-bfloat16 on 2^23 encoded samples read from HBM (against the MFMA roofline).
+bfloat16 on 2^23 encoded samples read from HBM (against the MFMA roofline),
+``train`` one training step (nerf_train_step: forward, loss, every gradient,
+Adam) on 4096 random rays x 64 samples of the 8x256 network, its algorithmic
+products against the MFMA roofline over the whole step's time.
 
 Prints one JSON line: rays/s (``value``), samples/s, the dominant kernel's
 achieved throughput against its roofline (timed live with HIP events on
@@ -40,6 +43,10 @@ MACS_8x256 = 593408
 MACS_4x64 = 21952
 MACS_HASH_FIELD = 19712
 MACS_CELL_2x32 = 5088
+# multiply-adds per sample of the products that carry a gradient back to a
+# layer's input: every layer but the first, without the columns of the
+# position encoding (skip layer) and of the direction encoding
+MACS_8x256_DINPUT = MACS_8x256 - 256 * 63 - 256 * 63 - 128 * 27
 
 # Memory-side bytes per launch of the dominant kernel(s), from rocprofv3
 # FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy (x2.0 and x1.0),
@@ -88,6 +95,8 @@ WORKLOADS = {
     "composite": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0),
     "hashgrid": dict(points=1 << 22, kind=0),
     "mlp": dict(poses=1, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0, rays=1 << 17),
+    # one training step: 4096 random rays of the coarse workload's images, 64 stratified samples, 8x256
+    "train": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0, rays=4096),
 }
 HBM_PEAK_GBS = 8000.0
 
@@ -408,6 +417,8 @@ def standalone(args, wl):
         far = torch.full((R,), 6.0, device=dev)
         z = torch.empty((R, N), device=dev)
         v.nerf_sample_stratified(near, far, N, 0, 0, True, z)
+    if name == "train":
+        return train_bench(args, wl)
     if name == "mlp":
         Rm = wl["rays"]
         x = (ro[:Rm, None, :] + z[:Rm, :, None] * rd[:Rm, None, :]).reshape(-1, 3).contiguous()
@@ -532,6 +543,74 @@ def standalone(args, wl):
                      "kernel": kernel, "kernel_ms": ms_kernel, "bytes_per_launch": bytes_per_unit * units},
     }
     if not args.no_cpu_baseline:
+        out_rec["cpu_baseline"] = base
+    print(json.dumps(out_rec), flush=True)
+
+
+def train_bench(args, wl):
+    """One training step (nerf_train_step) of the 8x256 network on a batch of
+    4096 random rays: forward, compositing, loss, every gradient, Adam."""
+    import torch
+    import seeded_inputs as si
+    import volume_rendering_amd as v
+    from volume_rendering_amd import _binding as B
+
+    dev = torch.device("cuda")
+    P = si.poses(wl["poses"], seed=0, hemisphere=wl["hemi"])
+    H, W, f = wl["H"], wl["W"], wl["focal"]
+    R_all, R, N = wl["poses"] * H * W, wl["rays"], wl["nc"]
+    ro_all = torch.empty((R_all, 3), device=dev)
+    rd_all = torch.empty((R_all, 3), device=dev)
+    for p in range(wl["poses"]):
+        v.nerf_gen_rays(P[p], W, H, f, f, 0.5 * W, 0.5 * H, ro_all[p * H * W:(p + 1) * H * W],
+                        rd_all[p * H * W:(p + 1) * H * W])
+    sel = torch.from_numpy(si.subset(R_all, R, seed=0)).to(dev)
+    ro, rd = ro_all[sel].contiguous(), rd_all[sel].contiguous()
+    near = torch.full((R,), 2.0, device=dev)
+    far = torch.full((R,), 6.0, device=dev)
+    tgt_h = si.target_colors(R, seed=0)
+    tgt = torch.from_numpy(tgt_h).to(dev)
+    dtype = 1 if args.dtype == "bf16" else 0
+    params_h = si.nerf_params(si.NERF_8x256, seed=0, net_id=0)
+    flat = torch.from_numpy(si.flat_params(params_h)).to(dev)
+    m, vv = torch.zeros_like(flat), torch.zeros_like(flat)
+    loss = torch.empty(1, device=dev)
+    cfg = B.nerf_train_cfg(net=B.nerf_mlp_desc(1, dtype), n_samples=N, use_pi=1, white_bkgd=0, jitter=1, seed=0,
+                           ray_offset=0, lr=5e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+    ws = torch.empty(v.nerf_train_workspace_size(cfg, R), dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def step():
+        it[0] += 1
+        cfg.seed = it[0]
+        v.nerf_train_step(ro, rd, near, far, tgt, cfg, flat, loss, m, vv, it[0], workspace=ws)
+
+    ms_step, ms_kernel = _timed(args, step, torch)
+    S = R * N
+    flops = 2.0 * (2 * MACS_8x256 + MACS_8x256_DINPUT) * S
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    dt_name = "bf16" if dtype else "f32"
+    out_rec = {
+        "metric": "training rays/s, one network pass (8x256, 64 samples per ray; MFMA util %)",
+        "value": R / (ms_step * 1e-3), "unit": "rays/s", "samples_per_sec": S / (ms_step * 1e-3), "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt_name,
+        "data": "synthetic: 4096 seeded random rays of 8 hemisphere poses at 400x400, random target colours, "
+                "He-uniform random weights",
+        "config": {"workload": "train", "rays": R, "samples_per_ray": N, "net": "8x256", "optimizer": "Adam"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[dt_name], "unit": "TFLOP/s",
+                     "frac": achieved / PEAK[dt_name], "traffic": None, "kernel": "whole step (every kernel)",
+                     "kernel_ms": ms_kernel, "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import backward as obwd
+        o_h, d_h = ro.cpu().numpy(), rd.cpu().numpy()
+        n_h, f_h = near.cpu().numpy(), far.cpu().numpy()
+        mode = "bf16" if dtype else "f64"
+        base = _cpu_rate(lambda s_: obwd.train_loss_and_grads(params_h, o_h[s_], d_h[s_], n_h[s_], f_h[s_],
+                                                              tgt_h[s_], N, 10, 4, seed=0, mode=mode,
+                                                              ray_offset=s_),
+                         R, args.cpu_seconds, "rays/s", "rays (loss and every gradient)")
         out_rec["cpu_baseline"] = base
     print(json.dumps(out_rec), flush=True)
 

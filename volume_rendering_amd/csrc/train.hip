@@ -29,9 +29,6 @@ namespace nerf {
 
 namespace {
 
-constexpr int kGT = 64;  // output tile (rows and columns) of a workgroup
-constexpr int kGK = 32;  // k per tile step
-
 __device__ __forceinline__ float elt_f(float v) { return v; }
 __device__ __forceinline__ float elt_f(__bf16 v) { return (float)v; }
 template <class T>
@@ -45,7 +42,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Matrix products
+//
+// One tile scheme for both products.  A workgroup of four waves (2 x 2)
+// computes an output tile of 64*RB rows x 64*CB columns; each wave owns
+// RB x CB blocks of 32 x 32, one matrix-engine accumulator each
+// (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2_f32).  Tile row i is the
+// instruction's A operand and tile column j its B operand, so a lane's
+// accumulator r holds rows 8(r/4) + 4(lane/32) + r%4 of column lane%32.
+// Operands stream through a double-buffered LDS ring in k-steps of 64 bytes
+// per row (32 bfloat16 or 16 float32 values; rows padded by 16 bytes); the
+// next step's global loads are in flight while the current step multiplies.
 // ---------------------------------------------------------------------------
+template <class T, int KB = 64>
+struct Tl {
+    static constexpr int PER = 16 / (int)sizeof(T);  // elements per 16 bytes
+    static constexpr int BK = KB / (int)sizeof(T);   // k per step (KB bytes per row)
+    static constexpr int P = BK + PER;               // LDS row pitch (elements)
+};
+
 struct SegA {
     const void* p;
     int ld;       // elements per row
@@ -53,6 +67,8 @@ struct SegA {
     int row_div;  // row of product row m is m / row_div
 };
 
+// Forward and input-gradient products: C[m][n] = sum_k A[m][k] B[n][k]
+// (tile rows: n; tile columns: m).
 struct GemmNT {
     SegA a0, a1;        // a1.kpad == 0: one segment
     const void* b;      // [N][ldb], ldb >= a0.kpad + a1.kpad
@@ -66,165 +82,395 @@ struct GemmNT {
     int ldc, c_col0, n_store, c_f32;  // stores columns n < n_store at c[m*ldc + c_col0 + n]
 };
 
+// Weight gradients: part[split][m][n] = sum over the split's k of
+// A[k][m] B[k / b_row_div][n] (tile rows: m; tile columns: n), and with
+// bpart the bias gradients bpart[split][m] = sum over the split's k of A[k][m].
 struct GemmTN {
     const void* a;  // [K][lda], m contiguous
-    int lda, M;
+    int lda, M;     // M (a multiple of 32) <= lda
     const void* b;  // [K / b_row_div][ldb], n contiguous
     int ldb, N, b_row_div;
-    int K, k_chunk;  // samples, samples per split (a multiple of 32)
+    int K, k_chunk;  // samples, samples per split (a multiple of 64)
     float* part;     // [splits][M][N]
+    float* bpart;    // [splits][M] or NULL
 };
 
-// 64 rows x 32 k of a row-major (k contiguous) matrix into LDS.
-template <class T, int LDS_LD>
-__device__ __forceinline__ void tile_rows(T (*dst)[LDS_LD], const T* src, int ld, int row_div, int r0, int R, int k0,
-                                          int tid) {
-    constexpr int PER = 16 / (int)sizeof(T);       // elements per 16-byte piece
-    constexpr int PIECES = kGT * kGK / PER / 256;  // pieces per thread
-#pragma unroll
-    for (int q = 0; q < PIECES; ++q) {
-        const int e = (tid + 256 * q) * PER;
-        const int row = e / kGK, kc = e % kGK;
-        const int r = r0 + row;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < R) v = *reinterpret_cast<const u32x4*>(src + (size_t)(r / row_div) * ld + k0 + kc);
-        *reinterpret_cast<u32x4*>(&dst[row][kc]) = v;
-    }
-}
+// ROWS rows x one k-step of a row-major (k contiguous) matrix: 4 pieces of
+// 16 bytes per row; rows at or beyond R read as zero.
+template <class T, int ROWS>
+struct DirectTile {
+    static constexpr int UNITS = ROWS * 4;
+    static constexpr int UPT = (UNITS + 255) / 256;
+    u32x4 v[UPT];
 
-// 32 k x 64 columns of a k-major (columns contiguous) matrix, transposed into
-// LDS as [column][k].
-template <class T, int LDS_LD>
-__device__ __forceinline__ void tile_cols(T (*dst)[LDS_LD], const T* src, int ld, int row_div, int c0, int C, int k0,
-                                          int k_end, int tid) {
-    constexpr int PER = 16 / (int)sizeof(T);
-    constexpr int PIECES = kGT * kGK / PER / 256;
+    __device__ __forceinline__ void load(const T* src, int ld, int row_div, int r0, int R, int k, int tid) {
 #pragma unroll
-    for (int q = 0; q < PIECES; ++q) {
-        const int e = (tid + 256 * q) * PER;
-        const int kk = e / kGT, cc = e % kGT;
-        const int k = k0 + kk;
-        T v[PER];
-        if (k < k_end && c0 + cc < C) {
-            *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src + (size_t)(k / row_div) * ld + c0 + cc);
-        } else {
-#pragma unroll
-            for (int j = 0; j < PER; ++j) v[j] = elt_from<T>(0.0f);
+        for (int q = 0; q < UPT; ++q) {
+            const int u = tid + 256 * q;
+            v[q] = u32x4{0u, 0u, 0u, 0u};
+            if (UNITS % 256 == 0 || u < UNITS) {
+                const int r = r0 + (u >> 2);
+                if (r < R) {
+                    const int row = row_div == 1 ? r : r / row_div;
+                    v[q] = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + k + (u & 3) * Tl<T>::PER);
+                }
+            }
         }
-#pragma unroll
-        for (int j = 0; j < PER; ++j) dst[cc + j][kk] = v[j];
     }
-}
+    __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+        for (int q = 0; q < UPT; ++q) {
+            const int u = tid + 256 * q;
+            if (UNITS % 256 == 0 || u < UNITS)
+                *reinterpret_cast<u32x4*>(lds + (u >> 2) * Tl<T>::P + (u & 3) * Tl<T>::PER) = v[q];
+        }
+    }
+};
 
-// acc += A-tile x B-tile over 32 k; the wave's 32x32 block is (wm, wn).
-template <class T, int LDS_LD>
-__device__ __forceinline__ void tile_mma(f32x16& acc, const T (*As)[LDS_LD], const T (*Bs)[LDS_LD], int wm, int wn,
-                                         int lane) {
-    const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31), h = lane >> 5;
+// One k-step x COLS columns of a k-major (columns contiguous) matrix,
+// transposed into LDS rows [column][k]: each unit loads PER k-rows of PER
+// columns (16 bytes each) and transposes the PER x PER block in registers.
+// Thread t takes units t - base (+256, ...).  k at or beyond k_end and
+// columns at or beyond C read as zero.
+template <class T, int COLS, int KB>
+struct TransTile {
+    static constexpr int PER = Tl<T, KB>::PER;
+    static constexpr int CU = COLS / PER;  // units across the columns
+    static constexpr int UNITS = (Tl<T, KB>::BK / PER) * CU;
+    static constexpr int UPT = (UNITS + 255) / 256;
+    union Piece {
+        u32x4 u;
+        T e[PER];
+    };
+    Piece v[UPT][PER];
+
+    __device__ __forceinline__ void load(const T* src, int ld, int row_div, int c0, int C, int k0, int k_end,
+                                         int t) {
+#pragma unroll
+        for (int q = 0; q < UPT; ++q) {
+            const int u = t + 256 * q;
+#pragma unroll
+            for (int r = 0; r < PER; ++r) v[q][r].u = u32x4{0u, 0u, 0u, 0u};
+            if (u >= 0 && u < UNITS) {
+                const int c = c0 + (u % CU) * PER;
+                const int kb = k0 + (u / CU) * PER;
+                if (c < C) {
+#pragma unroll
+                    for (int r = 0; r < PER; ++r) {
+                        const int k = kb + r;
+                        if (k < k_end) {
+                            const int row = row_div == 1 ? k : k / row_div;
+                            v[q][r].u = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + c);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(T* lds, int t) const {
+#pragma unroll
+        for (int q = 0; q < UPT; ++q) {
+            const int u = t + 256 * q;
+            if (u >= 0 && u < UNITS) {
+                const int col = (u % CU) * PER, kq = (u / CU) * PER;
+#pragma unroll
+                for (int c = 0; c < PER; ++c) {
+                    Piece w;
+#pragma unroll
+                    for (int r = 0; r < PER; ++r) w.e[r] = v[q][r].e[c];
+                    *reinterpret_cast<u32x4*>(lds + (col + c) * Tl<T, KB>::P + kq) = w.u;
+                }
+            }
+        }
+    }
+};
+
+// acc += (the wave's rows of the row tile) x (its columns of the column tile)
+// over one k-step.  R and C point at the wave's first row of each tile.
+template <class T, int RB, int CB, int KB = 64>
+__device__ __forceinline__ void wave_mma(f32x16 (&acc)[RB][CB], const T* R, const T* C, int lane) {
+    constexpr int P = Tl<T, KB>::P;
+    const int l32 = lane & 31, h = lane >> 5;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int ks = 0; ks < kGK / 16; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[ra][16 * ks + 8 * h]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&Bs[rb][16 * ks + 8 * h]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        for (int ks = 0; ks < Tl<T, KB>::BK / 16; ++ks) {
+            bf16x8 a[RB], b[CB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(R + (32 * i + l32) * P + 16 * ks + 8 * h);
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(C + (32 * j + l32) * P + 16 * ks + 8 * h);
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     } else {
 #pragma unroll
-        for (int ks = 0; ks < kGK / 2; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[ra][2 * ks + h], Bs[rb][2 * ks + h], acc, 0, 0, 0);
-    }
-}
-
-// Row (m) of accumulator r of a lane in its wave's 32x32 block.
-__device__ __forceinline__ int acc_m(int r, int lane) { return 8 * (r / 4) + 4 * (lane >> 5) + (r % 4); }
-
-template <class T>
-__global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
-    constexpr int LD = kGK + 16 / (int)sizeof(T);  // padded LDS rows (fewer bank conflicts)
-    __shared__ __attribute__((aligned(16))) T As[kGT][LD];
-    __shared__ __attribute__((aligned(16))) T Bs[kGT][LD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
-    f32x16 acc = {};
-    const int K = g.a0.kpad + g.a1.kpad;
-    for (int k0 = 0; k0 < K; k0 += kGK) {
-        const bool first = k0 < g.a0.kpad;  // a k step never straddles the segments
-        const SegA sa = first ? g.a0 : g.a1;
-        tile_rows<T, LD>(As, (const T*)sa.p, sa.ld, sa.row_div, m0, g.M, first ? k0 : k0 - g.a0.kpad, tid);
-        tile_rows<T, LD>(Bs, (const T*)g.b, g.ldb, 1, n0, g.N, k0, tid);
-        __syncthreads();
-        tile_mma<T, LD>(acc, As, Bs, wm, wn, lane);
-        __syncthreads();
-    }
-    const int n = n0 + wn * 32 + (lane & 31);
-    if (n >= g.n_store) return;
-    const float bias = g.bias ? g.bias[n] : 0.0f;
+        for (int ks = 0; ks < Tl<T, KB>::BK / 2; ++ks) {
+            float a[RB], b[CB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 32 + acc_m(r, lane);
-        if (m >= g.M) continue;
-        float v = acc[r] + bias;
-        if (g.relu) v = fmaxf(v, 0.0f);
-        if (g.mask && !(elt_f(((const T*)g.mask)[(size_t)m * g.ldm + n]) > 0.0f)) v = 0.0f;
-        const size_t at = (size_t)m * g.ldc + g.c_col0 + n;
-        if (g.c_f32)
-            ((float*)g.c)[at] = v;
-        else
-            ((T*)g.c)[at] = elt_from<T>(v);
+            for (int i = 0; i < RB; ++i) a[i] = R[(32 * i + l32) * P + 2 * ks + h];
+#pragma unroll
+            for (int j = 0; j < CB; ++j) b[j] = C[(32 * j + l32) * P + 2 * ks + h];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
     }
 }
 
 template <class T>
-__global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
-    constexpr int LD = kGK + 16 / (int)sizeof(T);
-    __shared__ __attribute__((aligned(16))) T As[kGT][LD];
-    __shared__ __attribute__((aligned(16))) T Bs[kGT][LD];
+__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)x[e];
+    } else {
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        v[0] = x.x;
+        v[1] = x.y;
+        v[2] = x.z;
+        v[3] = x.w;
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)v[e];
+        *reinterpret_cast<bf16x4*>(p) = x;
+    } else {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+template <class T, int RB, int CB>
+__global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
+    constexpr int P = Tl<T>::P, BK = Tl<T>::BK, TR = 64 * RB, TC = 64 * CB;
+    // epilogue staging: per phase PH block-rows (128 bytes of features) of both halves
+    constexpr int PH = (int)(128 / (32 * sizeof(T))) < RB ? (int)(128 / (32 * sizeof(T))) : RB;
+    constexpr int FW = 32 * PH;                         // features per half and phase
+    constexpr int SP = 2 * FW + (int)(16 / sizeof(T));  // staged row pitch (elements)
+    constexpr int RING = (TR + TC) * P, STAGE = TC * SP;
+    __shared__ __attribute__((aligned(16))) T lds_all[2 * RING > STAGE ? 2 * RING : STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int n0 = blockIdx.y * TR, m0 = blockIdx.x * TC;
+    DirectTile<T, TR> rt;
+    DirectTile<T, TC> ct;
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+    const int K = g.a0.kpad + g.a1.kpad;
+    auto load = [&](int k0) {
+        rt.load((const T*)g.b, g.ldb, 1, n0, g.N, k0, tid);
+        if (k0 < g.a0.kpad)  // a k-step never straddles the segments
+            ct.load((const T*)g.a0.p, g.a0.ld, g.a0.row_div, m0, g.M, k0, tid);
+        else
+            ct.load((const T*)g.a1.p, g.a1.ld, g.a1.row_div, m0, g.M, k0 - g.a0.kpad, tid);
+    };
+    load(0);
+    rt.store(lds_all, tid);
+    ct.store(lds_all + TR * P, tid);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        const bool more = k0 + BK < K;
+        if (more) load(k0 + BK);
+        const T* cur = lds_all + buf * RING;
+        wave_mma<T, RB, CB>(acc, cur + wr * 32 * RB * P, cur + TR * P + wc * 32 * CB * P, lane);
+        if (more) {
+            T* nxt = lds_all + (buf ^ 1) * RING;
+            rt.store(nxt, tid);
+            ct.store(nxt + TR * P, tid);
+        }
+        __syncthreads();
+        buf ^= 1;
+    }
+    const int l32 = lane & 31, h = lane >> 5;
+    if (!g.c_f32 && g.n_store == g.N && g.c_col0 == 0) {
+        // Through LDS, so that every row leaves as whole 128-byte lines: in
+        // phase p each wave stages PH block-rows (128 bytes of features per
+        // row) of its accumulators, after bias and ReLU, as [sample][half,
+        // feature]; then 16-byte pieces go out along the rows, masked.
+        constexpr int PPR = 2 * FW * (int)sizeof(T) / 16;  // 16-byte pieces per staged row
+        T* st = lds_all;
+#pragma unroll
+        for (int p = 0; p < RB / PH; ++p) {
+#pragma unroll
+            for (int ii = 0; ii < PH; ++ii) {
+                const int i = p * PH + ii;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int ml = wc * 32 * CB + 32 * j + l32;
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int fl = 32 * ii + 8 * gq + 4 * h;  // feature within the half and phase
+                        const int n = n0 + wr * 32 * RB + 32 * i + 8 * gq + 4 * h;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = acc[i][j][4 * gq + e] + (g.bias ? g.bias[n + e] : 0.0f);
+                            if (g.relu) v[e] = fmaxf(v[e], 0.0f);
+                        }
+                        store4<T>(st + ml * SP + wr * FW + fl, v);
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < TC * PPR / 256; ++q) {
+                const int u = tid + 256 * q;
+                const int ml = u / PPR, pc = u % PPR;
+                const int half = pc / (PPR / 2), e0 = (pc % (PPR / 2)) * (int)(16 / sizeof(T));
+                const int m = m0 + ml;
+                const int n = n0 + half * 32 * RB + p * FW + e0;
+                if (m < g.M && n < g.N) {
+                    union {
+                        u32x4 u;
+                        T e[16 / sizeof(T)];
+                    } x, mk;
+                    x.u = *reinterpret_cast<const u32x4*>(st + ml * SP + half * FW + e0);
+                    if (g.mask) {
+                        mk.u = *reinterpret_cast<const u32x4*>((const T*)g.mask + (size_t)m * g.ldm + n);
+#pragma unroll
+                        for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
+                            if (!(elt_f(mk.e[e]) > 0.0f)) x.e[e] = elt_from<T>(0.0f);
+                    }
+                    *reinterpret_cast<u32x4*>((T*)g.c + (size_t)m * g.ldc + g.c_col0 + n) = x.u;
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    // narrow float32 outputs (the heads into raw): element stores
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int m = m0 + wc * 32 * CB + 32 * j + l32;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = n0 + wr * 32 * RB + 32 * i + 8 * gq + 4 * h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (n + e >= g.n_store) continue;
+                    float x = acc[i][j][4 * gq + e] + (g.bias ? g.bias[n + e] : 0.0f);
+                    if (g.relu) x = fmaxf(x, 0.0f);
+                    if (g.mask && !(elt_f(((const T*)g.mask)[(size_t)m * g.ldm + n + e]) > 0.0f)) x = 0.0f;
+                    const size_t at = (size_t)m * g.ldc + g.c_col0 + n + e;
+                    if (g.c_f32)
+                        ((float*)g.c)[at] = x;
+                    else
+                        ((T*)g.c)[at] = elt_from<T>(x);
+                }
+            }
+        }
+    }
+}
+
+// Weight gradients, k-steps of 128 bytes per row.  When both tiles' units
+// fit one pass of the workgroup, the row tile is loaded by the first threads
+// and the column tile by the rest.
+template <class T, int RB, int CB>
+__global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
+    constexpr int KB = 128;
+    constexpr int P = Tl<T, KB>::P, BK = Tl<T, KB>::BK, TR = 64 * RB, TC = 64 * CB;
+    using RT = TransTile<T, TR, KB>;
+    using CT = TransTile<T, TC, KB>;
+    constexpr int CBASE = RT::UNITS + CT::UNITS <= 256 ? RT::UNITS : 0;
+    __shared__ __attribute__((aligned(16))) T lds[2][(TR + TC) * P];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int m0 = blockIdx.x * TR, n0 = blockIdx.y * TC;
     const int kb = blockIdx.z * g.k_chunk;
     const int ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
-    f32x16 acc = {};
-    for (int k0 = kb; k0 < ke; k0 += kGK) {
-        tile_cols<T, LD>(As, (const T*)g.a, g.lda, 1, m0, g.M, k0, ke, tid);
-        tile_cols<T, LD>(Bs, (const T*)g.b, g.ldb, g.b_row_div, n0, g.N, k0, ke, tid);
-        __syncthreads();
-        tile_mma<T, LD>(acc, As, Bs, wm, wn, lane);
-        __syncthreads();
-    }
-    const int n = n0 + wn * 32 + (lane & 31);
-    if (n >= g.N) return;
-    float* out = g.part + (size_t)blockIdx.z * g.M * g.N;
+    const bool bias = g.bpart && blockIdx.y == 0 && tid < TR;
+    RT rt;
+    CT ct;
+    f32x16 acc[RB][CB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 32 + acc_m(r, lane);
-        if (m < g.M) out[(size_t)m * g.N + n] = acc[r];
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+    float bsum = 0.0f;
+    auto load = [&](int k0) {
+        rt.load((const T*)g.a, g.lda, 1, m0, g.M, k0, ke, tid);
+        ct.load((const T*)g.b, g.ldb, g.b_row_div, n0, g.N, k0, ke, tid - CBASE);
+    };
+    auto store = [&](T* l) {
+        rt.store(l, tid);
+        ct.store(l + TR * P, tid - CBASE);
+    };
+    load(kb);
+    store(lds[0]);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kb; k0 < ke; k0 += BK) {
+        const bool more = k0 + BK < ke;
+        if (more) load(k0 + BK);
+        if (bias) {
+            const T* row = lds[buf] + tid * P;
+#pragma unroll
+            for (int k = 0; k < BK; ++k) bsum += elt_f(row[k]);
+        }
+        wave_mma<T, RB, CB, KB>(acc, lds[buf] + wr * 32 * RB * P, lds[buf] + TR * P + wc * 32 * CB * P, lane);
+        if (more) store(lds[buf ^ 1]);
+        __syncthreads();
+        buf ^= 1;
     }
-}
-
-// Column sums of a k-major [K][lda] matrix over each split: part[split][m].
-template <class T>
-__global__ void __launch_bounds__(256) k_colsum(const T* a, int lda, int M, int K, int k_chunk, float* part) {
-    const int kb = blockIdx.x * k_chunk;
-    const int ke = kb + k_chunk < K ? kb + k_chunk : K;
-    for (int m = threadIdx.x; m < M; m += blockDim.x) {
-        float s = 0.0f;
-        for (int k = kb; k < ke; ++k) s += elt_f(a[(size_t)k * lda + m]);
-        part[(size_t)blockIdx.x * M + m] = s;
+    float* out = g.part + (size_t)blockIdx.z * g.M * g.N;
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int n = n0 + wc * 32 * CB + 32 * j + l32;
+        if (n >= g.N) continue;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wr * 32 * RB + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (m < g.M) out[(size_t)m * g.N + n] = acc[i][j][r];
+            }
     }
+    if (bias && m0 + tid < g.M) g.bpart[(size_t)blockIdx.z * g.M + m0 + tid] = bsum;
 }
 
 // grad[off + m*ld + col0 + n] = sum over splits (in order) of part[s][m][n],
-// for m < rows, n < cols.
+// for m < rows, n < cols; N a multiple of 4 (each thread sums 4 columns).
 __global__ void __launch_bounds__(256) k_reduce(const float* part, int splits, int M, int N, int rows, int cols,
                                                 float* grad, int64_t off, int ld, int col0) {
+    const int cq = (cols + 3) / 4;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)rows * cols) return;
-    const int m = (int)(t / cols), n = (int)(t % cols);
-    float s = 0.0f;
-    for (int q = 0; q < splits; ++q) s += part[((size_t)q * M + m) * N + n];
-    grad[off + (int64_t)m * ld + col0 + n] = s;
+    if (t >= (int64_t)rows * cq) return;
+    const int m = (int)(t / cq), n = 4 * (int)(t % cq);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int q = 0; q < splits; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(part + ((size_t)q * M + m) * N + n);
+        s.x += x.x;
+        s.y += x.y;
+        s.z += x.z;
+        s.w += x.w;
+    }
+    const float v[4] = {s.x, s.y, s.z, s.w};
+    float* o = grad + off + (int64_t)m * ld + col0 + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (n + e < cols) o[e] = v[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -549,7 +795,10 @@ size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, 
         off += (bytes + 255) / 256 * 256;
         return base ? base + at : nullptr;
     };
-    b.k_chunk = 4096;
+    // about 128 splits of the samples for the weight gradients (whole
+    // multiples of 64, at least 512 samples each)
+    const int64_t per = ((S + 127) / 128 + 63) / 64 * 64;
+    b.k_chunk = (int)(per > 512 ? per : 512);
     b.splits = (int)((S + b.k_chunk - 1) / b.k_chunk);
     b.ptr[BZ] = take(4 * (size_t)S);
     b.ptr[BE] = take(es * (size_t)S * p.ldE);
@@ -590,16 +839,23 @@ namespace {
 
 template <class T>
 void gemm_nt(const GemmNT& g, hipStream_t s) {
-    hipLaunchKernelGGL(k_gemm_nt<T>, dim3((unsigned)((g.M + kGT - 1) / kGT), (unsigned)((g.N + kGT - 1) / kGT)),
-                       dim3(256), 0, s, g);
+    // tile rows: the product's columns n (weights); tile columns: its rows m (samples)
+    const unsigned gx4 = (unsigned)((g.M + 255) / 256), gx2 = (unsigned)((g.M + 127) / 128);
+    if (g.N > 128)
+        hipLaunchKernelGGL((k_gemm_nt<T, 4, 2>), dim3(gx2, (unsigned)((g.N + 255) / 256)), dim3(256), 0, s, g);
+    else if (g.N > 64)
+        hipLaunchKernelGGL((k_gemm_nt<T, 2, 2>), dim3(gx2, 1), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_gemm_nt<T, 1, 4>), dim3(gx4, 1), dim3(256), 0, s, g);
 }
 
-// Weight gradient of one input segment: part = A^T B over the samples, then
-// the ordered reduction into the flat gradient.
+// Weight gradient of one input segment: part = A^T B over each split of the
+// samples, then the ordered reduction into the flat gradient; with b_off >= 0
+// also the bias gradient (the column sums of A).
 template <class T>
 void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int rows_pad, const void* in, int ld_in,
             int cols, int cols_pad, int row_div, int64_t S, float* grad, int64_t w_off, int in_total, int col0,
-            hipStream_t s) {
+            int64_t b_off, hipStream_t s) {
     GemmTN g{};
     g.a = dpre;
     g.lda = ld_dpre;
@@ -611,21 +867,24 @@ void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int row
     g.K = (int)S;
     g.k_chunk = b.k_chunk;
     g.part = (float*)b.ptr[BPART];
-    hipLaunchKernelGGL(k_gemm_tn<T>, dim3((unsigned)((rows_pad + kGT - 1) / kGT), (unsigned)((cols_pad + kGT - 1) / kGT),
-                                          (unsigned)b.splits),
-                       dim3(256), 0, s, g);
-    const int64_t n = (int64_t)rows * cols;
+    g.bpart = b_off >= 0 ? (float*)b.ptr[BBPART] : nullptr;
+    const int RB = rows_pad > 64 ? 2 : 1, CB = cols_pad > 64 ? 2 : 1;
+    const dim3 grid((unsigned)((rows_pad + 64 * RB - 1) / (64 * RB)), (unsigned)((cols_pad + 64 * CB - 1) / (64 * CB)),
+                    (unsigned)b.splits);
+    if (RB == 2 && CB == 2)
+        hipLaunchKernelGGL((k_gemm_tn<T, 2, 2>), grid, dim3(256), 0, s, g);
+    else if (RB == 2)
+        hipLaunchKernelGGL((k_gemm_tn<T, 2, 1>), grid, dim3(256), 0, s, g);
+    else if (CB == 2)
+        hipLaunchKernelGGL((k_gemm_tn<T, 1, 2>), grid, dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_gemm_tn<T, 1, 1>), grid, dim3(256), 0, s, g);
+    const int64_t n = (int64_t)rows * ((cols + 3) / 4);
     hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BPART],
                        b.splits, rows_pad, cols_pad, rows, cols, grad, w_off, in_total, col0);
-}
-
-template <class T>
-void grad_b(const TrainBufs& b, const void* dpre, int ld, int rows, int64_t S, float* grad, int64_t b_off,
-            hipStream_t s) {
-    hipLaunchKernelGGL(k_colsum<T>, dim3((unsigned)b.splits), dim3(256), 0, s, (const T*)dpre, ld, rows, (int)S,
-                       b.k_chunk, (float*)b.ptr[BBPART]);
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BBPART],
-                       b.splits, rows, 1, rows, 1, grad, b_off, 1, 0);
+    if (b_off >= 0)  // bias partials [split][rows_pad]: one row of rows_pad columns per split
+        hipLaunchKernelGGL(k_reduce, dim3((unsigned)((rows + 3) / 4 + 255) / 256), dim3(256), 0, s,
+                           (const float*)b.ptr[BBPART], b.splits, 1, rows_pad, 1, rows, grad, b_off, 0, 0);
 }
 
 template <class T>
@@ -757,8 +1016,7 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
     // --- backward ----------------------------------------------------------------
     // rgb head
     grad_w<T>(b, b.ptr[BDRGB], 32, 3, 32, b.ptr[BG], p.ldG, p.DW, p.ldG, 1, S, grad, p.w_off[RGB], p.in_total[RGB], 0,
-              s);
-    grad_b<T>(b, b.ptr[BDRGB], 32, 3, S, grad, p.b_off[RGB], s);
+              p.b_off[RGB], s);
     {
         GemmNT g{};  // dG = dRGB W_rgb, masked by G > 0
         g.a0 = SegA{b.ptr[BDRGB], 32, 32, 1};
@@ -774,10 +1032,10 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         gemm_nt<T>(g, s);
     }
     // direction layer: weights over [feature, direction encoding]
-    grad_w<T>(b, b.ptr[BDG], p.ldG, p.DW, p.ldG, b.ptr[BF], W, W, W, 1, S, grad, p.w_off[DIR], p.in_total[DIR], 0, s);
+    grad_w<T>(b, b.ptr[BDG], p.ldG, p.DW, p.ldG, b.ptr[BF], W, W, W, 1, S, grad, p.w_off[DIR], p.in_total[DIR], 0,
+              p.b_off[DIR], s);
     grad_w<T>(b, b.ptr[BDG], p.ldG, p.DW, p.ldG, b.ptr[BV], p.ldV, p.de, p.ldV, N, S, grad, p.w_off[DIR],
-              p.in_total[DIR], W, s);
-    grad_b<T>(b, b.ptr[BDG], p.ldG, p.DW, S, grad, p.b_off[DIR], s);
+              p.in_total[DIR], W, -1, s);
     {
         GemmNT g{};  // dF = dG W_dir[:, :W]
         g.a0 = SegA{b.ptr[BDG], p.ldG, p.ldG, 1};
@@ -791,10 +1049,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         gemm_nt<T>(g, s);
     }
     // feature and density heads
-    grad_w<T>(b, b.ptr[BDF], W, W, W, H(D - 1), W, W, W, 1, S, grad, p.w_off[FEAT], W, 0, s);
-    grad_b<T>(b, b.ptr[BDF], W, W, S, grad, p.b_off[FEAT], s);
-    grad_w<T>(b, b.ptr[BDSIG], 32, 1, 32, H(D - 1), W, W, W, 1, S, grad, p.w_off[SIG], W, 0, s);
-    grad_b<T>(b, b.ptr[BDSIG], 32, 1, S, grad, p.b_off[SIG], s);
+    grad_w<T>(b, b.ptr[BDF], W, W, W, H(D - 1), W, W, W, 1, S, grad, p.w_off[FEAT], W, 0, p.b_off[FEAT], s);
+    grad_w<T>(b, b.ptr[BDSIG], 32, 1, 32, H(D - 1), W, W, W, 1, S, grad, p.w_off[SIG], W, 0, p.b_off[SIG], s);
     void* dh = b.ptr[BDH0];
     void* dh_next = b.ptr[BDH1];
     {
@@ -815,13 +1071,14 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
     // hidden layers, last to first
     for (int l = D - 1; l >= 0; --l) {
         if (l == 0) {
-            grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[0], p.in_total[0], 0, s);
+            grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[0], p.in_total[0], 0,
+                      p.b_off[0], s);
         } else {
-            grad_w<T>(b, dh, W, W, W, H(l - 1), W, W, W, 1, S, grad, p.w_off[l], p.in_total[l], 0, s);
+            grad_w<T>(b, dh, W, W, W, H(l - 1), W, W, W, 1, S, grad, p.w_off[l], p.in_total[l], 0, p.b_off[l], s);
             if (L[l].s1.kind == SEG_ENC)
-                grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[l], p.in_total[l], W, s);
+                grad_w<T>(b, dh, W, W, W, b.ptr[BE], p.ldE, p.pe, p.ldE, 1, S, grad, p.w_off[l], p.in_total[l], W,
+                          -1, s);
         }
-        grad_b<T>(b, dh, W, W, S, grad, p.b_off[l], s);
         if (l > 0) {
             GemmNT g{};  // d(previous hidden) = d_pre W_l[:, :W], masked by that layer's output
             g.a0 = SegA{dh, W, W, 1};
