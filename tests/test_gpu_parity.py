@@ -43,7 +43,8 @@ def test_gen_rays_bit_exact(v, H, W, f, hemi):
     assert np.array_equal(host(ro), o) and np.array_equal(host(rd), d)
 
 
-@pytest.mark.parametrize("n,jitter,offset", [(16, True, 0), (64, True, 12345), (192, False, 0), (1, True, 7)])
+@pytest.mark.parametrize("n,jitter,offset", [(16, True, 0), (64, True, 12345), (192, False, 0), (1, True, 7),
+                                             (64, True, 2 ** 32 - 500), (16, True, 2 ** 40 + 3)])
 def test_stratified_bit_exact(v, n, jitter, offset):
     say(f"stratified n={n} jitter={jitter}")
     R = 1000
@@ -231,11 +232,11 @@ def test_sample_pdf_unordered_coarse(v):
 # ----------------------------------------------------------------------------
 
 def _render(v, mode, kind, dtype, ro, rd, near, far, nets, nc, nf=0, seed=0, jitter=True, chunk=0, grid=None,
-            white=False):
+            white=False, use_pi=True, ray_offset=0):
     import volume_rendering_amd._binding as B
     R = ro.shape[0]
-    cfg = B.nerf_render_cfg(mode=mode, n_coarse=nc, n_fine=nf, use_pi=1, white_bkgd=int(white), jitter=int(jitter),
-                            seed=seed, ray_offset=0, chunk=chunk, box_lo=-1.5, box_hi=1.5)
+    cfg = B.nerf_render_cfg(mode=mode, n_coarse=nc, n_fine=nf, use_pi=int(use_pi), white_bkgd=int(white),
+                            jitter=int(jitter), seed=seed, ray_offset=ray_offset, chunk=chunk, box_lo=-1.5, box_hi=1.5)
     dz, dw = empty((R, nc + nf)), empty((R, nc))
     cfg.dbg_z, cfg.dbg_w_coarse = dz.data_ptr(), dw.data_ptr()
     w = B.nerf_weights(net=B.nerf_mlp_desc(kind, dtype), coarse=nets[0].data_ptr(),
@@ -248,18 +249,20 @@ def _render(v, mode, kind, dtype, ro, rd, near, far, nets, nc, nf=0, seed=0, jit
     return host(rgb), host(depth), host(acc), host(dz), host(dw)
 
 
-def test_render_tiny_coarse_fp32(v):
+@pytest.mark.parametrize("use_pi,ray_offset", [(True, 0), (False, 0), (True, 2 ** 32 - 300)])
+def test_render_tiny_coarse_fp32(v, use_pi, ray_offset):
     """32x32 rays, focal 40, a sphere pose; 16 jittered samples; PE 6/4;
-    float32 4x64 network."""
-    say("render tiny")
+    float32 4x64 network; both encodings, and ray counters that cross 2^32
+    inside the image."""
+    say(f"render tiny use_pi={use_pi} ray_offset={ray_offset}")
     pose = si.poses(1, seed=0, hemisphere=False)[0]
     ro, rd = gpu_rays(32, 32, 40.0, pose)
     o, d = page_rays(32, 32, 40.0, pose)
     near, far = _near_far(1024)
     params = si.nerf_params(si.NERF_4x64, seed=0)
     net = v.weights.pack_to_device(2, 0, params)
-    rgb, depth, acc, dz, dw = _render(v, 0, 2, 0, ro, rd, near, far, [net], 16)
-    ref = oren.render_nerf(o, d, near, far, params, None, 16, 0, 6, 4, seed=0)
+    rgb, depth, acc, dz, dw = _render(v, 0, 2, 0, ro, rd, near, far, [net], 16, use_pi=use_pi, ray_offset=ray_offset)
+    ref = oren.render_nerf(o, d, near, far, params, None, 16, 0, 6, 4, seed=0, use_pi=use_pi, ray_offset=ray_offset)
     assert np.array_equal(dz, ref["z_c"])
     assert max_abs(rgb, ref["rgb"]) <= RGB_TOL
     assert max_abs(acc, ref["acc"]) <= ACC_TOL
@@ -385,3 +388,57 @@ def test_render_chunk_invariance_and_determinism(v):
     c = _render(v, 0, 2, 1, ro, rd, near, far, nets, 64, 128, seed=3)
     for x, y, z in zip(a, b, c):
         assert np.array_equal(x, y) and np.array_equal(x, z)
+
+
+@pytest.mark.parametrize("use_pi", [True, False])
+def test_fused_encoding_accuracy(v, use_pi):
+    """The frequency encoding computed inside the fused render, measured
+    directly.  One sample per ray (its interval is 1e10 |d| long, so its
+    weight is exactly 1 and rgb = sigmoid(rgb_raw)) and a float32 4x64
+    network that carries three encoding columns unchanged to rgb_raw
+    (unit weights, a +2 bias that keeps them through the ReLUs, and -2 in the
+    rgb head: the only rounding is of gamma + 2, at most 1.2e-7).  gamma is
+    recovered from rgb by the logit and compared with the encoding of the
+    same points in float64."""
+    say(f"fused encoding accuracy use_pi={use_pi}")
+    from oracle import encoding as oenc
+    from oracle import sampling as osamp2
+    shape = si.NERF_4x64
+    W, D, DW = shape.width, shape.depth, shape.dir_width
+    cols = [3 + 6 * 5 + 0, 3 + 6 * 5 + 3 + 1, 3 + 6 * 2 + 2]  # sin(2^5 pi x), cos(2^5 pi y), sin(4 pi z)
+    z32 = lambda *s: np.zeros(s, np.float32)
+    layers = []
+    for l in range(D):
+        Wl = z32(W, shape.pos_ch if l == 0 else W)
+        bl = z32(W)
+        for k, c in enumerate(cols):
+            Wl[k, c if l == 0 else k] = 1.0
+        if l == 0:
+            bl[:3] = 2.0
+        layers.append((Wl, bl))
+    feat = (z32(W, W), z32(W))
+    dirl = (z32(DW, W + shape.dir_ch), z32(DW))
+    rgbl = (z32(3, DW), np.full(3, -2.0, np.float32))
+    for k in range(3):
+        feat[0][k, k] = 1.0
+        dirl[0][k, k] = 1.0
+        rgbl[0][k, k] = 1.0
+    params = {"shape": shape, "layers": layers, "sigma": (z32(1, W), np.full(1, 10.0, np.float32)), "feature": feat,
+              "dir": dirl, "rgb": rgbl}
+    net = v.weights.pack_to_device(2, 0, params)
+    H = Wd = 64
+    pose = si.poses(1, seed=5)[0]
+    ro, rd = gpu_rays(H, Wd, 60.0, pose)
+    o, d = page_rays(H, Wd, 60.0, pose)
+    near, far = _near_far(H * Wd, 1.0, 7.0)
+    rgb, _, acc, dz, _ = _render(v, 0, 2, 0, ro, rd, near, far, [net], 1, seed=9, use_pi=use_pi)
+    assert np.all(acc == 1.0)
+    x = osamp2.points(o, d, dz)  # the render's own sample depths (bit-exact with the oracle's)
+    gamma = oenc.freq_encode(x.reshape(-1, 3), 6, True, use_pi)[:, cols]
+    p = rgb.astype(np.float64)
+    got = np.log(p / (1.0 - p))
+    err = np.abs(got - gamma)
+    say(f"  max |gamma error| {err.max():.2e} (p99.9 {np.quantile(err, 0.999):.2e}) over {err.size} values")
+    # the route itself (gamma + 2 in float32, a float32 sigmoid, the logit)
+    # is good to about 4e-7, which the library sincosf (use_pi=0) shows
+    assert err.max() <= 1e-6

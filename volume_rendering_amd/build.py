@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["render_nerf_bf16.hip", "render_nerf_f32.hip", "render_hash.hip", "mlp_bf16.hip", "mlp_f32.hip",
-           "kernels.hip", "kilo.hip", "abi.cpp", "pack.cpp", "noalloc.hip", "train.hip"]
+           "kernels.hip", "kilo.hip", "abi.cpp", "pack.cpp", "layouts.cpp", "noalloc.hip", "train.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-function"]

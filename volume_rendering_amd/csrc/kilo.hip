@@ -29,7 +29,7 @@
 
 namespace nerf {
 
-constexpr int kScanBlock = 1024;  // elements per local-scan block (256 threads x 4)
+constexpr int kScanBlock = kKiloScanBlock;
 constexpr int kXcds = 8;          // accelerator complex dies; the persistent grid is a multiple
 
 // ---------------------------------------------------------------------------
@@ -484,44 +484,6 @@ __global__ void k_kilo_n_live(const uint32_t* __restrict__ ray_start, int64_t n_
 // ---------------------------------------------------------------------------
 // Workspace and launch
 // ---------------------------------------------------------------------------
-size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k) {
-    const uint64_t max_live = (uint64_t)n_rays * (uint64_t)n_samples;
-    const uint64_t max_tiles = (max_live + 31) / 32 + (uint64_t)n_cells;
-    const uint64_t nb = (uint64_t)((n_rays + kScanBlock - 1) / kScanBlock);
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = off;
-        off += (bytes + 255) / 256 * 256;
-        return at;
-    };
-    const int words = (n_samples + kWave - 1) / kWave;
-    const size_t o_mask = take(8 * (size_t)n_rays * words);
-    const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
-                 o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
-                 o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
-                 o_sl = take(4 * max_live), o_ts = take(4 * ((size_t)n_cells + 1)),
-                 o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
-                 o_raw = take(16 * max_live);
-    if (base && k) {
-        k->live_mask = (unsigned long long*)(base + o_mask);
-        k->mask_words = words;
-        k->live_count = (uint32_t*)(base + o_live);
-        k->ray_start = (uint32_t*)(base + o_start);
-        k->block_sums = (uint32_t*)(base + o_bs);
-        k->ent_ray = (uint32_t*)(base + o_er);
-        k->ent_meta = (uint32_t*)(base + o_em);
-        k->cell_count = (uint32_t*)(base + o_cc);
-        k->cell_start = (uint32_t*)(base + o_cs);
-        k->ent_slot = (uint32_t*)(base + o_sl);
-        k->tile_start = (uint32_t*)(base + o_ts);
-        k->tile_cell = (uint32_t*)(base + o_tc);
-        k->tile_off = (uint32_t*)(base + o_to);
-        k->bucket = (uint32_t*)(base + o_bk);
-        k->raw_live = (float*)(base + o_raw);
-    }
-    return off;
-}
-
 void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int add_n_live, hipStream_t s) {
     const int64_t n = a.n_rays;
     const int n_cells = k.cell_res * k.cell_res * k.cell_res;

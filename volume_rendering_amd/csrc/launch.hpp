@@ -103,6 +103,9 @@ size_t train_workspace_layout(int kind, int bf16, int64_t n_rays, int n_samples,
 int64_t train_param_count(int kind);
 void launch_train_step(int kind, int bf16, const TrainArgs& t, hipStream_t s);
 
+// Rays per local-scan block of the many-network render's prefix sums (256 threads x 4).
+constexpr int kKiloScanBlock = 1024;
+
 // Workspace layout of the many-tiny-networks render for n_rays x n_samples.
 size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k);
 

@@ -1,0 +1,102 @@
+// Workspace layouts of the many-network render and of a training step:
+// host arithmetic only, shared by the launchers and the C ABI's size queries.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "nets.hpp"
+#include "train_plan.hpp"
+
+namespace nerf {
+
+size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k) {
+    const uint64_t max_live = (uint64_t)n_rays * (uint64_t)n_samples;
+    const uint64_t max_tiles = (max_live + 31) / 32 + (uint64_t)n_cells;
+    const uint64_t nb = (uint64_t)((n_rays + kKiloScanBlock - 1) / kKiloScanBlock);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const int words = (n_samples + 63) / 64;  // 64-bit live masks, one bit per sample
+    const size_t o_mask = take(8 * (size_t)n_rays * words);
+    const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
+                 o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
+                 o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
+                 o_sl = take(4 * max_live), o_ts = take(4 * ((size_t)n_cells + 1)),
+                 o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
+                 o_raw = take(16 * max_live);
+    if (base && k) {
+        k->live_mask = (unsigned long long*)(base + o_mask);
+        k->mask_words = words;
+        k->live_count = (uint32_t*)(base + o_live);
+        k->ray_start = (uint32_t*)(base + o_start);
+        k->block_sums = (uint32_t*)(base + o_bs);
+        k->ent_ray = (uint32_t*)(base + o_er);
+        k->ent_meta = (uint32_t*)(base + o_em);
+        k->cell_count = (uint32_t*)(base + o_cc);
+        k->cell_start = (uint32_t*)(base + o_cs);
+        k->ent_slot = (uint32_t*)(base + o_sl);
+        k->tile_start = (uint32_t*)(base + o_ts);
+        k->tile_cell = (uint32_t*)(base + o_tc);
+        k->tile_off = (uint32_t*)(base + o_to);
+        k->bucket = (uint32_t*)(base + o_bk);
+        k->raw_live = (float*)(base + o_raw);
+    }
+    return off;
+}
+
+// Workspace of one step (bytes), laid out into b when base is given.
+size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, void* bufs_out) {
+    const NetPlan p = make_plan(kind);
+    const int64_t S = R * N;
+    const size_t es = bf16 ? 2 : 4;
+    TrainBufs b{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> void* {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return base ? base + at : nullptr;
+    };
+    // about 128 splits of the samples for the weight gradients (whole
+    // multiples of 64, at least 512 samples each)
+    const int64_t per = ((S + 127) / 128 + 63) / 64 * 64;
+    b.k_chunk = (int)(per > 512 ? per : 512);
+    b.splits = (int)((S + b.k_chunk - 1) / b.k_chunk);
+    b.ptr[BZ] = take(4 * (size_t)S);
+    b.ptr[BE] = take(es * (size_t)S * p.ldE);
+    b.ptr[BV] = take(es * (size_t)R * p.ldV);
+    for (int l = 0; l < p.D; ++l) b.ptr[BH0 + l] = take(es * (size_t)S * p.W);
+    b.ptr[BF] = take(es * (size_t)S * p.W);
+    b.ptr[BG] = take(es * (size_t)S * p.ldG);
+    b.ptr[BRAW] = take(16 * (size_t)S);
+    b.ptr[BDRGB] = take(es * (size_t)S * 32);
+    b.ptr[BDSIG] = take(es * (size_t)S * 32);
+    b.ptr[BDG] = take(es * (size_t)S * p.ldG);
+    b.ptr[BDF] = take(es * (size_t)S * p.W);
+    b.ptr[BDH0] = take(es * (size_t)S * p.W);
+    b.ptr[BDH1] = take(es * (size_t)S * p.W);
+    b.ptr[BSQ] = take(4 * (size_t)R);
+    b.ptr[BGRAD] = take(4 * (size_t)p.P);
+    const int maxk = p.ldE > p.W ? p.ldE : p.W;
+    b.ptr[BPART] = take(4 * (size_t)b.splits * pad32(p.W + 32) * pad32(maxk + 32));
+    b.ptr[BBPART] = take(4 * (size_t)b.splits * pad32(p.W + 32));
+    const int nl = p.D + 4;
+    const Layer* L = net_layers(kind);
+    for (int l = 0; l < nl; ++l) {
+        const int no = pad32(L[l].n_out);
+        const int k1 = L[l].s0.kind == SEG_HIDDEN ? pad32(L[l].s0.width) : p.ldE;
+        const int k2 = L[l].s1.kind == SEG_NONE ? 0 : (l == p.D + 2 ? p.ldV : p.ldE);
+        b.wf[l] = take(es * (size_t)no * (k1 + k2));
+        b.wt[l] = take(es * (size_t)k1 * no);
+        b.bias[l] = (float*)take(4 * (size_t)no);
+    }
+    b.wt_head = take(es * (size_t)p.W * (p.W + 32));
+    if (bufs_out) *static_cast<TrainBufs*>(bufs_out) = b;
+    return off;
+}
+
+int64_t train_param_count(int kind) { return make_plan(kind).P; }
+
+}  // namespace nerf

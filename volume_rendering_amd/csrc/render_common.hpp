@@ -125,7 +125,6 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
     const bool live = r0 < a.n_rays;
     const int64_t r = live ? r0 : a.n_rays - 1;
     const int lane = lane_id();
-    const int h = lane >> 5;
     const uint64_t ray = a.ray_offset + (uint64_t)r;
 
     const float o[3] = {a.ro[3 * r], a.ro[3 * r + 1], a.ro[3 * r + 2]};
@@ -315,7 +314,6 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
     const bool live = r0 < a.n_rays;
     const int64_t r = live ? r0 : a.n_rays - 1;
     const int lane = lane_id();
-    const int h = lane >> 5;
     const uint64_t ray = a.ray_offset + (uint64_t)r;
     const float o[3] = {a.ro[3 * r], a.ro[3 * r + 1], a.ro[3 * r + 2]};
     const float d[3] = {a.rd[3 * r], a.rd[3 * r + 1], a.rd[3 * r + 2]};

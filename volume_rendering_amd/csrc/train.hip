@@ -24,6 +24,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "nets.hpp"
+#include "train_plan.hpp"
 
 namespace nerf {
 
@@ -724,116 +725,7 @@ __global__ void __launch_bounds__(256) k_adam(float* __restrict__ p, float* __re
     p[i] -= lr * (mi * c1) / (sqrtf(vi * c2) + eps);
 }
 
-// ---------------------------------------------------------------------------
-// Network plan
-// ---------------------------------------------------------------------------
-int pad32(int n) { return (n + 31) / 32 * 32; }
-
-// Buffers of a step (ids into TrainBufs::ptr).
-enum : int { BZ = 0, BE, BV, BF, BG, BRAW, BDRGB, BDSIG, BDG, BDF, BDH0, BDH1, BSQ, BGRAD, BPART, BBPART, BH0 };
-
-struct NetPlan {
-    int D, W, skip, Lpos, Ldir, DW;
-    int pe, de, ldE, ldV, ldG;
-    // flat offsets of each layer's weights and biases, and its input width
-    int64_t w_off[16], b_off[16];
-    int in_total[16];
-    int64_t P;  // parameters
-};
-
-NetPlan make_plan(int kind) {
-    NetPlan p{};
-    const Layer* L = net_layers(kind);
-    const int nl = net_n_layers(kind);
-    p.D = nl - 4;
-    p.W = L[0].n_out;
-    p.skip = -1;
-    for (int l = 1; l < p.D; ++l)
-        if (L[l].s1.kind == SEG_ENC) p.skip = l - 1;
-    p.Lpos = L[0].s0.L;
-    p.Ldir = L[p.D + 2].s1.L;
-    p.DW = L[p.D + 2].n_out;
-    p.pe = 3 + 6 * p.Lpos;
-    p.de = 3 + 6 * p.Ldir;
-    p.ldE = pad32(p.pe);
-    p.ldV = pad32(p.de);
-    p.ldG = pad32(p.DW);
-    int64_t off = 0;
-    for (int l = 0; l < nl; ++l) {
-        p.in_total[l] = L[l].s0.width + L[l].s1.width;
-        p.w_off[l] = off;
-        off += (int64_t)L[l].n_out * p.in_total[l];
-        p.b_off[l] = off;
-        off += L[l].n_out;
-    }
-    p.P = off;
-    return p;
-}
-
-struct TrainBufs {
-    void* ptr[BH0 + 16];
-    int splits, k_chunk;
-    // weights: forward matrices, transposed matrices, biases (per layer), the
-    // combined feature+density transpose
-    void* wf[16];
-    void* wt[16];
-    float* bias[16];
-    void* wt_head;
-};
-
 }  // namespace
-
-// Workspace of one step (bytes), laid out into b when base is given.
-size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, void* bufs_out) {
-    const NetPlan p = make_plan(kind);
-    const int64_t S = R * N;
-    const size_t es = bf16 ? 2 : 4;
-    TrainBufs b{};
-    size_t off = 0;
-    auto take = [&](size_t bytes) -> void* {
-        const size_t at = off;
-        off += (bytes + 255) / 256 * 256;
-        return base ? base + at : nullptr;
-    };
-    // about 128 splits of the samples for the weight gradients (whole
-    // multiples of 64, at least 512 samples each)
-    const int64_t per = ((S + 127) / 128 + 63) / 64 * 64;
-    b.k_chunk = (int)(per > 512 ? per : 512);
-    b.splits = (int)((S + b.k_chunk - 1) / b.k_chunk);
-    b.ptr[BZ] = take(4 * (size_t)S);
-    b.ptr[BE] = take(es * (size_t)S * p.ldE);
-    b.ptr[BV] = take(es * (size_t)R * p.ldV);
-    for (int l = 0; l < p.D; ++l) b.ptr[BH0 + l] = take(es * (size_t)S * p.W);
-    b.ptr[BF] = take(es * (size_t)S * p.W);
-    b.ptr[BG] = take(es * (size_t)S * p.ldG);
-    b.ptr[BRAW] = take(16 * (size_t)S);
-    b.ptr[BDRGB] = take(es * (size_t)S * 32);
-    b.ptr[BDSIG] = take(es * (size_t)S * 32);
-    b.ptr[BDG] = take(es * (size_t)S * p.ldG);
-    b.ptr[BDF] = take(es * (size_t)S * p.W);
-    b.ptr[BDH0] = take(es * (size_t)S * p.W);
-    b.ptr[BDH1] = take(es * (size_t)S * p.W);
-    b.ptr[BSQ] = take(4 * (size_t)R);
-    b.ptr[BGRAD] = take(4 * (size_t)p.P);
-    const int maxk = p.ldE > p.W ? p.ldE : p.W;
-    b.ptr[BPART] = take(4 * (size_t)b.splits * pad32(p.W + 32) * pad32(maxk + 32));
-    b.ptr[BBPART] = take(4 * (size_t)b.splits * pad32(p.W + 32));
-    const int nl = p.D + 4;
-    const Layer* L = net_layers(kind);
-    for (int l = 0; l < nl; ++l) {
-        const int no = pad32(L[l].n_out);
-        const int k1 = L[l].s0.kind == SEG_HIDDEN ? pad32(L[l].s0.width) : p.ldE;
-        const int k2 = L[l].s1.kind == SEG_NONE ? 0 : (l == p.D + 2 ? p.ldV : p.ldE);
-        b.wf[l] = take(es * (size_t)no * (k1 + k2));
-        b.wt[l] = take(es * (size_t)k1 * no);
-        b.bias[l] = (float*)take(4 * (size_t)no);
-    }
-    b.wt_head = take(es * (size_t)p.W * (p.W + 32));
-    if (bufs_out) *static_cast<TrainBufs*>(bufs_out) = b;
-    return off;
-}
-
-int64_t train_param_count(int kind) { return make_plan(kind).P; }
 
 namespace {
 
