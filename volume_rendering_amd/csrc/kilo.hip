@@ -8,18 +8,17 @@
 //   count     one wave per ray: stratified samples, box and occupancy test,
 //             live-sample mask and number of live samples per ray
 //   scan      exclusive prefix sum of the counts (ray start offsets)
-//   compact   one wave per ray, one lane per live sample (from the mask):
-//             live samples written in (ray, sample) order
-//             with their cell id; per-cell histogram, whose running counts
-//             give each sample its slot in the cell's bucket
-//   cells     one workgroup: per-cell start offsets and tile offsets
-//   scatter   the tile list, and live samples into per-cell buckets (bucket
-//             order within a cell is arbitrary: each sample is its own matrix
-//             column and writes only its own entry)
-//   mlp       persistent waves over the tile list: each tile is up to 64
-//             (bf16) or 32 (f32) samples of one cell, evaluated by that
-//             cell's network read straight from global memory
-//   composite one wave per ray over its live samples in order (dead ones
+//   compact   32 rays per workgroup, one thread per live sample: live
+//             samples written in (ray, sample) order with their cell id and
+//             their rank among the workgroup's samples of that cell
+//   cells     one workgroup: per-cell start offsets
+//   scatter   live samples into per-cell buckets, as (point, entry, view
+//             direction) records (bucket order within a cell is arbitrary:
+//             each sample is its own matrix column and writes only its own
+//             entry)
+//   mlp       one workgroup per cell: the cell's network copied into LDS
+//             once, then tiles of 64 (bf16) or 32 (f32) of its samples
+//   composite 16 lanes per ray over its live samples in order (dead ones
 //             change nothing), stop at the first with transmittance below term_T
 #include <hip/hip_runtime.h>
 
@@ -30,7 +29,6 @@
 namespace nerf {
 
 constexpr int kScanBlock = kKiloScanBlock;
-constexpr int kXcds = 8;          // accelerator complex dies; the persistent grid is a multiple
 
 // ---------------------------------------------------------------------------
 // Scans
@@ -214,78 +212,69 @@ __global__ void __launch_bounds__(256) k_kilo_count(RenderArgs a, KiloArgs k) {
 
 constexpr int kKiloMaxSamples = 256;
 
-// Compact: a workgroup takes kCompactRays consecutive rays (each wave
-// kCompactRays/4 of them in turn), one lane per live sample.  Cell counts
-// are first aggregated in an LDS hash table (one LDS atomic per distinct
-// cell of a wave); each used entry then takes one device-scope atomic for
-// its base in the cell's bucket, and a last pass over the workgroup's
-// (contiguous) entries turns (entry, local rank) into bucket slots.  A
-// sample that finds the table full takes its global slot directly (flagged
-// in bit 31).
+// Compact: a workgroup takes kCompactRays consecutive rays, whose live
+// samples are the contiguous entries [ray_start[r0], ray_start[r1]).  Each
+// wave first lists the live samples of its rays into LDS (ray, sample), in
+// order; then every thread takes one entry: its point, its cell, and its
+// rank among the workgroup's samples of that cell, from an LDS hash table
+// of per-cell counters (one LDS atomic per sample).  Each used table entry
+// then takes one device-scope atomic for its base in the cell's bucket, and
+// a last pass turns (entry, local rank) into bucket slots.  A sample that
+// finds the table full takes its global slot directly (flagged in bit 31).
 constexpr int kCompactRays = 32;
 constexpr int kCellTable = 1024;  // power of two
 constexpr uint32_t kSlotFinal = 0x80000000u;
 
 __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) {
-    __shared__ int lists[4][kKiloMaxSamples];
+    __shared__ uint16_t ents[kCompactRays * kKiloMaxSamples];  // (ray - r0) << 8 | sample
     __shared__ int keys[kCellTable];
     __shared__ uint32_t counts[kCellTable];
     for (int i = threadIdx.x; i < kCellTable; i += blockDim.x) {
         keys[i] = -1;
         counts[i] = 0u;
     }
-    __syncthreads();
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     const unsigned long long below = (1ull << lane) - 1ull;
-    int* idx = lists[wave];
     const int64_t r0 = (int64_t)blockIdx.x * kCompactRays;
+    const int64_t r1 = r0 + kCompactRays < a.n_rays ? r0 + kCompactRays : a.n_rays;
+    const uint32_t e0 = k.ray_start[r0], e1 = k.ray_start[r1];
     for (int j = 0; j < kCompactRays / 4; ++j) {
         const int64_t r = r0 + wave * (kCompactRays / 4) + j;
-        if (r >= a.n_rays) break;
-        const RayIn R = load_ray(a, r);
-        const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
-        const uint32_t pos = k.ray_start[r];
-        for (int base = 0; base < nlive; base += kWave) {
-            const int q = base + lane;
-            const bool live = q < nlive;
-            int cell = 0, i = 0;
-            if (live) {
-                i = idx[q];
-                float x[3];
-                sample_point(a, R, r, i, x);
-                cell = cell_of(k, x);
-            }
-            uint32_t slot = 0;
-            for (unsigned long long rem = __ballot(live); rem;) {
-                const int leader = __ffsll((long long)rem) - 1;
-                const int c = __shfl(cell, leader, kWave);
-                const unsigned long long same = __ballot(live && cell == c);
-                uint32_t b = 0;
-                if (lane == leader) {
-                    const uint32_t n = (uint32_t)__popcll(same);
-                    int h = (int)(((uint32_t)c * 2654435761u) >> 22) & (kCellTable - 1);
-                    int probes = 0;
-                    for (; probes < kCellTable; ++probes, h = (h + 1) & (kCellTable - 1)) {
-                        const int prev = atomicCAS(&keys[h], -1, c);
-                        if (prev == -1 || prev == c) break;
-                    }
-                    if (probes < kCellTable)
-                        b = ((uint32_t)h << 20) | atomicAdd(&counts[h], n);
-                    else
-                        b = kSlotFinal | atomicAdd(&k.cell_count[c], n);
-                }
-                b = __shfl(b, leader, kWave);
-                if ((same >> lane) & 1ull) slot = b + (uint32_t)__popcll(same & below);
-                rem &= ~same;
-            }
-            if (live) {
-                const uint32_t e = pos + (uint32_t)q;
-                k.ent_ray[e] = (uint32_t)r;
-                k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
-                k.ent_slot[e] = slot;
-            }
+        if (r >= r1) break;
+        const unsigned long long* mask = k.live_mask + r * k.mask_words;
+        uint32_t c = k.ray_start[r] - e0;
+        for (int w = 0; w < k.mask_words; ++w) {
+            const unsigned long long mw = mask[w];
+            if ((mw >> lane) & 1ull)
+                ents[c + __popcll(mw & below)] = (uint16_t)(((uint32_t)(r - r0) << 8) | (uint32_t)(kWave * w + lane));
+            c += (uint32_t)__popcll(mw);
         }
+    }
+    __syncthreads();
+    for (uint32_t q = threadIdx.x; q < e1 - e0; q += blockDim.x) {
+        const uint32_t pk = ents[q];
+        const int64_t r = r0 + (pk >> 8);
+        const int i = (int)(pk & 0xFFu);
+        const RayIn R = load_ray(a, r);
+        float x[3];
+        sample_point(a, R, r, i, x);
+        const int cell = cell_of(k, x);
+        uint32_t slot = 0;
+        int h = (int)(((uint32_t)cell * 2654435761u) >> 22) & (kCellTable - 1);
+        int probes = 0;
+        for (; probes < kCellTable; ++probes, h = (h + 1) & (kCellTable - 1)) {
+            const int prev = atomicCAS(&keys[h], -1, cell);
+            if (prev == -1 || prev == cell) break;
+        }
+        if (probes < kCellTable)
+            slot = ((uint32_t)h << 20) | atomicAdd(&counts[h], 1u);
+        else
+            slot = kSlotFinal | atomicAdd(&k.cell_count[cell], 1u);
+        const uint32_t e = e0 + q;
+        k.ent_ray[e] = (uint32_t)r;
+        k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
+        k.ent_slot[e] = slot;
     }
     __syncthreads();
     // one device-scope atomic per used table entry: its base in the bucket
@@ -294,107 +283,132 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
         if (c >= 0) counts[h] = atomicAdd(&k.cell_count[c], counts[h]);
     }
     __syncthreads();
-    const int64_t r1 = r0 + kCompactRays < a.n_rays ? r0 + kCompactRays : a.n_rays;
-    const uint32_t e0 = k.ray_start[r0], e1 = k.ray_start[r1];
     for (uint32_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
         const uint32_t t = k.ent_slot[e];
         k.ent_slot[e] = (t & kSlotFinal) ? (t & ~kSlotFinal) : counts[t >> 20] + (t & 0xFFFFFu);
     }
 }
 
-// One workgroup of 1024 threads: cell start offsets and tile offsets.
-__global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells, int tile) {
+// One workgroup of 1024 threads: cell start offsets (exclusive scan of the
+// per-cell counts; entry n_cells is the total).
+__global__ void __launch_bounds__(1024) k_kilo_cells(KiloArgs k, int n_cells) {
     __shared__ uint32_t lds[17];
-    uint32_t carry_s = 0, carry_t = 0;
+    uint32_t carry = 0;
     for (int c0 = 0; c0 < n_cells; c0 += blockDim.x) {
         const int c = c0 + threadIdx.x;
         const uint32_t cnt = c < n_cells ? k.cell_count[c] : 0u;
-        const uint32_t nt = (cnt + tile - 1) / tile;
-        uint32_t ts, tt;
-        const uint32_t es = block_excl_scan(cnt, lds, ts);
-        const uint32_t et = block_excl_scan(nt, lds, tt);
-        if (c < n_cells) {
-            k.cell_start[c] = carry_s + es;
-            k.tile_start[c] = carry_t + et;
-        }
-        carry_s += ts;
-        carry_t += tt;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(cnt, lds, tot);
+        if (c < n_cells) k.cell_start[c] = carry + ex;
+        carry += tot;
     }
-    if (threadIdx.x == 0) {
-        k.cell_start[n_cells] = carry_s;
-        k.tile_start[n_cells] = carry_t;
-    }
+    if (threadIdx.x == 0) k.cell_start[n_cells] = carry;
 }
 
-// Grid-wide: live samples into their cells' buckets, and the tile list
-// (tile t belongs to the cell c with tile_start[c] <= t < tile_start[c+1],
-// found by binary search).
-__global__ void __launch_bounds__(256) k_kilo_scatter(KiloArgs k, int64_t n_rays, int n_cells, int tile) {
-    const uint32_t total = k.ray_start[n_rays];
+// Grid-wide: live samples into their cells' buckets.  A bucket slot holds
+// what the cell network needs, so that a tile's inputs are one contiguous
+// read: (x, y, z, entry index) and the ray's unit direction.
+__global__ void __launch_bounds__(256) k_kilo_scatter(RenderArgs a, KiloArgs k) {
+    const uint32_t total = k.ray_start[a.n_rays];
     const uint32_t stride = gridDim.x * blockDim.x;
-    const uint32_t t_id = blockIdx.x * blockDim.x + threadIdx.x;
-    for (uint32_t e = t_id; e < total; e += stride) {
-        const uint32_t c = k.ent_meta[e] & 0xFFFFu;
-        k.bucket[k.cell_start[c] + k.ent_slot[e]] = e;
-    }
-    const uint32_t n_tiles = k.tile_start[n_cells];
-    for (uint32_t t = t_id; t < n_tiles; t += stride) {
-        int lo = 0, hi = n_cells;  // largest c with tile_start[c] <= t
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (k.tile_start[mid] <= t)
-                lo = mid;
-            else
-                hi = mid;
-        }
-        k.tile_cell[t] = (uint32_t)lo;
-        k.tile_off[t] = (t - k.tile_start[lo]) * (uint32_t)tile;
+    for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const uint32_t meta = k.ent_meta[e], r = k.ent_ray[e];
+        const RayIn R = load_ray(a, r);
+        float x[3];
+        sample_point(a, R, r, (int)(meta >> 16), x);
+        const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
+        f32x4* slot = reinterpret_cast<f32x4*>(k.bucket) + 2 * (size_t)(k.cell_start[meta & 0xFFFFu] + k.ent_slot[e]);
+        slot[0] = f32x4{x[0], x[1], x[2], __uint_as_float(e)};
+        slot[1] = f32x4{R.d[0] / dn, R.d[1] / dn, R.d[2] / dn, 0.0f};
     }
 }
 
-// Persistent waves over the tile list: tile t holds samples
-// [tile_off, tile_off + 32*SB) of its cell's bucket.
+// A network held in LDS for the whole workgroup: the weight tiles are read
+// with the same look-ahead as a stream from global memory.
+template <class T, int KIND, int LOOK = 3>
+struct LdsResident {
+    using Op = typename T::Op;
+    static constexpr int TB = tile_bytes(T::prec);
+    static constexpr int NT = (int)(net_tiles_bytes(KIND, T::prec) / TB);
+    const NERF_AS_LDS char* base;  // this lane's bytes of tile 0
+    Op buf[LOOK];
+    __device__ __forceinline__ LdsResident(const NERF_AS_LDS char* tiles, int lane)
+        : base(tiles + lane * (int)sizeof(Op)) {}
+    template <int TILE>
+    __device__ __forceinline__ Op read() const {
+        return *reinterpret_cast<const NERF_AS_LDS Op*>(base + TILE * TB);
+    }
+    __device__ __forceinline__ void begin() {
+        static_for<0, LOOK>([&](auto t) {
+            if constexpr (t.value < NT) buf[t.value] = read<t.value>();
+        });
+    }
+    template <int TILE>
+    __device__ __forceinline__ Op get() {
+        const Op cur = buf[TILE % LOOK];
+        if constexpr (TILE + LOOK < NT) buf[TILE % LOOK] = read<TILE + LOOK>();
+        return cur;
+    }
+};
+
+// One workgroup per cell: the cell's packed network (tiles and biases) is
+// copied into LDS once, then the four waves take the cell's tiles of 32*SB
+// bucketed samples in turn.
 template <class T>
-__global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int n_cells) {
+__global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k) {
     constexpr int K = NET_CELL_2x32;
     constexpr int SB = T::SB;
     constexpr int ES = seg_steps(net_layers(K)[0].s0, T::prec);
     constexpr int DS = seg_steps(net_layers(K)[4].s1, T::prec);
+    constexpr int NET_BYTES = (int)net_packed_bytes(K, T::prec);
+    static_assert(NET_BYTES % 16 == 0, "16-byte copies");
+    __shared__ __attribute__((aligned(16))) char net[NET_BYTES];
+    const uint32_t c = blockIdx.x;
+    const uint32_t cs = k.cell_start[c], cnt = k.cell_start[c + 1] - cs;
+    if (cnt == 0) return;
+    const char* packed = (const char*)k.cells + (size_t)c * k.cell_stride;
+    for (int o = threadIdx.x * 16; o < NET_BYTES; o += blockDim.x * 16)
+        *reinterpret_cast<f32x4*>(net + o) = *reinterpret_cast<const f32x4*>(packed + o);
+    __syncthreads();
+    const NERF_AS_LDS char* lnet = (const NERF_AS_LDS char*)net;
+    const NERF_AS_LDS float* bias = (const NERF_AS_LDS float*)(lnet + net_bias_offset(K, T::prec, 0));
     const int lane = lane_id();
-    // The tile list is cell-major.  Workgroups are dealt to the 8 XCDs
-    // round robin (blockIdx % 8), so XCD x takes the x-th eighth of the list:
-    // the tiles of one cell then run on one XCD, close together in time, and
-    // that cell's network is fetched into one L2 once.
-    const uint32_t total_tiles = k.tile_start[n_cells];
-    const uint32_t xcd = blockIdx.x % kXcds, bx = blockIdx.x / kXcds;
-    const uint32_t t_end = (uint32_t)((uint64_t)total_tiles * (xcd + 1) / kXcds);
-    const uint32_t nwaves = gridDim.x / kXcds * (blockDim.x / kWave);
-    for (uint32_t t = (uint32_t)((uint64_t)total_tiles * xcd / kXcds) + bx * (blockDim.x / kWave) + threadIdx.x / kWave;
-         t < t_end; t += nwaves) {
-        const uint32_t c = k.tile_cell[t], off = k.tile_off[t];
-        const uint32_t cs = k.cell_start[c], cnt = k.cell_start[c + 1] - cs;
-        uint32_t e[SB];
-        bool valid[SB];
-        float x[SB][3], v[SB][3];
+    const uint32_t n_tiles = (cnt + 32 * SB - 1) / (32 * SB);
+    const f32x4* slots = reinterpret_cast<const f32x4*>(k.bucket) + 2 * (size_t)cs;
+    // a tile's bucket slots, read one tile ahead of their use
+    auto fetch = [&](uint32_t t, f32x4 (&p)[SB], f32x4 (&q)[SB]) {
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            const uint32_t j = off + sb * 32 + (lane & 31);
-            valid[sb] = j < cnt;
-            e[sb] = k.bucket[cs + (valid[sb] ? j : off)];
-            const uint32_t r = k.ent_ray[e[sb]];
-            const int i = (int)(k.ent_meta[e[sb]] >> 16);
-            const RayIn R = load_ray(a, r);
-            sample_point(a, R, r, i, x[sb]);
-            const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
+            const uint32_t j = t * 32 * SB + sb * 32 + (lane & 31);
+            const uint32_t jj = j < cnt ? j : cnt - 1;
+            p[sb] = slots[2 * jj];
+            q[sb] = slots[2 * jj + 1];
+        }
+    };
+    constexpr uint32_t kWaves = 256 / kWave;
+    uint32_t t = threadIdx.x / kWave;
+    f32x4 p[SB], q[SB];
+    if (t < n_tiles) fetch(t, p, q);
+    for (; t < n_tiles; t += kWaves) {
+        f32x4 pn[SB], qn[SB];
+        if (t + kWaves < n_tiles) fetch(t + kWaves, pn, qn);
+        float x[SB][3], v[SB][3];
+        uint32_t e[SB];
+        bool valid[SB];
 #pragma unroll
-            for (int q = 0; q < 3; ++q) v[sb][q] = R.d[q] / dn;
+        for (int sb = 0; sb < SB; ++sb) {
+            valid[sb] = t * 32 * SB + sb * 32 + (lane & 31) < cnt;
+            e[sb] = __float_as_uint(p[sb][3]);
+#pragma unroll
+            for (int c3 = 0; c3 < 3; ++c3) {
+                x[sb][c3] = p[sb][c3];
+                v[sb][c3] = q[sb][c3];
+            }
         }
         typename T::Op enc[ES][SB], denc[DS][SB];
         enc_operands<10>(enc, x, a.use_pi != 0, lane);
         enc_operands<4>(denc, v, a.use_pi != 0, lane);
-        const char* packed = (const char*)k.cells + (size_t)c * k.cell_stride;
-        GlobalStream<T, K> ws(packed, lane, 0);
-        const float* bias = (const float*)(packed + net_bias_offset(K, T::prec, 0));
+        LdsResident<T, K> ws(lnet, lane);
         f32x16 sig[SB], rgb[SB];
         nerf_forward<T, K>(enc, denc, ws, bias, sig, rgb, lane);
         if (lane < 32) {
@@ -404,53 +418,93 @@ __global__ void __launch_bounds__(256) k_kilo_mlp(RenderArgs a, KiloArgs k, int 
                     reinterpret_cast<f32x4*>(k.raw_live)[e[sb]] =
                         f32x4{rgb[sb][0], rgb[sb][1], rgb[sb][2], sig[sb][0]};
         }
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+            p[sb] = pn[sb];
+            q[sb] = qn[sb];
+        }
     }
 }
 
-// One wave per ray, over its live samples only: a dead sample has density 0,
-// so its weight is 0 and its survival factor 1 - 0 + 1e-10 rounds to 1 in
-// float32 - skipping it changes no product.  A live sample's interval needs
-// the depth of the next sample, live or not (recomputed from its counter).
+// Sixteen lanes per ray (four rays per wave), over its live samples only: a
+// dead sample has density 0, so its weight is 0 and its survival factor
+// 1 - 0 + 1e-10 rounds to 1 in float32 - skipping it changes no product.  A
+// live sample's interval needs the depth of the next sample, live or not
+// (recomputed from its counter).  Transmittance is a 16-lane product scan
+// per chunk of live samples, carried across chunks.
+constexpr int kRowLanes = 16;
+
+__device__ __forceinline__ float row_scan_mul(float v, int j) {
+#pragma unroll
+    for (int off = 1; off < kRowLanes; off <<= 1) {
+        const float o = __shfl_up(v, off, kRowLanes);
+        if (j >= off) v *= o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+    for (int off = kRowLanes / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kRowLanes);
+    return v;
+}
+
 __global__ void __launch_bounds__(256) k_kilo_composite(RenderArgs a, KiloArgs k) {
-    __shared__ int lists[4][kKiloMaxSamples];
-    const int wave = threadIdx.x / kWave;
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r >= a.n_rays) return;
-    const RayIn R = load_ray(a, r);
+    constexpr int RAYS = 256 / kRowLanes;
+    __shared__ uint8_t lists[RAYS][kKiloMaxSamples];
     const int lane = lane_id();
+    const int row = lane / kRowLanes, j = lane % kRowLanes;
+    const int slot = (int)(threadIdx.x / kRowLanes);
+    const int64_t r_raw = (int64_t)blockIdx.x * RAYS + slot;
+    const bool ray_ok = r_raw < a.n_rays;
+    const int64_t r = ray_ok ? r_raw : a.n_rays - 1;  // a row past the last ray repeats it and stores nothing
+    const RayIn R = load_ray(a, r);
     const int N = a.n_coarse;
     const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
-    if (a.dbg_z)
-        for (int i = lane; i < N; i += kWave) a.dbg_z[r * N + i] = sample_z(a, R, r, i);
-    int* idx = lists[wave];
-    const int nlive = live_list(k.live_mask + r * k.mask_words, k.mask_words, idx);
+    if (a.dbg_z && ray_ok)
+        for (int i = j; i < N; i += kRowLanes) a.dbg_z[r * N + i] = sample_z(a, R, r, i);
+    // the ray's live samples, in order: lane j of the row takes bits 4j..4j+3 of each mask word
+    uint8_t* list = lists[slot];
+    const unsigned long long* mask = k.live_mask + r * k.mask_words;
+    int nlive = 0;
+    for (int w = 0; w < k.mask_words; ++w) {
+        const unsigned long long mw = mask[w];
+        const uint32_t sub = (uint32_t)(mw >> (4 * j)) & 0xFu;
+        int at = nlive + __popcll(mw & ((1ull << (4 * j)) - 1ull));
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if ((sub >> b) & 1u) list[at++] = (uint8_t)(kWave * w + 4 * j + b);
+        nlive += __popcll(mw);
+    }
+    wave_lds_sync();
     const f32x4* raw = reinterpret_cast<const f32x4*>(k.raw_live) + k.ray_start[r];
     float carry = 1.0f, sr = 0.f, sg = 0.f, sbl = 0.f, sd = 0.f, sa = 0.f;
     bool stopped = false;
-    for (int base = 0; base < nlive; base += kWave) {
-        const int q = base + lane;
-        const bool valid = q < nlive;
+    for (int base = 0; __ballot(base < nlive && !stopped); base += kRowLanes) {
+        const int q = base + j;
+        const bool valid = q < nlive && !stopped;
         float alpha = 0.f, zi = 0.f;
         f32x4 rw = {0.f, 0.f, 0.f, 0.f};
         if (valid) {
-            const int i = idx[q];
+            const int i = list[q];
             zi = sample_z(a, R, r, i);
             const float delta = (i + 1 < N) ? (sample_z(a, R, r, i + 1) - zi) * dn : 1e10f * dn;
             rw = raw[q];
             alpha = 1.0f - expf(-fmaxf(rw[3], 0.0f) * delta);
         }
         const float surv = valid ? (1.0f - alpha + 1e-10f) : 1.0f;
-        const float incl = wave_scan_mul(surv);
-        float excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 1.0f;
+        const float incl = row_scan_mul(surv, j);
+        float excl = __shfl_up(incl, 1, kRowLanes);
+        if (j == 0) excl = 1.0f;
         const float T = carry * excl;
         bool stop_here = false;
         if (k.term_T > 0.0f) {
             // the first live sample (in order) with T < term_T and all later ones are dropped
             const unsigned long long m = __ballot(valid && T < k.term_T);
-            const int first = m ? __builtin_ctzll(m) : kWave;
-            stop_here = stopped || (lane >= first);
-            if (m) stopped = true;
+            const uint32_t mrow = (uint32_t)(m >> (kRowLanes * row)) & 0xFFFFu;
+            const int first = mrow ? __builtin_ctz(mrow) : kRowLanes;
+            stop_here = j >= first;
+            if (mrow) stopped = true;
         }
         const float w = (valid && !stop_here) ? T * alpha : 0.0f;
         sa += w;
@@ -458,15 +512,14 @@ __global__ void __launch_bounds__(256) k_kilo_composite(RenderArgs a, KiloArgs k
         sr += w * sigmoidf_(rw[0]);
         sg += w * sigmoidf_(rw[1]);
         sbl += w * sigmoidf_(rw[2]);
-        carry *= __shfl(incl, kWave - 1, kWave);
-        if (stopped) break;
+        carry *= __shfl(incl, kRowLanes - 1, kRowLanes);
     }
-    sr = wave_sum(sr);
-    sg = wave_sum(sg);
-    sbl = wave_sum(sbl);
-    sd = wave_sum(sd);
-    sa = wave_sum(sa);
-    if (lane == 0) {
+    sr = row_sum(sr);
+    sg = row_sum(sg);
+    sbl = row_sum(sbl);
+    sd = row_sum(sd);
+    sa = row_sum(sa);
+    if (j == 0 && ray_ok) {
         const float bg = a.white ? 1.0f - sa : 0.0f;
         a.rgb[3 * r] = sr + bg;
         a.rgb[3 * r + 1] = sg + bg;
@@ -497,15 +550,13 @@ void launch_render_kilo(int bf16, const RenderArgs& a, const KiloArgs& k, int ad
     hipLaunchKernelGGL(k_scan_add, dim3((unsigned)((n + 1 + 255) / 256)), dim3(256), 0, s, k.ray_start, n,
                        k.block_sums, nb);
     hipLaunchKernelGGL(k_kilo_compact, dim3((unsigned)((n + kCompactRays - 1) / kCompactRays)), dim3(256), 0, s, a, k);
-    const int tile = bf16 ? 64 : 32;
-    hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells, tile);
-    hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, k, n, n_cells, tile);
-    const dim3 persist(256 * 16);  // a multiple of kXcds (the tile partition)
+    hipLaunchKernelGGL(k_kilo_cells, dim3(1), dim3(1024), 0, s, k, n_cells);
+    hipLaunchKernelGGL(k_kilo_scatter, dim3(2048), dim3(256), 0, s, a, k);
     if (bf16)
-        hipLaunchKernelGGL(k_kilo_mlp<TBF16>, persist, dim3(256), 0, s, a, k, n_cells);
+        hipLaunchKernelGGL(k_kilo_mlp<TBF16>, dim3((unsigned)n_cells), dim3(256), 0, s, a, k);
     else
-        hipLaunchKernelGGL(k_kilo_mlp<TF32>, persist, dim3(256), 0, s, a, k, n_cells);
-    hipLaunchKernelGGL(k_kilo_composite, rays4, dim3(256), 0, s, a, k);
+        hipLaunchKernelGGL(k_kilo_mlp<TF32>, dim3((unsigned)n_cells), dim3(256), 0, s, a, k);
+    hipLaunchKernelGGL(k_kilo_composite, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s, a, k);
     if (k.dbg_n_live)
         hipLaunchKernelGGL(k_kilo_n_live, dim3(1), dim3(64), 0, s, k.ray_start, n, k.dbg_n_live, add_n_live);
 }

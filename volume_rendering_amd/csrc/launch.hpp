@@ -69,10 +69,8 @@ struct KiloArgs {
     uint32_t* ent_slot;    // [max_live]: place in the cell's bucket
     uint32_t* cell_count;  // [n_cells]
     uint32_t* cell_start;  // [n_cells + 1]
-    uint32_t* tile_start;  // [n_cells + 1]
-    uint32_t* tile_cell;   // [max_tiles]
-    uint32_t* tile_off;    // [max_tiles]
-    uint32_t* bucket;      // [max_live]
+    float* bucket;         // [max_live][8]: per bucket slot, the sample's point, its entry index
+                           // (bits of a float) and its unit view direction
     float* raw_live;       // [max_live, 4]
 };
 

@@ -11,7 +11,6 @@ namespace nerf {
 
 size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* base, KiloArgs* k) {
     const uint64_t max_live = (uint64_t)n_rays * (uint64_t)n_samples;
-    const uint64_t max_tiles = (max_live + 31) / 32 + (uint64_t)n_cells;
     const uint64_t nb = (uint64_t)((n_rays + kKiloScanBlock - 1) / kKiloScanBlock);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -24,9 +23,7 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
     const size_t o_live = take(4 * (size_t)n_rays), o_start = take(4 * ((size_t)n_rays + 1)),
                  o_bs = take(4 * (nb + 1)), o_er = take(4 * max_live), o_em = take(4 * max_live),
                  o_cc = take(4 * (size_t)n_cells), o_cs = take(4 * ((size_t)n_cells + 1)),
-                 o_sl = take(4 * max_live), o_ts = take(4 * ((size_t)n_cells + 1)),
-                 o_tc = take(4 * max_tiles), o_to = take(4 * max_tiles), o_bk = take(4 * max_live),
-                 o_raw = take(16 * max_live);
+                 o_sl = take(4 * max_live), o_bk = take(32 * max_live), o_raw = take(16 * max_live);
     if (base && k) {
         k->live_mask = (unsigned long long*)(base + o_mask);
         k->mask_words = words;
@@ -38,10 +35,7 @@ size_t kilo_workspace_layout(int64_t n_rays, int n_samples, int n_cells, char* b
         k->cell_count = (uint32_t*)(base + o_cc);
         k->cell_start = (uint32_t*)(base + o_cs);
         k->ent_slot = (uint32_t*)(base + o_sl);
-        k->tile_start = (uint32_t*)(base + o_ts);
-        k->tile_cell = (uint32_t*)(base + o_tc);
-        k->tile_off = (uint32_t*)(base + o_to);
-        k->bucket = (uint32_t*)(base + o_bk);
+        k->bucket = (float*)(base + o_bk);
         k->raw_live = (float*)(base + o_raw);
     }
     return off;
