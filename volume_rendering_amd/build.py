@@ -60,6 +60,13 @@ def build(verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # a kernel whose host-side launch stub the compiler did not emit (e.g. a
+    # target-only builtin in code the host pass also sees) links fine and
+    # fails only when the library is loaded: refuse such a library here
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in und.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernels without host launch stubs:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -23,6 +23,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mlp.hpp"
 #include "nets.hpp"
 #include "train_plan.hpp"
 
@@ -322,7 +323,7 @@ __global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
                         float v[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            v[e] = acc[i][j][4 * gq + e] + (g.bias ? g.bias[n + e] : 0.0f);
+                            v[e] = acc[i][j][4 * gq + e] + (g.bias && n < g.N ? g.bias[n + e] : 0.0f);
                             if (g.relu) v[e] = fmaxf(v[e], 0.0f);
                         }
                         store4<T>(st + ml * SP + wr * FW + fl, v);
@@ -380,6 +381,177 @@ __global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
                 }
             }
         }
+    }
+}
+
+// Forward and input-gradient products in bfloat16 with the operand tiles
+// copied global -> LDS by direct buffer loads (no register staging), three
+// k-steps deep: while step t multiplies, steps t+1 and t+2 are in flight.
+// A tile row is 64 bytes (32 k) whose four 16-byte pieces are XOR-swizzled
+// by row, so that the operand reads (32 rows at one k offset) fall in
+// distinct banks.  Each copy instruction fills 1 KB of LDS (16 rows); rows
+// past the matrix get an out-of-range offset and read as zero.
+constexpr int kDmaStages = 3;
+constexpr uint32_t kDmaSkip = 0x7FFFF000u;  // offset beyond any tile: the copy reads zeros
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
+
+// 16 bytes per lane from the buffer at byte offset off into LDS at
+// dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (NERF_AS_LDS void*)dst, 16, (int)off, 0, 0, 0);
+}
+
+template <int RB, int CB>
+__global__ void __launch_bounds__(256) k_gemm_nt_dma(GemmNT g) {
+    using T = __bf16;
+    constexpr int TR = 64 * RB, TC = 64 * CB;
+    constexpr int STAGE = (TR + TC) * 64;  // bytes
+    constexpr int QR = TR / 64, QC = TC / 64;  // 1 KB copies per wave per step
+    constexpr int PH = 2 < RB ? 2 : RB;        // epilogue: block-rows per phase (128 bytes of features)
+    constexpr int FW = 32 * PH;
+    constexpr int SP = 2 * FW + 8;             // staged row pitch (elements)
+    constexpr int RING = kDmaStages * STAGE, EPI = TC * SP * 2;
+    __shared__ __attribute__((aligned(1024))) char lds[RING > EPI ? RING : EPI];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int n0 = blockIdx.y * TR, m0 = blockIdx.x * TC;
+    const int K = g.a0.kpad + g.a1.kpad, nk = K / 32;
+
+    // buffer resources over this tile's rows of the weights and of each activation segment
+    const int nrows = g.N - n0 < TR ? g.N - n0 : TR;
+    const __amdgpu_buffer_rsrc_t rb = dma_rsrc((const T*)g.b + (size_t)n0 * g.ldb, nrows * g.ldb * 2);
+    const int mend = g.M - m0 < TC ? g.M : m0 + TC;  // one past the tile's last product row
+    __amdgpu_buffer_rsrc_t rs[2];
+    int first[2];
+    const SegA* seg[2] = {&g.a0, &g.a1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const SegA& a = *seg[q];
+        const int rd = a.row_div > 0 ? a.row_div : 1;
+        first[q] = m0 / rd;
+        const int last = (mend - 1) / rd;
+        rs[q] = dma_rsrc((const T*)a.p + (size_t)first[q] * a.ld, a.kpad ? (last - first[q] + 1) * a.ld * 2 : 0);
+    }
+    // per-lane source offsets of this wave's copies (16 rows of 4 pieces each)
+    uint32_t vr[QR], vc[2][QC];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) {
+        const int row = (wave * QR + q) * 16 + (lane >> 2);
+        const int pc = (lane & 3) ^ swz(row);
+        vr[q] = n0 + row < g.N ? (uint32_t)(row * g.ldb * 2 + pc * 16) : kDmaSkip;
+    }
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+        const SegA& a = *seg[sg];
+        const int rd = a.row_div > 0 ? a.row_div : 1;
+#pragma unroll
+        for (int q = 0; q < QC; ++q) {
+            const int row = (wave * QC + q) * 16 + (lane >> 2);
+            const int pc = (lane & 3) ^ swz(row);
+            const int m = m0 + row;
+            vc[sg][q] = m < g.M ? (uint32_t)((m / rd - first[sg]) * a.ld * 2 + pc * 16) : kDmaSkip;
+        }
+    }
+    auto issue = [&](int t) {
+        char* slot = lds + (t % kDmaStages) * STAGE;
+        const uint32_t kb = (uint32_t)t * 64u;  // byte offset of the step in a weight row
+#pragma unroll
+        for (int q = 0; q < QR; ++q) dma16(rb, slot + (wave * QR + q) * 1024, vr[q] + kb);
+        const bool s0 = t * 32 < g.a0.kpad;
+        const uint32_t ka = s0 ? kb : kb - (uint32_t)g.a0.kpad * 2u;
+#pragma unroll
+        for (int q = 0; q < QC; ++q)
+            dma16(s0 ? rs[0] : rs[1], slot + TR * 64 + (wave * QC + q) * 1024, (s0 ? vc[0][q] : vc[1][q]) + ka);
+    };
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+    const int l32 = lane & 31, h = lane >> 5, sw = swz(l32);
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int t = 0; t < nk; ++t) {
+        if (t + 1 < nk)
+            wait_vm_lgkm0<QR + QC>();
+        else
+            wait_vm_lgkm0<0>();
+        compiler_fence();
+        __syncthreads();
+        if (t + 2 < nk) issue(t + 2);
+        const char* slot = lds + (t % kDmaStages) * STAGE;
+        const char* R = slot + (wr * 32 * RB) * 64;
+        const char* C = slot + TR * 64 + (wc * 32 * CB) * 64;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int off = (((2 * ks + h) ^ sw) * 16);
+            bf16x8 a[RB], b[CB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) a[i] = *reinterpret_cast<const bf16x8*>(R + (32 * i + l32) * 64 + off);
+#pragma unroll
+            for (int j = 0; j < CB; ++j) b[j] = *reinterpret_cast<const bf16x8*>(C + (32 * j + l32) * 64 + off);
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+    // Epilogue through LDS (as k_gemm_nt): whole 128-byte lines per row
+    constexpr int PPR = 2 * FW * 2 / 16;
+    T* st = reinterpret_cast<T*>(lds);
+#pragma unroll
+    for (int p = 0; p < RB / PH; ++p) {
+#pragma unroll
+        for (int ii = 0; ii < PH; ++ii) {
+            const int i = p * PH + ii;
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int ml = wc * 32 * CB + 32 * j + l32;
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int fl = 32 * ii + 8 * gq + 4 * h;
+                    const int n = n0 + wr * 32 * RB + 32 * i + 8 * gq + 4 * h;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = acc[i][j][4 * gq + e] + (g.bias && n < g.N ? g.bias[n + e] : 0.0f);
+                        if (g.relu) v[e] = fmaxf(v[e], 0.0f);
+                    }
+                    store4<T>(st + ml * SP + wr * FW + fl, v);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < TC * PPR / 256; ++q) {
+            const int u = tid + 256 * q;
+            const int ml = u / PPR, pc = u % PPR;
+            const int half = pc / (PPR / 2), e0 = (pc % (PPR / 2)) * 8;
+            const int m = m0 + ml;
+            const int n = n0 + half * 32 * RB + p * FW + e0;
+            if (m < g.M && n < g.N) {
+                union {
+                    u32x4 u;
+                    T e[8];
+                } x, mk;
+                x.u = *reinterpret_cast<const u32x4*>(st + ml * SP + half * FW + e0);
+                if (g.mask) {
+                    mk.u = *reinterpret_cast<const u32x4*>((const T*)g.mask + (size_t)m * g.ldm + n);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (!(elt_f(mk.e[e]) > 0.0f)) x.e[e] = elt_from<T>(0.0f);
+                }
+                *reinterpret_cast<u32x4*>((T*)g.c + (size_t)m * g.ldc + n) = x.u;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -729,10 +901,27 @@ __global__ void __launch_bounds__(256) k_adam(float* __restrict__ p, float* __re
 
 namespace {
 
+// bfloat16 products with whole-width bfloat16 outputs: the direct-copy kernel
+void gemm_nt_dma(const GemmNT& g, hipStream_t s) {
+    const unsigned gx4 = (unsigned)((g.M + 255) / 256), gx2 = (unsigned)((g.M + 127) / 128);
+    if (g.N > 128)
+        hipLaunchKernelGGL((k_gemm_nt_dma<4, 2>), dim3(gx2, (unsigned)((g.N + 255) / 256)), dim3(256), 0, s, g);
+    else if (g.N > 64)
+        hipLaunchKernelGGL((k_gemm_nt_dma<2, 2>), dim3(gx2, 1), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_gemm_nt_dma<1, 4>), dim3(gx4, 1), dim3(256), 0, s, g);
+}
+
 template <class T>
 void gemm_nt(const GemmNT& g, hipStream_t s) {
     // tile rows: the product's columns n (weights); tile columns: its rows m (samples)
     const unsigned gx4 = (unsigned)((g.M + 255) / 256), gx2 = (unsigned)((g.M + 127) / 128);
+    if constexpr (sizeof(T) == 2) {
+        if (!g.c_f32 && g.n_store == g.N && g.c_col0 == 0) {
+            gemm_nt_dma(g, s);
+            return;
+        }
+    }
     if (g.N > 128)
         hipLaunchKernelGGL((k_gemm_nt<T, 4, 2>), dim3(gx2, (unsigned)((g.N + 255) / 256)), dim3(256), 0, s, g);
     else if (g.N > 64)
