@@ -1,7 +1,8 @@
 """Throughput of the NeRF forward-render hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid|mlp|train]
+                    [--workload hierarchical|coarse|tiny|hash|kilo|encode|composite|hashgrid|mlp|train|
+                                train_hierarchical]
                     [--dtype bf16|f32] [--no-cpu-baseline]
 
 A step is one ``nerf_render`` over the whole workload with rays, weights
@@ -17,7 +18,9 @@ coarse workload's 81.92M sample points, ``composite`` the compositing of its
 bfloat16 on 2^23 encoded samples read from HBM (against the MFMA roofline),
 ``train`` one training step (nerf_train_step: forward, loss, every gradient,
 Adam) on 4096 random rays x 64 samples of the 8x256 network, its algorithmic
-products against the MFMA roofline over the whole step's time.
+products against the MFMA roofline over the whole step's time;
+``train_hierarchical`` the page's two-network step (coarse 64 samples,
+inverse-CDF resampling, fine network on the 192 merged samples).
 
 Prints one JSON line: rays/s (``value``), samples/s, the dominant kernel's
 achieved throughput against its roofline (timed live with HIP events on
@@ -97,6 +100,9 @@ WORKLOADS = {
     "mlp": dict(poses=1, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0, rays=1 << 17),
     # one training step: 4096 random rays of the coarse workload's images, 64 stratified samples, 8x256
     "train": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=0, kind=0, chunk=0, rays=4096),
+    # the page's two-network step: coarse 64 + fine 128 (192 merged), two 8x256 networks
+    "train_hierarchical": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=128, kind=0, chunk=0,
+                               rays=4096),
 }
 HBM_PEAK_GBS = 8000.0
 
@@ -417,7 +423,7 @@ def standalone(args, wl):
         far = torch.full((R,), 6.0, device=dev)
         z = torch.empty((R, N), device=dev)
         v.nerf_sample_stratified(near, far, N, 0, 0, True, z)
-    if name == "train":
+    if name in ("train", "train_hierarchical"):
         return train_bench(args, wl)
     if name == "mlp":
         Rm = wl["rays"]
@@ -548,8 +554,11 @@ def standalone(args, wl):
 
 
 def train_bench(args, wl):
-    """One training step (nerf_train_step) of the 8x256 network on a batch of
-    4096 random rays: forward, compositing, loss, every gradient, Adam."""
+    """One training step of the 8x256 network on a batch of 4096 random rays
+    (nerf_train_step: forward, compositing, loss, every gradient, Adam); with
+    n_fine > 0 the page's two-network step: the coarse network on 64
+    stratified samples (weights out), inverse-CDF resampling, the fine
+    network on the 192 merged samples."""
     import torch
     import seeded_inputs as si
     import volume_rendering_amd as v
@@ -558,7 +567,7 @@ def train_bench(args, wl):
     dev = torch.device("cuda")
     P = si.poses(wl["poses"], seed=0, hemisphere=wl["hemi"])
     H, W, f = wl["H"], wl["W"], wl["focal"]
-    R_all, R, N = wl["poses"] * H * W, wl["rays"], wl["nc"]
+    R_all, R, NC, NF = wl["poses"] * H * W, wl["rays"], wl["nc"], wl["nf"]
     ro_all = torch.empty((R_all, 3), device=dev)
     rd_all = torch.empty((R_all, 3), device=dev)
     for p in range(wl["poses"]):
@@ -571,33 +580,49 @@ def train_bench(args, wl):
     tgt_h = si.target_colors(R, seed=0)
     tgt = torch.from_numpy(tgt_h).to(dev)
     dtype = 1 if args.dtype == "bf16" else 0
-    params_h = si.nerf_params(si.NERF_8x256, seed=0, net_id=0)
-    flat = torch.from_numpy(si.flat_params(params_h)).to(dev)
-    m, vv = torch.zeros_like(flat), torch.zeros_like(flat)
-    loss = torch.empty(1, device=dev)
-    cfg = B.nerf_train_cfg(net=B.nerf_mlp_desc(1, dtype), n_samples=N, use_pi=1, white_bkgd=0, jitter=1, seed=0,
-                           ray_offset=0, lr=5e-4, beta1=0.9, beta2=0.999, eps=1e-8)
-    ws = torch.empty(v.nerf_train_workspace_size(cfg, R), dtype=torch.uint8, device=dev)
+    nets_h = [si.nerf_params(si.NERF_8x256, seed=0, net_id=k) for k in range(2 if NF else 1)]
+    state = [(torch.from_numpy(si.flat_params(ph)).to(dev),) for ph in nets_h]
+    state = [(p_[0], torch.zeros_like(p_[0]), torch.zeros_like(p_[0])) for p_ in state]
+    loss = torch.empty(2, device=dev)
+    cfgs = [B.nerf_train_cfg(net=B.nerf_mlp_desc(1, dtype), n_samples=n, use_pi=1, white_bkgd=0, jitter=1, seed=0,
+                             ray_offset=0, lr=5e-4, beta1=0.9, beta2=0.999, eps=1e-8) for n in ([NC, NC + NF] if NF
+                                                                                                else [NC])]
+    ws = torch.empty(max(v.nerf_train_workspace_size(c, R) for c in cfgs), dtype=torch.uint8, device=dev)
+    if NF:
+        w_c = torch.empty((R, NC), device=dev)
+        z_c = torch.empty((R, NC), device=dev)
+        z2 = torch.empty((R, NC + NF), device=dev)
+        cfgs[0].weights = w_c.data_ptr()
+        cfgs[1].z = z2.data_ptr()
     it = [0]
 
     def step():
         it[0] += 1
-        cfg.seed = it[0]
-        v.nerf_train_step(ro, rd, near, far, tgt, cfg, flat, loss, m, vv, it[0], workspace=ws)
+        for c in cfgs:
+            c.seed = it[0]
+        p0, m0, v0 = state[0]
+        v.nerf_train_step(ro, rd, near, far, tgt, cfgs[0], p0, loss[0:1], m0, v0, it[0], workspace=ws)
+        if NF:
+            v.nerf_sample_stratified(near, far, NC, it[0], 0, True, z_c)
+            v.nerf_sample_pdf(z_c, w_c, NF, it[0], 0, z_merged=z2)
+            p1, m1, v1 = state[1]
+            v.nerf_train_step(ro, rd, near, far, tgt, cfgs[1], p1, loss[1:2], m1, v1, it[0], workspace=ws)
 
     ms_step, ms_kernel = _timed(args, step, torch)
-    S = R * N
+    S = R * (NC + (NC + NF if NF else 0))  # network samples of the step
     flops = 2.0 * (2 * MACS_8x256 + MACS_8x256_DINPUT) * S
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     dt_name = "bf16" if dtype else "f32"
     out_rec = {
-        "metric": "training rays/s, one network pass (8x256, 64 samples per ray; MFMA util %)",
+        "metric": ("training rays/s, coarse 64 + fine 128 samples, two 8x256 networks (MFMA util %)" if NF else
+                   "training rays/s, one network pass (8x256, 64 samples per ray; MFMA util %)"),
         "value": R / (ms_step * 1e-3), "unit": "rays/s", "samples_per_sec": S / (ms_step * 1e-3), "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt_name,
         "data": "synthetic: 4096 seeded random rays of 8 hemisphere poses at 400x400, random target colours, "
                 "He-uniform random weights",
-        "config": {"workload": "train", "rays": R, "samples_per_ray": N, "net": "8x256", "optimizer": "Adam"},
+        "config": {"workload": args.workload, "rays": R, "n_coarse": NC, "n_fine": NF, "net": "8x256",
+                   "networks": len(state), "optimizer": "Adam"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[dt_name], "unit": "TFLOP/s",
                      "frac": achieved / PEAK[dt_name], "traffic": None, "kernel": "whole step (every kernel)",
                      "kernel_ms": ms_kernel, "flop_per_launch": flops},
@@ -607,11 +632,14 @@ def train_bench(args, wl):
         o_h, d_h = ro.cpu().numpy(), rd.cpu().numpy()
         n_h, f_h = near.cpu().numpy(), far.cpu().numpy()
         mode = "bf16" if dtype else "f64"
-        base = _cpu_rate(lambda s_: obwd.train_loss_and_grads(params_h, o_h[s_], d_h[s_], n_h[s_], f_h[s_],
-                                                              tgt_h[s_], N, 10, 4, seed=0, mode=mode,
-                                                              ray_offset=s_),
-                         R, args.cpu_seconds, "rays/s", "rays (loss and every gradient)")
-        out_rec["cpu_baseline"] = base
+        if NF:
+            fn = (lambda s_: obwd.hierarchical_train_step(nets_h[0], nets_h[1], o_h[s_], d_h[s_], n_h[s_], f_h[s_],
+                                                          tgt_h[s_], NC, NF, 10, 4, seed=0, mode=mode,
+                                                          ray_offset=s_))
+        else:
+            fn = (lambda s_: obwd.train_loss_and_grads(nets_h[0], o_h[s_], d_h[s_], n_h[s_], f_h[s_], tgt_h[s_], NC,
+                                                       10, 4, seed=0, mode=mode, ray_offset=s_))
+        out_rec["cpu_baseline"] = _cpu_rate(fn, R, args.cpu_seconds, "rays/s", "rays (loss and every gradient)")
     print(json.dumps(out_rec), flush=True)
 
 

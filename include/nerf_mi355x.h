@@ -358,6 +358,12 @@ typedef struct {
     uint64_t seed;         /* Philox key of the stratified jitter (as nerf_sample_stratified) */
     uint64_t ray_offset;   /* global index of ray 0 */
     float lr, beta1, beta2, eps; /* Adam */
+    const float* z;        /* optional device [n_rays, n_samples], ascending per ray: the sample
+                              depths to use instead of stratified ones (the fine pass of the
+                              page's training step: merged coarse and inverse-CDF samples, which
+                              carry no gradient); NULL: stratified */
+    float* weights;        /* optional device [n_rays, n_samples]: the compositing weights
+                              w_i = T_i alpha_i of this pass (input to nerf_sample_pdf) */
 } nerf_train_cfg;
 
 /* Flat parameter count of a network kind: the weights and biases in the
@@ -386,9 +392,14 @@ size_t nerf_train_workspace_size(const nerf_train_cfg* cfg, int64_t n_rays);
  * colours.  Weight gradients are sums over samples in a fixed order: a
  * step is deterministic.  workspace: device, 256-byte aligned, at least
  * nerf_train_workspace_size bytes, or NULL (allocated stream-ordered and
- * freed after the work).  Errors: null pointers, unsupported network,
- * n_samples outside 1..256, n_rays * n_samples above 2^28, step < 1 with
- * Adam, one of adam_m/adam_v missing, workspace too small. */
+ * freed after the work).  The page's two-network step (coarse and fine
+ * networks, MSE of both renderings) is two calls: the coarse network on
+ * stratified samples with cfg.weights set, nerf_sample_pdf on those weights
+ * (z_merged), then the fine network with cfg.z = z_merged; the sampled
+ * depths carry no gradient, so each network's gradient is that of its own
+ * term.  Errors: null pointers, unsupported network, n_samples outside
+ * 1..256, n_rays * n_samples above 2^28, step < 1 with Adam, one of
+ * adam_m/adam_v missing, misaligned z or weights, workspace too small. */
 nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const float* t_near, const float* t_far,
                             const float* target_rgb, int64_t n_rays, const nerf_train_cfg* cfg, float* params,
                             float* adam_m, float* adam_v, int64_t step, float* grad, float* loss, float* rgb,

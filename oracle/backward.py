@@ -151,17 +151,48 @@ def train_loss_and_grads(params, rays_o, rays_d, t_near, t_far, target, n_sample
     """Loss (MSE of the rendered rgb against ``target``) and its gradient for
     one network pass over stratified samples.  Returns (loss, rgb, grads)."""
     z = sampling.stratified(t_near, t_far, n_samples, seed, jitter, ray_offset)
+    loss, rgb, grads, _ = train_pass(params, rays_o, rays_d, z, target, L_pos, L_dir, mode, use_pi, white_bkgd)
+    return loss, rgb, grads
+
+
+def train_pass(params, rays_o, rays_d, z, target, L_pos=10, L_dir=4, mode="f64", use_pi=True, white_bkgd=False):
+    """One network pass over given sample depths ``z`` [R, N] (float32,
+    ascending): loss, rendered rgb, the gradient of the loss with respect to
+    every parameter, and the compositing weights [R, N].  The depths carry no
+    gradient (the page's fine samples come from the coarse weights under
+    no_grad)."""
+    z = np.asarray(z, dtype=np.float32)
     R, N = z.shape
     x = sampling.points(rays_o, rays_d, z)
     pe = encoding.freq_encode(x.reshape(-1, 3), L_pos, True, use_pi)
     de = np.repeat(encoding.freq_encode(sampling.view_dirs(rays_d), L_dir, True, use_pi), N, axis=0)
     raw, cache = nerf_forward_cache(params, pe, de, mode)
     raw = raw.reshape(R, N, 4)
-    rgb, _, _, _ = composite.volume_render(raw, z, rays_d, white_bkgd)
+    rgb, _, _, w = composite.volume_render(raw, z, rays_d, white_bkgd)
     loss = mse(rgb, target)
     d_rgb = 2.0 * (rgb - np.asarray(target, np.float64)) / rgb.size
     d_raw = composite_backward(raw, z, rays_d, d_rgb, white_bkgd).reshape(R * N, 4)
-    return loss, rgb, nerf_backward(params, cache, d_raw, mode)
+    return loss, rgb, nerf_backward(params, cache, d_raw, mode), w
+
+
+def hierarchical_train_step(coarse, fine, rays_o, rays_d, t_near, t_far, target, n_coarse=64, n_fine=128,
+                            L_pos=10, L_dir=4, seed=0, jitter=True, mode="f64", use_pi=True, white_bkgd=False,
+                            ray_offset=0):
+    """The page's training objective on one batch (Section 2 Code, 7.
+    Training loop: MSE of the coarse and of the fine rendering): the coarse
+    network on stratified samples, fine samples drawn from the coarse
+    weights (``sampling.hierarchical_fine_samples``, weights as float32, no
+    gradient through them) and merged, the fine network on the merged
+    samples.  The loss is the sum of the two MSEs, so each network's
+    gradient is that of its own term.  Returns dict(loss_c, loss_f, rgb_c,
+    rgb_f, grads_c, grads_f, w_c, z_c, bins, z2)."""
+    z_c = sampling.stratified(t_near, t_far, n_coarse, seed, jitter, ray_offset)
+    loss_c, rgb_c, g_c, w_c = train_pass(coarse, rays_o, rays_d, z_c, target, L_pos, L_dir, mode, use_pi,
+                                         white_bkgd)
+    _, bins, z2 = sampling.hierarchical_fine_samples(z_c, w_c.astype(np.float32), n_fine, seed, ray_offset)
+    loss_f, rgb_f, g_f, _ = train_pass(fine, rays_o, rays_d, z2, target, L_pos, L_dir, mode, use_pi, white_bkgd)
+    return dict(loss_c=loss_c, loss_f=loss_f, rgb_c=rgb_c, rgb_f=rgb_f, grads_c=g_c, grads_f=g_f, w_c=w_c, z_c=z_c,
+                bins=bins, z2=z2)
 
 
 def flatten(params_or_grads) -> np.ndarray:

@@ -216,3 +216,59 @@ def test_training_fits_a_teacher(v, dtype):
     say(f"  losses {['%.3e' % x for x in losses]}")
     assert np.all(np.isfinite(losses))
     assert losses[-1] < 0.05 * losses[0]
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_hierarchical_train_step(v, dtype):
+    """The page's two-network step as two calls and the sampler: the coarse
+    pass (stratified, weights out), nerf_sample_pdf on its weights, the fine
+    pass on the merged depths (cfg.z).  Each pass is checked against the
+    oracle's pass on the same depths; the merged depths against the oracle's
+    chain (bins may flip where float32 and float64 weights straddle a CDF
+    step)."""
+    say(f"train hierarchical dtype={dtype}")
+    torch = torch_cuda()
+    shape = si.NERF_4x64
+    R, NC, NF = 60, 16, 32
+    b = _batch(R, seed=9)
+    pc, pf = si.nerf_params(shape, seed=31), si.nerf_params(shape, seed=32)
+    mode = "bf16" if dtype else "f64"
+    ref = obwd.hierarchical_train_step(pc, pf, b["o"], b["d"], b["near"], b["far"], b["tgt"], n_coarse=NC, n_fine=NF,
+                                       L_pos=6, L_dir=4, seed=7, mode=mode)
+    tol = GRAD_TOL_BF16 if dtype else GRAD_TOL_F32
+    # coarse pass with its weights
+    w = empty((R, NC))
+    cfg = _cfg(v, shape, dtype, NC)
+    cfg.weights = w.data_ptr()
+    out_c = _gpu_step(v, b, cfg, si.flat_params(pc))
+    w_h = host(w)
+    say(f"  coarse loss gpu {out_c['loss']:.6e} oracle {ref['loss_c']:.6e}; weights max err "
+        f"{np.max(np.abs(w_h - ref['w_c'])):.2e}")
+    assert abs(out_c["loss"] - ref["loss_c"]) <= (1e-2 if dtype else 1e-5) * ref["loss_c"]
+    assert np.max(np.abs(w_h - ref["w_c"])) <= (2e-2 if dtype else 1e-5)
+    _compare_grads("coarse pass", out_c["grad"], obwd.flatten(ref["grads_c"]), pc, tol)
+    # the sampler on the GPU's weights, end to end
+    zc = empty((R, NC))
+    v.nerf_sample_stratified(dev(b["near"]), dev(b["far"]), NC, 7, 0, True, zc)
+    assert np.array_equal(host(zc), ref["z_c"])
+    z2 = empty((R, NC + NF))
+    bins = empty((R, NF), dtype=torch.int32)
+    v.nerf_sample_pdf(zc, w, NF, 7, 0, bin_idx=bins, z_merged=z2)
+    z2_h = host(z2)
+    # the chosen bins are integers; the depths inside a bin move with the
+    # weights' last bits, so they are compared within a tolerance
+    same = np.all(host(bins) == ref["bins"], axis=1)
+    dz = np.max(np.abs(z2_h - ref["z2"]), axis=1)
+    say(f"  chosen bins identical on {same.mean():.1%} of rays; merged depths on those within {dz[same].max():.2e}")
+    assert same.mean() >= (0.8 if dtype else 0.95)
+    if not dtype:
+        assert dz[same].max() <= 1e-4
+    # fine pass on the oracle's merged depths
+    cfg_f = _cfg(v, shape, dtype, NC + NF)
+    z_in = dev(ref["z2"].astype(np.float32))
+    cfg_f.z = z_in.data_ptr()
+    out_f = _gpu_step(v, b, cfg_f, si.flat_params(pf))
+    say(f"  fine loss gpu {out_f['loss']:.6e} oracle {ref['loss_f']:.6e}")
+    assert abs(out_f["loss"] - ref["loss_f"]) <= (1e-2 if dtype else 1e-5) * ref["loss_f"]
+    _compare_grads("fine pass", out_f["grad"], obwd.flatten(ref["grads_f"]), pf, tol)
+    torch.cuda.synchronize()

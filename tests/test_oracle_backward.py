@@ -118,3 +118,39 @@ def test_flat_order_is_the_packing_order():
     assert flat.size == si.NERF_4x64.n_params()
     back = backward.unflatten(flat, p)
     assert all(np.array_equal(a, b) for a, b in zip(v.weights.forward_order(back), v.weights.forward_order(p)))
+
+
+def test_hierarchical_step_gradients_match_central_differences():
+    """The two-network objective (coarse MSE + fine MSE, fine samples from the
+    coarse weights with no gradient through them): each network's gradient
+    equals central differences of the total loss with the sample depths held
+    fixed at the unperturbed ones."""
+    pc = si.nerf_params(TINY, seed=4)
+    pf = si.nerf_params(TINY, seed=5)
+    pc = dict(pc, sigma=(pc["sigma"][0] * 4.0, pc["sigma"][1] + np.float32(0.5)))
+    o, d, near, far, target = _tiny_batch(R=3, seed=2)
+    kw = dict(n_coarse=5, n_fine=4, L_pos=1, L_dir=1, seed=3)
+    out = backward.hierarchical_train_step(pc, pf, o, d, near, far, target, **kw)
+    assert out["z2"].shape == (3, 9) and np.all(np.diff(out["z2"], axis=1) >= 0)
+    z_c, z2 = out["z_c"], out["z2"]
+
+    def total(pc_, pf_):
+        lc = backward.train_pass(pc_, o, d, z_c, target, 1, 1)[0]
+        lf = backward.train_pass(pf_, o, d, z2, target, 1, 1)[0]
+        return lc + lf
+
+    for which, p, g in (("coarse", pc, out["grads_c"]), ("fine", pf, out["grads_f"])):
+        flat = backward.flatten(p)
+        ana = backward.flatten(g)
+        h = 1e-6
+        for k in range(0, flat.size, 7):  # every 7th parameter
+            fp, fm = flat.copy(), flat.copy()
+            fp[k] += h
+            fm[k] -= h
+            if which == "coarse":
+                lp, lm = total(backward_unflat(fp, p), pf), total(backward_unflat(fm, p), pf)
+            else:
+                lp, lm = total(pc, backward_unflat(fp, p)), total(pc, backward_unflat(fm, p))
+            num = (lp - lm) / (2 * h)
+            assert abs(num - ana[k]) <= 1e-6 * max(1.0, np.abs(ana).max()), (which, k, num, ana[k])
+    assert abs(out["loss_c"] + out["loss_f"] - total(pc, pf)) < 1e-12

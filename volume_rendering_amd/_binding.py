@@ -69,7 +69,8 @@ class nerf_render_cfg(C.Structure):
 class nerf_train_cfg(C.Structure):
     _fields_ = [("net", nerf_mlp_desc), ("n_samples", C.c_int32), ("use_pi", C.c_int32), ("white_bkgd", C.c_int32),
                 ("jitter", C.c_int32), ("seed", C.c_uint64), ("ray_offset", C.c_uint64), ("lr", C.c_float),
-                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float)]
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("z", C.c_void_p),
+                ("weights", C.c_void_p)]
 
 
 def lib():
@@ -258,7 +259,8 @@ def nerf_train_step(rays_o, rays_d, t_near, t_far, target_rgb, cfg: nerf_train_c
                     adam_v=None, step=0, grad=None, rgb=None, workspace=None):
     """One training step; ``params`` (and the Adam moments) are float32
     device tensors updated in place, ``loss`` a float32 device tensor [1],
-    ``workspace`` an optional device uint8 tensor."""
+    ``workspace`` an optional device uint8 tensor.  ``cfg.z`` and
+    ``cfg.weights`` are device pointers (``tensor.data_ptr()``) or None."""
     ws, wsb = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     _check(lib().nerf_train_step(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), _ptr(target_rgb),
                                  rays_o.shape[0], C.byref(cfg), _ptr(params), _ptr(adam_m), _ptr(adam_v), int(step),

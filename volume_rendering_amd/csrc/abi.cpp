@@ -337,7 +337,8 @@ nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const floa
                  "nerf_train_step: NULL input or output");
     NERF_REQUIRE(aligned4(rays_o) && aligned4(rays_d) && aligned4(t_near) && aligned4(t_far) &&
                      aligned4(target_rgb) && aligned4(params) && aligned4(loss) && (!grad || aligned4(grad)) &&
-                     (!rgb || aligned4(rgb)) && (!adam_m || (aligned4(adam_m) && aligned4(adam_v))),
+                     (!rgb || aligned4(rgb)) && (!adam_m || (aligned4(adam_m) && aligned4(adam_v))) &&
+                     (!cfg->z || aligned4(cfg->z)) && (!cfg->weights || aligned4(cfg->weights)),
                  "nerf_train_step: misaligned pointer");
     const int bf16 = cfg->net.dtype == NERF_BF16;
     const size_t need = train_workspace_layout(cfg->net.kind, bf16, n_rays, cfg->n_samples, nullptr, nullptr);
@@ -380,6 +381,8 @@ nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const floa
     t.eps = cfg->eps;
     t.loss = loss;
     t.rgb_out = rgb;
+    t.z_in = cfg->z;
+    t.w_out = cfg->weights;
     t.workspace = workspace;
     clear_pending();
     launch_train_step(cfg->net.kind, bf16, t, as_stream(stream));

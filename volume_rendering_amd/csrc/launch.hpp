@@ -94,6 +94,8 @@ struct TrainArgs {
     float lr, beta1, beta2, eps;
     float* loss;     // [1]
     float* rgb_out;  // [n_rays, 3] or NULL
+    const float* z_in;  // [n_rays, n_samples] sample depths, or NULL (stratified)
+    float* w_out;       // [n_rays, n_samples] compositing weights, or NULL
     void* workspace;
 };
 

@@ -709,18 +709,25 @@ __device__ __forceinline__ void encode_row(const float (&x)[3], int L, int use_p
     for (; c < ld; ++c) row[c] = elt_from<T>(0.0f);
 }
 
+// Sample depths (stratified, or the caller's z_in), points and position
+// encodings.
 template <class T>
 __global__ void __launch_bounds__(256) k_train_samples(const float* __restrict__ ro, const float* __restrict__ rd,
                                                        const float* __restrict__ tn, const float* __restrict__ tf,
-                                                       int64_t R, int N, uint64_t seed, uint64_t ray_offset,
-                                                       int jitter, int L, int use_pi, float* __restrict__ z, T* E,
-                                                       int ldE) {
+                                                       const float* __restrict__ z_in, int64_t R, int N,
+                                                       uint64_t seed, uint64_t ray_offset, int jitter, int L,
+                                                       int use_pi, float* __restrict__ z, T* E, int ldE) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= R * N) return;
     const int64_t r = s / N;
     const int i = (int)(s - r * N);
-    const float u = jitter ? philox_uniform(seed, ray_offset + (uint64_t)r, (uint32_t)i, kStreamJitter) : 0.5f;
-    const float zi = stratified_z(tn[r], tf[r], i, N, u);
+    float zi;
+    if (z_in) {
+        zi = z_in[s];
+    } else {
+        const float u = jitter ? philox_uniform(seed, ray_offset + (uint64_t)r, (uint32_t)i, kStreamJitter) : 0.5f;
+        zi = stratified_z(tn[r], tf[r], i, N, u);
+    }
     z[s] = zi;
     float x[3];
 #pragma unroll
@@ -756,7 +763,8 @@ __global__ void __launch_bounds__(256) k_composite_train(const float* __restrict
                                                          const float* __restrict__ rd,
                                                          const float* __restrict__ target, int64_t R, int N,
                                                          int white, float inv_count, T* d_rgb, T* d_sig,
-                                                         float* __restrict__ rgb_out, float* __restrict__ sq_err) {
+                                                         float* __restrict__ rgb_out, float* __restrict__ sq_err,
+                                                         float* __restrict__ w_out) {
     struct Lds {
         float alpha[kTrainMaxSamples], s[kTrainMaxSamples], trans[kTrainMaxSamples], w[kTrainMaxSamples];
         float delta[kTrainMaxSamples], c[kTrainMaxSamples][3];
@@ -797,6 +805,7 @@ __global__ void __launch_bounds__(256) k_composite_train(const float* __restrict
             S.c[i][0] = c0;
             S.c[i][1] = c1;
             S.c[i][2] = c2;
+            if (w_out) w_out[r * N + i] = w;
             sr += w * c0;
             sg += w * c1;
             sb += w * c2;
@@ -1017,8 +1026,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
 
     // --- samples and encodings -----------------------------------------------
     hipLaunchKernelGGL(k_train_samples<T>, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, s, t.ro, t.rd, t.tn, t.tf,
-                       R, N, t.seed, t.ray_offset, t.jitter, p.Lpos, t.use_pi, (float*)b.ptr[BZ], (T*)b.ptr[BE],
-                       p.ldE);
+                       t.z_in, R, N, t.seed, t.ray_offset, t.jitter, p.Lpos, t.use_pi, (float*)b.ptr[BZ],
+                       (T*)b.ptr[BE], p.ldE);
     hipLaunchKernelGGL(k_train_dirs<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, t.rd, R, p.Ldir, t.use_pi,
                        (T*)b.ptr[BV], p.ldV);
 
@@ -1091,7 +1100,7 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
     const float inv_count = (float)(1.0 / (3.0 * (double)R));
     hipLaunchKernelGGL(k_composite_train<T>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
                        (const float*)b.ptr[BRAW], (const float*)b.ptr[BZ], t.rd, t.target, R, N, t.white, inv_count,
-                       (T*)b.ptr[BDRGB], (T*)b.ptr[BDSIG], t.rgb_out, (float*)b.ptr[BSQ]);
+                       (T*)b.ptr[BDRGB], (T*)b.ptr[BDSIG], t.rgb_out, (float*)b.ptr[BSQ], t.w_out);
     hipLaunchKernelGGL(k_train_loss, dim3(1), dim3(256), 0, s, (const float*)b.ptr[BSQ], R, inv_count, t.loss);
 
     // --- backward ----------------------------------------------------------------
