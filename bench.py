@@ -62,9 +62,14 @@ KERNEL_SOURCES = {
     "encode": ["kernels.hip", "common.hpp", "launch.hpp"],
     "composite": ["kernels.hip", "common.hpp", "launch.hpp"],
     "hashgrid": ["kernels.hip", "raysteps.hpp", "common.hpp", "launch.hpp"],
+    "kilo": ["kilo.hip", "mlp.hpp", "nets.hpp", "raysteps.hpp", "common.hpp", "launch.hpp", "layouts.cpp"],
+    "train": ["train.hip", "train_plan.hpp", "layouts.cpp", "mlp.hpp", "nets.hpp", "common.hpp", "launch.hpp"],
 }
 MEASURED_TRAFFIC = {
-    ("hashgrid", "f32"): (6.446e9, "a7357bfc988a821a"),
+    ("hierarchical", "bf16"): (5.126e8, "e7cbe7830b559f28"),  # k_render_nerf per launch
+    ("kilo", "bf16"): (1.5036e9, "74bbecaec5af5c6a"),         # every kernel of one render
+    ("hashgrid", "f32"): (6.4763e9, "f7ffc74c1c631199"),      # both encoder kernels
+    ("train", "bf16"): (1.24786e10, "52b63710b639d988"),      # every kernel of one step
 }
 
 
@@ -624,7 +629,9 @@ def train_bench(args, wl):
         "config": {"workload": args.workload, "rays": R, "n_coarse": NC, "n_fine": NF, "net": "8x256",
                    "networks": len(state), "optimizer": "Adam"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[dt_name], "unit": "TFLOP/s",
-                     "frac": achieved / PEAK[dt_name], "traffic": None, "kernel": "whole step (every kernel)",
+                     "frac": achieved / PEAK[dt_name],
+                     "traffic": measured_traffic("train", dt_name) if not NF else None,
+                     "kernel": "whole step (every kernel)",
                      "kernel_ms": ms_kernel, "flop_per_launch": flops},
     }
     if not args.no_cpu_baseline:
