@@ -69,7 +69,7 @@ MEASURED_TRAFFIC = {
     ("hierarchical", "bf16"): (5.126e8, "e7cbe7830b559f28"),  # k_render_nerf per launch
     ("kilo", "bf16"): (1.5036e9, "74bbecaec5af5c6a"),         # every kernel of one render
     ("hashgrid", "f32"): (6.4763e9, "f7ffc74c1c631199"),      # both encoder kernels
-    ("train", "bf16"): (1.24786e10, "52b63710b639d988"),      # every kernel of one step
+    ("train", "bf16"): (1.01826e10, "a85e48ae2d72b970"),      # every kernel of one step
 }
 
 

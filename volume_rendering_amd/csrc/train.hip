@@ -568,10 +568,20 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     __shared__ __attribute__((aligned(16))) T lds[2][(TR + TC) * P];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
-    const int m0 = blockIdx.x * TR, n0 = blockIdx.y * TC;
-    const int kb = blockIdx.z * g.k_chunk;
+    // The grid is one-dimensional.  Workgroups are dealt to the eight XCDs
+    // round robin (linear id mod 8), and each XCD has its own L2: the output
+    // tiles of one split of the samples get ids that are equal mod 8, so the
+    // workgroups that read the same operand rows share one L2.  Splits are
+    // padded to a multiple of 8; the padding exits at once.
+    const int n_mt = (g.M + TR - 1) / TR, n_nt = (g.N + TC - 1) / TC, tiles = n_mt * n_nt;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int tile = slot % tiles, split = xcd + 8 * (slot / tiles);
+    if (split * g.k_chunk >= g.K) return;
+    const int mt = tile % n_mt, nt = tile / n_mt;
+    const int m0 = mt * TR, n0 = nt * TC;
+    const int kb = split * g.k_chunk;
     const int ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
-    const bool bias = g.bpart && blockIdx.y == 0 && tid < TR;
+    const bool bias = g.bpart && nt == 0 && tid < TR;
     RT rt;
     CT ct;
     f32x16 acc[RB][CB];
@@ -605,7 +615,7 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
         __syncthreads();
         buf ^= 1;
     }
-    float* out = g.part + (size_t)blockIdx.z * g.M * g.N;
+    float* out = g.part + (size_t)split * g.M * g.N;
     const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -619,7 +629,7 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
                 if (m < g.M) out[(size_t)m * g.N + n] = acc[i][j][r];
             }
     }
-    if (bias && m0 + tid < g.M) g.bpart[(size_t)blockIdx.z * g.M + m0 + tid] = bsum;
+    if (bias && m0 + tid < g.M) g.bpart[(size_t)split * g.M + m0 + tid] = bsum;
 }
 
 // grad[off + m*ld + col0 + n] = sum over splits (in order) of part[s][m][n],
@@ -959,8 +969,8 @@ void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int row
     g.part = (float*)b.ptr[BPART];
     g.bpart = b_off >= 0 ? (float*)b.ptr[BBPART] : nullptr;
     const int RB = rows_pad > 64 ? 2 : 1, CB = cols_pad > 64 ? 2 : 1;
-    const dim3 grid((unsigned)((rows_pad + 64 * RB - 1) / (64 * RB)), (unsigned)((cols_pad + 64 * CB - 1) / (64 * CB)),
-                    (unsigned)b.splits);
+    const int tiles = ((rows_pad + 64 * RB - 1) / (64 * RB)) * ((cols_pad + 64 * CB - 1) / (64 * CB));
+    const dim3 grid((unsigned)(tiles * ((b.splits + 7) / 8 * 8)));  // XCD-grouped, see k_gemm_tn
     if (RB == 2 && CB == 2)
         hipLaunchKernelGGL((k_gemm_tn<T, 2, 2>), grid, dim3(256), 0, s, g);
     else if (RB == 2)
