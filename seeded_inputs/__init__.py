@@ -279,3 +279,42 @@ def flat_params(params: dict) -> np.ndarray:
     head."""
     seq = list(params["layers"]) + [params[k] for k in ("sigma", "feature", "dir", "rgb")]
     return np.concatenate([np.asarray(a, np.float32).ravel() for Wb in seq for a in Wb])
+
+
+TAG_INR = 9
+
+
+def hash_inr_params(sizes, n_levels: int, hidden: int = 32, n_out: int = 1, seed: int = 0):
+    """Parameters of a hash-grid INR: one float32 table [size, 2] per level,
+    U(-1e-4, 1e-4), and a decoder Linear(2L -> hidden), ReLU, Linear(hidden
+    -> n_out) with weights and biases U(+-1/sqrt(fan_in)).  Returns (tables,
+    (W1, b1, W2, b2))."""
+    g = rng(seed, TAG_INR)
+    tables = [_uniform(g, (int(s), 2), 1e-4) for s in sizes]
+    f = 2 * n_levels
+    W1 = _uniform(g, (hidden, f), 1.0 / math.sqrt(f))
+    b1 = _uniform(g, (hidden,), 1.0 / math.sqrt(f))
+    W2 = _uniform(g, (n_out, hidden), 1.0 / math.sqrt(hidden))
+    b2 = _uniform(g, (n_out,), 1.0 / math.sqrt(hidden))
+    return tables, (W1, b1, W2, b2)
+
+
+def hash_inr_flat(tables, mlp) -> np.ndarray:
+    """The C ABI's flat order: tables level by level, then W1, b1, W2, b2."""
+    return np.concatenate([np.asarray(t, np.float32).ravel() for t in tables] +
+                          [np.asarray(a, np.float32).ravel() for a in mlp])
+
+
+def inr_target_image(res: int = 96):
+    """A grey-level test image on a res x res grid of [0,1]^2 with structure at
+    several scales: a smooth product of low-frequency sines, thin vertical
+    stripes and a sharp-edged disk, rescaled to [0,1].  Returns (coords
+    float32 [res*res, 2] as (x, y), values float32 [res*res, 1])."""
+    t = np.linspace(0.0, 1.0, res)
+    X, Y = np.meshgrid(t, t)
+    img = 0.5 + 0.35 * np.sin(6 * np.pi * X) * np.sin(6 * np.pi * Y)
+    img = img + 0.25 * (np.sin(22 * np.pi * X) > 0)
+    img = img + 0.4 * (np.hypot(X - 0.5, Y - 0.5) < 0.18)
+    img = (img - img.min()) / (img.max() - img.min())
+    coords = np.stack([X.ravel(), Y.ravel()], axis=1).astype(np.float32)
+    return coords, img.ravel()[:, None].astype(np.float32)
