@@ -63,7 +63,12 @@ KERNEL_SOURCES = {
     "composite": ["kernels.hip", "common.hpp", "launch.hpp"],
     "hashgrid": ["kernels.hip", "raysteps.hpp", "common.hpp", "launch.hpp"],
     "kilo": ["kilo.hip", "mlp.hpp", "nets.hpp", "raysteps.hpp", "common.hpp", "launch.hpp", "layouts.cpp"],
-    "train": ["train.hip", "train_plan.hpp", "layouts.cpp", "mlp.hpp", "nets.hpp", "common.hpp", "launch.hpp"],
+    "train": ["train.hip", "train_plan.hpp", "optim.hpp", "layouts.cpp", "mlp.hpp", "nets.hpp", "common.hpp",
+              "launch.hpp"],
+    "hash_inr": ["hash_train.hip", "inr_plan.hpp", "optim.hpp", "layouts.cpp", "raysteps.hpp", "common.hpp",
+                 "launch.hpp"],
+    "hash_inr_4m": ["hash_train.hip", "inr_plan.hpp", "optim.hpp", "layouts.cpp", "raysteps.hpp", "common.hpp",
+                    "launch.hpp"],
 }
 MEASURED_TRAFFIC = {
     ("hierarchical", "bf16"): (5.126e8, "e7cbe7830b559f28"),  # k_render_nerf per launch
@@ -108,6 +113,11 @@ WORKLOADS = {
     # the page's two-network step: coarse 64 + fine 128 (192 merged), two 8x256 networks
     "train_hierarchical": dict(poses=8, hemi=True, H=400, W=400, focal=555.0, nc=64, nf=128, kind=0, chunk=0,
                                rays=4096),
+    # one full-batch Adam step of the 2D hash-grid INR of "Instant-NGP - Visual Experiments", Experiment 2
+    # (8 levels, T = 2^12, N 8..160, decoder 16 -> 32 -> 1, lr 1e-2) on its 96 x 96 image; the same model
+    # on a 2048 x 2048 image (4.19M points per step)
+    "hash_inr": dict(kind=0, res=96, L=8, T=2 ** 12, nmin=8, nmax=160, hidden=32, lr=1e-2),
+    "hash_inr_4m": dict(kind=0, res=2048, L=8, T=2 ** 12, nmin=8, nmax=160, hidden=32, lr=1e-2),
 }
 HBM_PEAK_GBS = 8000.0
 
@@ -430,6 +440,8 @@ def standalone(args, wl):
         v.nerf_sample_stratified(near, far, N, 0, 0, True, z)
     if name in ("train", "train_hierarchical"):
         return train_bench(args, wl)
+    if name.startswith("hash_inr"):
+        return inr_bench(args, wl)
     if name == "mlp":
         Rm = wl["rays"]
         x = (ro[:Rm, None, :] + z[:Rm, :, None] * rd[:Rm, None, :]).reshape(-1, 3).contiguous()
@@ -647,6 +659,73 @@ def train_bench(args, wl):
             fn = (lambda s_: obwd.train_loss_and_grads(nets_h[0], o_h[s_], d_h[s_], n_h[s_], f_h[s_], tgt_h[s_], NC,
                                                        10, 4, seed=0, mode=mode, ray_offset=s_))
         out_rec["cpu_baseline"] = _cpu_rate(fn, R, args.cpu_seconds, "rays/s", "rays (loss and every gradient)")
+    print(json.dumps(out_rec), flush=True)
+
+
+def inr_bench(args, wl):
+    """Full-batch training steps of the hash-grid INR (nerf_hash_inr_train_step:
+    lookups, decoder forward and backward, table gradients, decoder
+    gradients, loss, Adam over every parameter).  Algorithmic bytes per step:
+    the points and targets once, the tables once for the lookups, one
+    gradient write per parameter and Adam's 7 float accesses per parameter."""
+    import torch
+    import seeded_inputs as si
+    import volume_rendering_amd as v
+    from volume_rendering_amd import _binding as B
+
+    dev = torch.device("cuda")
+    res, L, T, H = wl["res"], wl["L"], wl["T"], wl["hidden"]
+    g = B.nerf_hashgrid_init(L, T, wl["nmin"], wl["nmax"], dim=2)
+    cfg = B.nerf_hash_inr_cfg(hidden=H, n_out=1, lr=wl["lr"], beta1=0.9, beta2=0.999, eps=1e-8)
+    sizes = [min(T, (int(g.res[l]) + 1) ** 2) for l in range(L)]
+    tables, mlp = si.hash_inr_params(sizes, L, H, 1, seed=1)
+    flat = si.hash_inr_flat(tables, mlp)
+    assert flat.size == B.nerf_hash_inr_param_count(g, cfg)
+    coords, target = si.inr_target_image(res)
+    n = coords.shape[0]
+    x, t = torch.from_numpy(coords).to(dev), torch.from_numpy(target).to(dev)
+    params = torch.from_numpy(flat).to(dev)
+    m, vv = torch.zeros_like(params), torch.zeros_like(params)
+    loss = torch.empty(1, device=dev)
+    ws = torch.empty(v.nerf_hash_inr_workspace_size(g, cfg, n), dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def step():
+        it[0] += 1
+        v.nerf_hash_inr_train_step(x, t, g, cfg, params, loss, m, vv, it[0], workspace=ws)
+
+    ms_step, ms_kernel = _timed(args, step, torch)
+    P = flat.size
+    tab = P - (H * 2 * L + H + H + 1)
+    bytes_step = n * 3 * 4 + tab * 4 + P * 4 + P * 28
+    achieved = bytes_step / (ms_kernel * 1e-3) / 1e9
+    out_rec = {
+        "metric": "hash-grid INR training points/s (one full-batch Adam step; HBM roofline %)",
+        "value": n / (ms_step * 1e-3), "unit": "points/s", "steps_per_sec": 1e3 / ms_step, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic: the seeded {res}x{res} test image (sines, stripes, a disk), seeded U(+-1e-4) tables "
+                "and U(+-1/sqrt(fan_in)) decoder",
+        "config": {"workload": args.workload, "points": n, "levels": L, "table_size": T, "n_min": wl["nmin"],
+                   "n_max": wl["nmax"], "hidden": H, "params": P, "optimizer": "Adam", "lr": wl["lr"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, "f32"),
+                     "kernel": "whole step (every kernel)", "kernel_ms": ms_kernel, "bytes_per_launch": bytes_step},
+        "final_loss": float(loss.item()),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import backward as obwd
+        from oracle import encoding, hash_inr
+        og = encoding.HashGrid(2, L, T, wl["nmin"], wl["nmax"])
+        pf = flat.astype(np.float64)
+        z = np.zeros_like(pf)
+
+        def fn(sel):
+            _, _, dt, dm = hash_inr.forward_backward(og, tables, mlp, coords[sel], target[sel])
+            obwd.adam(pf, hash_inr.flatten(dt, dm), z, z, 1, wl["lr"])
+
+        out_rec["cpu_baseline"] = _cpu_rate(fn, n, args.cpu_seconds, "points/s",
+                                            "points (forward, every gradient, Adam over all parameters)")
     print(json.dumps(out_rec), flush=True)
 
 

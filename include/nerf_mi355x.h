@@ -405,6 +405,52 @@ nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const floa
                             float* adam_m, float* adam_v, int64_t step, float* grad, float* loss, float* rgb,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decoder of the hash-grid INR ("Instant-NGP - Visual Experiments", shared
+ * toolkit HashINR): Linear(2L -> hidden), ReLU, Linear(hidden -> n_out) on
+ * the concatenated grid features. */
+typedef struct {
+    int32_t hidden;        /* 1..64 */
+    int32_t n_out;         /* 1..4 */
+    float lr, beta1, beta2, eps; /* Adam */
+} nerf_hash_inr_cfg;
+
+/* Flat parameter count of the hash-grid INR on grid g: 2 floats per table
+ * entry (levels back to back, as g's offsets), then W1 [hidden][2L], b1
+ * [hidden], W2 [n_out][hidden], b2 [n_out] (0 if g or cfg is invalid). */
+int64_t nerf_hash_inr_param_count(const nerf_hashgrid* g, const nerf_hash_inr_cfg* cfg);
+
+/* Device workspace of nerf_hash_inr_train_step for n points (0 if invalid). */
+size_t nerf_hash_inr_workspace_size(const nerf_hashgrid* g, const nerf_hash_inr_cfg* cfg, int64_t n);
+
+/* One full-batch training step of the hash-grid INR ("Instant-NGP - Visual
+ * Experiments (a 2D multiresolution hash grid)", shared toolkit HashGrid2D,
+ * HashINR and train; Experiment 2): the grid features of each point (as
+ * nerf_encode_hashgrid, but from learnable float32 tables inside params and
+ * times g->level_mask), the decoder, loss = mean over points and outputs of
+ * (prediction - target)^2, the gradient of every table entry and decoder
+ * parameter (a point's feature gradient reaches each of its corners' entries
+ * times the corner's weight and the level's mask), then (adam_m and adam_v
+ * given) one bias-corrected Adam step as in nerf_train_step.  g: host grid
+ * layout (dim 2 or 3, at most 16 levels; g->tables is not used).  x: device
+ * [n, dim] in [0,1]^dim; target: device [n, n_out]; params, adam_m, adam_v:
+ * device float32 [nerf_hash_inr_param_count] (params updated in place);
+ * grad: optional device [nerf_hash_inr_param_count], the gradient before the
+ * update; loss: device float32 [1]; pred: optional device [n, n_out].  The
+ * decoder gradients and the loss are summed in a fixed order.  Table
+ * gradients of levels with at most 32768 entries are exact sums of the
+ * contributions rounded to 2^-32 of the residual scale (each contribution,
+ * in units of the output residual, clamped to +-256), so the step is
+ * deterministic; larger levels add up with float atomics, whose last bits
+ * depend on the order in which points arrive.  workspace: device, 256-byte
+ * aligned, at least nerf_hash_inr_workspace_size bytes (about 8 L bytes per
+ * point, plus partial sums), or NULL (allocated stream-ordered).  Errors:
+ * null pointers, bad grid layout or cfg, n above 2^27, step < 1 with Adam,
+ * one Adam moment missing, workspace too small. */
+nerf_status nerf_hash_inr_train_step(const float* x, const float* target, int64_t n, const nerf_hashgrid* g,
+                                     const nerf_hash_inr_cfg* cfg, float* params, float* adam_m, float* adam_v,
+                                     int64_t step, float* grad, float* loss, float* pred, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* For callers that cannot allocate                                       */
 /* ---------------------------------------------------------------------- */

@@ -86,6 +86,10 @@ void launch_train_step(int, int, const TrainArgs& t, hipStream_t) {
     if (!t.workspace || !t.loss) std::abort();
     launched();
 }
+void launch_hash_inr_step(const GridArgs&, const HashInrArgs& a, hipStream_t) {
+    if (!a.workspace || !a.loss || a.hidden < 1) std::abort();
+    launched();
+}
 }  // namespace nerf
 
 // ---------------------------------------------------------------------------

@@ -253,3 +253,37 @@ def test_train_param_count_and_validation():
     assert call(1000, hashnet) == 2
     assert call(1 << 24, cfg) == 2  # 2^28 samples at most
     assert B.nerf_train_workspace_size(hashnet, 10) == 0
+
+
+def test_hash_inr_param_count_and_validation():
+    from oracle import encoding
+    L = v.lib()
+    g = B.nerf_hashgrid_init(8, 2 ** 12, 8, 160, dim=2)
+    og = encoding.HashGrid(2, 8, 2 ** 12, 8, 160)
+    cfg = B.nerf_hash_inr_cfg(hidden=32, n_out=1, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8)
+    tables, mlp = si.hash_inr_params(og.sizes, og.L, 32, 1)
+    assert B.nerf_hash_inr_param_count(g, cfg) == si.hash_inr_flat(tables, mlp).size
+    assert B.nerf_hash_inr_param_count(g, cfg) == 2 * sum(og.sizes) + 32 * 16 + 32 + 32 + 1  # 577 decoder params
+    # the feature gradients (2 floats per level and point) plus partial sums:
+    # one table partial per chunk of at least 1024 points
+    tab = 2 * sum(og.sizes)
+    ws = B.nerf_hash_inr_workspace_size(g, cfg, 9216)
+    assert 9216 * 16 * 4 + 9 * tab * 4 <= ws < 9216 * 16 * 4 + 9 * tab * 4 + (1 << 20)
+    ws1, ws2 = (B.nerf_hash_inr_workspace_size(g, cfg, n) for n in (1 << 22, 1 << 23))
+    assert ws2 - ws1 >= (1 << 22) * 16 * 4
+    assert B.nerf_hash_inr_workspace_size(g, cfg, (1 << 27) + 1) > 0  # sized; the step itself refuses it
+    bad = B.nerf_hash_inr_cfg(hidden=65, n_out=1)
+    assert B.nerf_hash_inr_param_count(g, bad) == 0
+    P = C.c_void_p(256)
+    # no points: nothing to do; the grid's tables pointer is not needed
+    assert L.nerf_hash_inr_train_step(None, None, 0, C.byref(g), C.byref(cfg), None, None, None, 0, None, None, None,
+                                      None, 0, None) == 0
+    assert L.nerf_hash_inr_train_step(P, P, 10, C.byref(g), C.byref(bad), P, None, None, 0, None, P, None, None, 0,
+                                      None) == 1
+    assert L.nerf_hash_inr_train_step(P, P, 10, C.byref(g), C.byref(cfg), P, P, None, 1, None, P, None, None, 0,
+                                      None) == 1  # one Adam moment
+    assert L.nerf_hash_inr_train_step(P, P, (1 << 27) + 1, C.byref(g), C.byref(cfg), P, None, None, 0, None, P, None,
+                                      None, 0, None) == 1
+    need = B.nerf_hash_inr_workspace_size(g, cfg, 10)
+    assert L.nerf_hash_inr_train_step(P, P, 10, C.byref(g), C.byref(cfg), P, None, None, 0, None, P, None, P,
+                                      need - 1, None) == 3

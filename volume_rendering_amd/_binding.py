@@ -27,7 +27,8 @@ EXPORTED = [
     "nerf_pack_mlp", "nerf_gen_rays", "nerf_sample_stratified", "nerf_encode_freq", "nerf_encode_sh16",
     "nerf_encode_hashgrid", "nerf_mlp", "nerf_composite", "nerf_sample_pdf", "nerf_render",
     "nerf_render_workspace_size", "nerf_render_noalloc", "nerf_render_poses", "nerf_train_param_count",
-    "nerf_train_workspace_size", "nerf_train_step",
+    "nerf_train_workspace_size", "nerf_train_step", "nerf_hash_inr_param_count", "nerf_hash_inr_workspace_size",
+    "nerf_hash_inr_train_step",
 ]
 
 
@@ -73,6 +74,11 @@ class nerf_train_cfg(C.Structure):
                 ("weights", C.c_void_p)]
 
 
+class nerf_hash_inr_cfg(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_out", C.c_int32), ("lr", C.c_float), ("beta1", C.c_float),
+                ("beta2", C.c_float), ("eps", C.c_float)]
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -105,6 +111,10 @@ def lib():
             "nerf_train_param_count": (I64, [I]),
             "nerf_train_workspace_size": (S, [C.POINTER(nerf_train_cfg), I64]),
             "nerf_train_step": (I, [P, P, P, P, P, I64, C.POINTER(nerf_train_cfg), P, P, P, I64, P, P, P, P, S, P]),
+            "nerf_hash_inr_param_count": (I64, [C.POINTER(nerf_hashgrid), C.POINTER(nerf_hash_inr_cfg)]),
+            "nerf_hash_inr_workspace_size": (S, [C.POINTER(nerf_hashgrid), C.POINTER(nerf_hash_inr_cfg), I64]),
+            "nerf_hash_inr_train_step": (I, [P, P, I64, C.POINTER(nerf_hashgrid), C.POINTER(nerf_hash_inr_cfg), P, P, P,
+                                             I64, P, P, P, P, S, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -265,3 +275,25 @@ def nerf_train_step(rays_o, rays_d, t_near, t_far, target_rgb, cfg: nerf_train_c
     _check(lib().nerf_train_step(_ptr(rays_o), _ptr(rays_d), _ptr(t_near), _ptr(t_far), _ptr(target_rgb),
                                  rays_o.shape[0], C.byref(cfg), _ptr(params), _ptr(adam_m), _ptr(adam_v), int(step),
                                  _ptr(grad), _ptr(loss), _ptr(rgb), ws, wsb, _stream()), "nerf_train_step")
+
+
+# ----------------------------------------------------------------------------
+# Hash-grid INR training step
+# ----------------------------------------------------------------------------
+
+def nerf_hash_inr_param_count(grid: nerf_hashgrid, cfg: nerf_hash_inr_cfg) -> int:
+    return lib().nerf_hash_inr_param_count(C.byref(grid), C.byref(cfg))
+
+
+def nerf_hash_inr_workspace_size(grid: nerf_hashgrid, cfg: nerf_hash_inr_cfg, n: int) -> int:
+    return lib().nerf_hash_inr_workspace_size(C.byref(grid), C.byref(cfg), n)
+
+
+def nerf_hash_inr_train_step(x, target, grid: nerf_hashgrid, cfg: nerf_hash_inr_cfg, params, loss, adam_m=None,
+                             adam_v=None, step=0, grad=None, pred=None, workspace=None):
+    """One full-batch step of the hash-grid INR; ``params`` and the Adam
+    moments are float32 device tensors updated in place."""
+    ws, wsb = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().nerf_hash_inr_train_step(_ptr(x), _ptr(target), x.shape[0], C.byref(grid), C.byref(cfg),
+                                          _ptr(params), _ptr(adam_m), _ptr(adam_v), int(step), _ptr(grad),
+                                          _ptr(loss), _ptr(pred), ws, wsb, _stream()), "nerf_hash_inr_train_step")

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["render_nerf_bf16.hip", "render_nerf_f32.hip", "render_hash.hip", "mlp_bf16.hip", "mlp_f32.hip",
-           "kernels.hip", "kilo.hip", "abi.cpp", "pack.cpp", "layouts.cpp", "noalloc.hip", "train.hip"]
+           "kernels.hip", "kilo.hip", "abi.cpp", "pack.cpp", "layouts.cpp", "noalloc.hip", "train.hip", "hash_train.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-function"]
@@ -31,6 +31,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"-I{INCLUDE}", f"-
 # AGPRs where the kernels place them), so epilogues read results directly
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
+# sources built without the VGPR-form option: the INR step's kernels (whose
+# small MFMA accumulators may live in AGPRs) make that pass of this compiler
+# fail on the larger decoder shapes
+DEVICE_AGPR_FORM = {"hash_train.hip"}
 
 
 def _compile(src: str) -> str:
@@ -38,7 +42,9 @@ def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        dev = DEVICE if src not in DEVICE_AGPR_FORM else [a for a in DEVICE if a not in ("-mllvm",
+                                                                                       "-amdgpu-mfma-vgpr-form")]
+        cmd += dev + ["-x", "hip"]
     cmd += ["-c", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

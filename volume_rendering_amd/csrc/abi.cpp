@@ -59,16 +59,24 @@ GridArgs grid_args(const nerf_hashgrid* g) {
     return a;
 }
 
+nerf_status check_grid_layout(const nerf_hashgrid* g, const char* who);
+
 nerf_status check_grid(const nerf_hashgrid* g, const char* who) {
     if (!g) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid is NULL", who);
     if (!g->tables) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid tables are NULL", who);
+    if ((reinterpret_cast<uintptr_t>(g->tables) & 7u) != 0)
+        return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 8-byte aligned", who);
+    return check_grid_layout(g, who);
+}
+
+// The grid's levels, resolutions and table layout (not its tables).
+nerf_status check_grid_layout(const nerf_hashgrid* g, const char* who) {
+    if (!g) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid is NULL", who);
     if (g->n_levels < 1 || g->n_levels > NERF_HASH_MAX_LEVELS || g->n_feat != 2)
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid not initialised (levels %d, features %d)", who,
                          g->n_levels, g->n_feat);
     if (g->table_size == 0 || (g->table_size & (g->table_size - 1)))
         return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: table size %u not a power of two", who, g->table_size);
-    if ((reinterpret_cast<uintptr_t>(g->tables) & 7u) != 0)
-        return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: tables not 8-byte aligned", who);
     if (g->dim != 2 && g->dim != 3) return nerf_fail(NERF_ERR_INVALID_ARGUMENT, "%s: grid dim %d", who, g->dim);
     for (int l = 0; l < g->n_levels; ++l) {
         const int N = g->res[l];
@@ -391,6 +399,80 @@ nerf_status nerf_train_step(const float* rays_o, const float* rays_d, const floa
         const hipError_t e = hipFreeAsync(own, as_stream(stream));
         if (st == NERF_OK && e != hipSuccess)
             st = nerf_fail(NERF_ERR_HIP, "nerf_train_step: workspace free: %s", hipGetErrorString(e));
+    }
+    return st;
+}
+
+static bool inr_cfg_ok(const nerf_hash_inr_cfg* c) {
+    return c && c->hidden >= 1 && c->hidden <= 64 && c->n_out >= 1 && c->n_out <= 4;
+}
+
+int64_t nerf_hash_inr_param_count(const nerf_hashgrid* g, const nerf_hash_inr_cfg* cfg) {
+    if (!inr_cfg_ok(cfg) || check_grid_layout(g, "nerf_hash_inr_param_count") != NERF_OK) return 0;
+    return hash_inr_param_count(grid_args(g), cfg->hidden, cfg->n_out);
+}
+
+size_t nerf_hash_inr_workspace_size(const nerf_hashgrid* g, const nerf_hash_inr_cfg* cfg, int64_t n) {
+    if (!inr_cfg_ok(cfg) || n < 0 || check_grid_layout(g, "nerf_hash_inr_workspace_size") != NERF_OK) return 0;
+    return hash_inr_workspace_layout(grid_args(g), cfg->hidden, cfg->n_out, n, nullptr, nullptr);
+}
+
+nerf_status nerf_hash_inr_train_step(const float* x, const float* target, int64_t n, const nerf_hashgrid* g,
+                                     const nerf_hash_inr_cfg* cfg, float* params, float* adam_m, float* adam_v,
+                                     int64_t step, float* grad, float* loss, float* pred, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    const char* who = "nerf_hash_inr_train_step";
+    NERF_REQUIRE(inr_cfg_ok(cfg), "%s: cfg NULL or hidden/n_out outside 1..64 / 1..4", who);
+    const nerf_status gs = check_grid_layout(g, who);
+    if (gs != NERF_OK) return gs;
+    NERF_REQUIRE(n >= 0 && n <= ((int64_t)1 << 27), "%s: n %lld above 2^27", who, (long long)n);
+    NERF_REQUIRE(!adam_m == !adam_v, "%s: give both Adam moments or neither", who);
+    NERF_REQUIRE(!adam_m || step >= 1, "%s: Adam step %lld < 1", who, (long long)step);
+    if (n == 0) return NERF_OK;
+    NERF_REQUIRE(x && target && params && loss, "%s: NULL input or output", who);
+    NERF_REQUIRE(aligned4(x) && aligned4(target) && aligned16(params) && aligned4(loss) && (!grad || aligned4(grad)) &&
+                     (!pred || aligned4(pred)) && (!adam_m || (aligned4(adam_m) && aligned4(adam_v))),
+                 "%s: misaligned pointer (params 16-byte aligned, the rest 4)", who);
+    const GridArgs ga = grid_args(g);
+    const size_t need = hash_inr_workspace_layout(ga, cfg->hidden, cfg->n_out, n, nullptr, nullptr);
+    void* own = nullptr;
+    if (workspace) {
+        if (workspace_bytes < need)
+            return nerf_fail(NERF_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, need);
+        NERF_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "%s: workspace must be 256-byte aligned",
+                     who);
+    } else {
+        clear_pending();
+        const hipError_t e = hipMallocAsync(&own, need, as_stream(stream));
+        if (e != hipSuccess)
+            return nerf_fail(NERF_ERR_WORKSPACE, "%s: cannot allocate %zu workspace bytes: %s", who, need,
+                             hipGetErrorString(e));
+        workspace = own;
+    }
+    HashInrArgs a{};
+    a.x = x;
+    a.target = target;
+    a.n = n;
+    a.hidden = cfg->hidden;
+    a.n_out = cfg->n_out;
+    a.params = params;
+    a.adam_m = adam_m;
+    a.adam_v = adam_v;
+    a.grad = grad;
+    a.step = step;
+    a.lr = cfg->lr;
+    a.beta1 = cfg->beta1;
+    a.beta2 = cfg->beta2;
+    a.eps = cfg->eps;
+    a.loss = loss;
+    a.pred = pred;
+    a.workspace = workspace;
+    clear_pending();
+    launch_hash_inr_step(ga, a, as_stream(stream));
+    nerf_status st = check_launch(who);
+    if (own) {
+        const hipError_t e = hipFreeAsync(own, as_stream(stream));
+        if (st == NERF_OK && e != hipSuccess) st = nerf_fail(NERF_ERR_HIP, "%s: workspace free: %s", who, hipGetErrorString(e));
     }
     return st;
 }

@@ -103,6 +103,28 @@ size_t train_workspace_layout(int kind, int bf16, int64_t n_rays, int n_samples,
 int64_t train_param_count(int kind);
 void launch_train_step(int kind, int bf16, const TrainArgs& t, hipStream_t s);
 
+// One training step of the hash-grid INR (learnable float32 tables and a
+// decoder with one hidden ReLU layer).
+struct HashInrArgs {
+    const float* x;       // [n, dim] points in [0,1]^dim
+    const float* target;  // [n, n_out]
+    int64_t n;
+    int hidden, n_out;
+    float* params;  // flat: tables (2 floats per entry, levels back to back), W1, b1, W2, b2
+    float* adam_m;  // NULL: no Adam step
+    float* adam_v;
+    float* grad;  // flat gradient out, or NULL (kept in the workspace)
+    int64_t step;
+    float lr, beta1, beta2, eps;
+    float* loss;  // [1]
+    float* pred;  // [n, n_out] or NULL
+    void* workspace;
+};
+
+int64_t hash_inr_param_count(const GridArgs& g, int hidden, int n_out);
+size_t hash_inr_workspace_layout(const GridArgs& g, int hidden, int n_out, int64_t n, char* base, void* out);
+void launch_hash_inr_step(const GridArgs& g, const HashInrArgs& a, hipStream_t s);
+
 // Rays per local-scan block of the many-network render's prefix sums (256 threads x 4).
 constexpr int kKiloScanBlock = 1024;
 

@@ -1,8 +1,9 @@
-// Workspace layouts of the many-network render and of a training step:
+// Workspace layouts of the many-network render and of the training steps:
 // host arithmetic only, shared by the launchers and the C ABI's size queries.
 #include <stddef.h>
 #include <stdint.h>
 
+#include "inr_plan.hpp"
 #include "launch.hpp"
 #include "nets.hpp"
 #include "train_plan.hpp"
@@ -92,5 +93,27 @@ size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, 
 }
 
 int64_t train_param_count(int kind) { return make_plan(kind).P; }
+
+int64_t hash_inr_param_count(const GridArgs& g, int hidden, int n_out) {
+    return inr_table_floats(g) + inr_decoder_params(g, hidden, n_out);
+}
+
+size_t hash_inr_workspace_layout(const GridArgs& g, int hidden, int n_out, int64_t n, char* base, void* out) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> float* {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return base ? reinterpret_cast<float*>(base + at) : nullptr;
+    };
+    const InrShape sh = inr_shape(g, hidden, n_out, n);
+    InrWs w{};
+    w.dfeat = take(4 * (size_t)n * 2 * g.n_levels);
+    w.part_dec = take(4 * (size_t)sh.groups * (size_t)sh.part_w);
+    w.part_tab = take(4 * (size_t)sh.scat_chunks * (size_t)sh.lds_tab_floats);
+    w.grad = take(4 * (size_t)hash_inr_param_count(g, hidden, n_out));
+    w.wpad = take(4 * (size_t)sh.weight_floats);
+    if (out) *static_cast<InrWs*>(out) = w;
+    return off;
+}
 
 }  // namespace nerf

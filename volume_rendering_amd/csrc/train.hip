@@ -25,6 +25,7 @@
 #include "launch.hpp"
 #include "mlp.hpp"
 #include "nets.hpp"
+#include "optim.hpp"
 #include "train_plan.hpp"
 
 namespace nerf {
@@ -886,36 +887,6 @@ __global__ void __launch_bounds__(256) k_composite_train(const float* __restrict
     }
 }
 
-// loss = inv_count * sum of the rays' squared errors, summed in a fixed order.
-__global__ void __launch_bounds__(256) k_train_loss(const float* __restrict__ sq_err, int64_t R, float inv_count,
-                                                    float* __restrict__ loss) {
-    __shared__ double part[256];
-    double s = 0.0;
-    for (int64_t r = threadIdx.x; r < R; r += blockDim.x) s += (double)sq_err[r];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int h = 128; h >= 1; h >>= 1) {
-        if ((int)threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) loss[0] = (float)(part[0] * (double)inv_count);
-}
-
-// Adam (Kingma and Ba, Algorithm 1) with bias correction: c1 = 1/(1-b1^t),
-// c2 = 1/(1-b2^t).
-__global__ void __launch_bounds__(256) k_adam(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
-                                              const float* __restrict__ g, int64_t P, float lr, float b1, float b2,
-                                              float eps, float c1, float c2) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= P) return;
-    const float gi = g[i];
-    const float mi = b1 * m[i] + (1.0f - b1) * gi;
-    const float vi = b2 * v[i] + (1.0f - b2) * gi * gi;
-    m[i] = mi;
-    v[i] = vi;
-    p[i] -= lr * (mi * c1) / (sqrtf(vi * c2) + eps);
-}
-
 }  // namespace
 
 namespace {
@@ -1199,12 +1170,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
     }
 
     // --- Adam ------------------------------------------------------------------
-    if (t.adam_m && t.adam_v && t.step >= 1) {
-        const double c1 = 1.0 / (1.0 - std::pow((double)t.beta1, (double)t.step));
-        const double c2 = 1.0 / (1.0 - std::pow((double)t.beta2, (double)t.step));
-        hipLaunchKernelGGL(k_adam, dim3((unsigned)((p.P + 255) / 256)), dim3(256), 0, s, t.params, t.adam_m, t.adam_v,
-                           (const float*)grad, p.P, t.lr, t.beta1, t.beta2, t.eps, (float)c1, (float)c2);
-    }
+    if (t.adam_m && t.adam_v && t.step >= 1)
+        adam_step(t.params, t.adam_m, t.adam_v, grad, p.P, t.lr, t.beta1, t.beta2, t.eps, t.step, s);
 }
 
 }  // namespace
