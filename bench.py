@@ -665,9 +665,11 @@ def train_bench(args, wl):
 def inr_bench(args, wl):
     """Full-batch training steps of the hash-grid INR (nerf_hash_inr_train_step:
     lookups, decoder forward and backward, table gradients, decoder
-    gradients, loss, Adam over every parameter).  Algorithmic bytes per step:
-    the points and targets once, the tables once for the lookups, one
-    gradient write per parameter and Adam's 7 float accesses per parameter."""
+    gradients, loss, Adam over every parameter), against the vector-ALU
+    roofline: per point 2 FLOP for each multiply-add of the decoder forward
+    (H F + H O), backward (H O + H F) and weight gradients (H F + H + O H + O),
+    and of the 4 corners x 2 features x L levels interpolation, gathered and
+    scattered."""
     import torch
     import seeded_inputs as si
     import volume_rendering_amd as v
@@ -675,10 +677,11 @@ def inr_bench(args, wl):
 
     dev = torch.device("cuda")
     res, L, T, H = wl["res"], wl["L"], wl["T"], wl["hidden"]
+    O, F = 1, 2 * wl["L"]
     g = B.nerf_hashgrid_init(L, T, wl["nmin"], wl["nmax"], dim=2)
-    cfg = B.nerf_hash_inr_cfg(hidden=H, n_out=1, lr=wl["lr"], beta1=0.9, beta2=0.999, eps=1e-8)
+    cfg = B.nerf_hash_inr_cfg(hidden=H, n_out=O, lr=wl["lr"], beta1=0.9, beta2=0.999, eps=1e-8)
     sizes = [min(T, (int(g.res[l]) + 1) ** 2) for l in range(L)]
-    tables, mlp = si.hash_inr_params(sizes, L, H, 1, seed=1)
+    tables, mlp = si.hash_inr_params(sizes, L, H, O, seed=1)
     flat = si.hash_inr_flat(tables, mlp)
     assert flat.size == B.nerf_hash_inr_param_count(g, cfg)
     coords, target = si.inr_target_image(res)
@@ -695,22 +698,22 @@ def inr_bench(args, wl):
         v.nerf_hash_inr_train_step(x, t, g, cfg, params, loss, m, vv, it[0], workspace=ws)
 
     ms_step, ms_kernel = _timed(args, step, torch)
-    P = flat.size
-    tab = P - (H * 2 * L + H + H + 1)
-    bytes_step = n * 3 * 4 + tab * 4 + P * 4 + P * 28
-    achieved = bytes_step / (ms_kernel * 1e-3) / 1e9
+    flop_point = 2 * (H * F + H * O + H * O + H * F + H * F + H + O * H + O) + 2 * 2 * (4 * F)
+    flops = float(flop_point) * n
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    peak = PEAK["f32"]
     out_rec = {
-        "metric": "hash-grid INR training points/s (one full-batch Adam step; HBM roofline %)",
+        "metric": "hash-grid INR training points/s (one full-batch Adam step; vector-ALU roofline %)",
         "value": n / (ms_step * 1e-3), "unit": "points/s", "steps_per_sec": 1e3 / ms_step, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": f"synthetic: the seeded {res}x{res} test image (sines, stripes, a disk), seeded U(+-1e-4) tables "
                 "and U(+-1/sqrt(fan_in)) decoder",
         "config": {"workload": args.workload, "points": n, "levels": L, "table_size": T, "n_min": wl["nmin"],
-                   "n_max": wl["nmax"], "hidden": H, "params": P, "optimizer": "Adam", "lr": wl["lr"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, "f32"),
-                     "kernel": "whole step (every kernel)", "kernel_ms": ms_kernel, "bytes_per_launch": bytes_step},
+                   "n_max": wl["nmax"], "hidden": H, "params": int(flat.size), "optimizer": "Adam", "lr": wl["lr"]},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(args.workload, "f32"), "kernel": "whole step (every kernel)",
+                     "kernel_ms": ms_kernel, "flop_per_launch": flops, "flop_per_point": flop_point},
         "final_loss": float(loss.item()),
     }
     if not args.no_cpu_baseline:

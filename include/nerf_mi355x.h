@@ -432,16 +432,17 @@ size_t nerf_hash_inr_workspace_size(const nerf_hashgrid* g, const nerf_hash_inr_
  * times the corner's weight and the level's mask), then (adam_m and adam_v
  * given) one bias-corrected Adam step as in nerf_train_step.  g: host grid
  * layout (dim 2 or 3, at most 16 levels; g->tables is not used).  x: device
- * [n, dim] in [0,1]^dim; target: device [n, n_out]; params, adam_m, adam_v:
- * device float32 [nerf_hash_inr_param_count] (params updated in place);
+ * [n, dim] in [0,1]^dim, 16-byte aligned; target: device [n, n_out];
+ * params (16-byte aligned), adam_m, adam_v: device float32
+ * [nerf_hash_inr_param_count] (params updated in place);
  * grad: optional device [nerf_hash_inr_param_count], the gradient before the
  * update; loss: device float32 [1]; pred: optional device [n, n_out].  The
  * decoder gradients and the loss are summed in a fixed order.  Table
- * gradients of levels with at most 32768 entries are exact sums of the
- * contributions rounded to 2^-32 of the residual scale (each contribution,
- * in units of the output residual, clamped to +-256), so the step is
- * deterministic; larger levels add up with float atomics, whose last bits
- * depend on the order in which points arrive.  workspace: device, 256-byte
+ * gradients of levels with at most 32768 entries are exact integer sums of
+ * per-thread float32 partial sums (consecutive points, in order) rounded to
+ * 2^-32 in units of the output residual (each such partial clamped to
+ * +-2048), so the step is deterministic; larger levels add up with float
+ * atomics, whose last bits depend on the order in which points arrive.  workspace: device, 256-byte
  * aligned, at least nerf_hash_inr_workspace_size bytes (about 8 L bytes per
  * point, plus partial sums), or NULL (allocated stream-ordered).  Errors:
  * null pointers, bad grid layout or cfg, n above 2^27, step < 1 with Adam,

@@ -265,10 +265,10 @@ def test_hash_inr_param_count_and_validation():
     assert B.nerf_hash_inr_param_count(g, cfg) == si.hash_inr_flat(tables, mlp).size
     assert B.nerf_hash_inr_param_count(g, cfg) == 2 * sum(og.sizes) + 32 * 16 + 32 + 32 + 1  # 577 decoder params
     # the feature gradients (2 floats per level and point) plus partial sums:
-    # one table partial per chunk of at least 1024 points
+    # one table partial per chunk of at least 4096 points
     tab = 2 * sum(og.sizes)
     ws = B.nerf_hash_inr_workspace_size(g, cfg, 9216)
-    assert 9216 * 16 * 4 + 9 * tab * 4 <= ws < 9216 * 16 * 4 + 9 * tab * 4 + (1 << 20)
+    assert 9216 * 16 * 4 + 3 * tab * 4 <= ws < 9216 * 16 * 4 + 3 * tab * 4 + (1 << 20)
     ws1, ws2 = (B.nerf_hash_inr_workspace_size(g, cfg, n) for n in (1 << 22, 1 << 23))
     assert ws2 - ws1 >= (1 << 22) * 16 * 4
     assert B.nerf_hash_inr_workspace_size(g, cfg, (1 << 27) + 1) > 0  # sized; the step itself refuses it
@@ -284,6 +284,8 @@ def test_hash_inr_param_count_and_validation():
                                       None) == 1  # one Adam moment
     assert L.nerf_hash_inr_train_step(P, P, (1 << 27) + 1, C.byref(g), C.byref(cfg), P, None, None, 0, None, P, None,
                                       None, 0, None) == 1
+    assert L.nerf_hash_inr_train_step(C.c_void_p(264), P, 10, C.byref(g), C.byref(cfg), P, None, None, 0, None, P,
+                                      None, None, 0, None) == 1  # x not 16-byte aligned
     need = B.nerf_hash_inr_workspace_size(g, cfg, 10)
     assert L.nerf_hash_inr_train_step(P, P, 10, C.byref(g), C.byref(cfg), P, None, None, 0, None, P, None, P,
                                       need - 1, None) == 3

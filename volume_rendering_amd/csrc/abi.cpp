@@ -430,9 +430,10 @@ nerf_status nerf_hash_inr_train_step(const float* x, const float* target, int64_
     NERF_REQUIRE(!adam_m || step >= 1, "%s: Adam step %lld < 1", who, (long long)step);
     if (n == 0) return NERF_OK;
     NERF_REQUIRE(x && target && params && loss, "%s: NULL input or output", who);
-    NERF_REQUIRE(aligned4(x) && aligned4(target) && aligned16(params) && aligned4(loss) && (!grad || aligned4(grad)) &&
-                     (!pred || aligned4(pred)) && (!adam_m || (aligned4(adam_m) && aligned4(adam_v))),
-                 "%s: misaligned pointer (params 16-byte aligned, the rest 4)", who);
+    NERF_REQUIRE(aligned16(x) && aligned4(target) && aligned16(params) && aligned4(loss) &&
+                     (!grad || aligned4(grad)) && (!pred || aligned4(pred)) &&
+                     (!adam_m || (aligned4(adam_m) && aligned4(adam_v))),
+                 "%s: misaligned pointer (x and params 16-byte aligned, the rest 4)", who);
     const GridArgs ga = grid_args(g);
     const size_t need = hash_inr_workspace_layout(ga, cfg->hidden, cfg->n_out, n, nullptr, nullptr);
     void* own = nullptr;

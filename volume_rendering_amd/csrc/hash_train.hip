@@ -53,9 +53,11 @@ struct InrStep {
     int lds_levels;         // those levels
     int iters;              // points per thread of the decoder kernel
     int part_w;             // floats per decoder partial
-    int64_t scat_chunk;     // points per scatter chunk
+    int64_t scat_chunk;     // points per scatter chunk (a multiple of 4 per thread)
     int scat_chunks;
-    float* dfeat;           // [L][n][2]: feature gradients (residual units)
+    int scat_jobs;
+    int64_t dstride;        // points per level slice of dfeat (n rounded up to even)
+    float* dfeat;           // [L][dstride][2]: feature gradients (residual units)
     float* part_dec;        // [decode groups][part_w]
     float* part_tab;        // [scatter chunks][lds_tab_floats]
     float* grad;            // flat gradient (the global-atomic levels accumulate here)
@@ -64,7 +66,8 @@ struct InrStep {
 
 // Padded decoder: one row of RW = FM + 8 floats per hidden unit j (W1[j][0..FM),
 // b1[j], W2[0..3][j], 3 zeros), then b2[0..3] and 4 zeros, then W1 transposed
-// ([FM][HM], for the per-level feature gradient); zeros outside the real sizes.
+// ([FM][HM], for the per-level feature gradient), then W2 ([4][HM], for the
+// outputs); zeros outside the real sizes.
 __global__ void __launch_bounds__(256) k_inr_pad(const float* __restrict__ dec, int H, int F, int O, int HM, int FM,
                                                  float* __restrict__ wp) {
     const float* W1 = dec;
@@ -72,7 +75,7 @@ __global__ void __launch_bounds__(256) k_inr_pad(const float* __restrict__ dec, 
     const float* W2 = b1 + H;
     const float* b2 = W2 + O * H;
     const int RW = FM + 8;
-    const int n = HM * RW + 8 + FM * HM;
+    const int n = HM * RW + 8 + FM * HM + 4 * HM;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
         float v = 0.0f;
         if (i < HM * RW) {
@@ -88,9 +91,12 @@ __global__ void __launch_bounds__(256) k_inr_pad(const float* __restrict__ dec, 
         } else if (i < HM * RW + 8) {
             const int o = i - HM * RW;
             if (o < O) v = b2[o];
-        } else {
+        } else if (i < HM * RW + 8 + FM * HM) {
             const int k = (i - HM * RW - 8) / HM, j = (i - HM * RW - 8) % HM;
             if (j < H && k < F) v = W1[j * F + k];
+        } else {
+            const int o = (i - HM * RW - 8 - FM * HM) / HM, j = (i - HM * RW - 8 - FM * HM) % HM;
+            if (j < H && o < O) v = W2[o * H + j];
         }
         wp[i] = v;
     }
@@ -175,14 +181,15 @@ __device__ __forceinline__ void wave_sync() {
 template <int DIM, int HM, int FM>
 __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrArgs a, InrStep f,
                                                             const float* __restrict__ wp) {
-    // staged point: dpre | h | feat | dy[0..3], 1, 0 ... (16)
-    constexpr int SW = 2 * HM + FM + 16;
+    // staged point: dpre | h | feat | dy[0..3], 1, 0 ... (16), padded to a
+    // stride of 20 banks mod 32 (16-byte row writes of 8 lanes cover every
+    // bank; the operand reads of 4 rows x 16 columns meet at most 2-way)
+    constexpr int SW = inr_stage_width(HM, FM);
     constexpr int LM = FM / 2;
     constexpr int HT = HM / 16, FT = FM / 16;
     constexpr int RW = FM + 8;  // padded decoder row
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int L = g.n_levels, F = 2 * L, H = a.hidden, O = a.n_out;
     float* stage = lds + wave * (kInrStageRows * SW);
 
     // C[j][k] over the wave's points: dpre[j] feat[k] (W1), h[j] dy[k] (W2),
@@ -211,6 +218,11 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
         asm volatile("" : "+s"(foff), "+s"(boff));
         const float* wf = wp + foff;
         const float* wb = wp + boff;
+        // per-iteration copies of the level and output counts: the
+        // comparisons against them are then made where they are used, not
+        // kept for every level and output as lane masks in SGPRs
+        int L = g.n_levels, O = a.n_out;
+        asm volatile("" : "+s"(L), "+s"(O));
         float feat[FM], h[HM], dpre[HM], dy[4];
 #pragma unroll
         for (int k = 0; k < FM; ++k) feat[k] = 0.0f;
@@ -240,20 +252,28 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
                 feat[2 * l] = lv.mask * a0;
                 feat[2 * l + 1] = lv.mask * a1;
             }
-            // decoder forward
-            float y[4];
-#pragma unroll
-            for (int o = 0; o < 4; ++o) y[o] = wf[HM * RW + o];
+            // decoder forward: the hidden units row by row, then the outputs
+            // (each pass over uniform data of its own, so that no weight
+            // waits in registers for a later use)
 #pragma unroll
             for (int j = 0; j < HM; ++j) {
-                float w[RW];
-                load_row<RW>(wf + j * RW, w);
+                float w[FM + 1];
+                load_row<FM + 1>(wf + j * RW, w);
                 float s = w[FM];
 #pragma unroll
                 for (int k = 0; k < FM; ++k) s = fmaf(w[k], feat[k], s);
                 h[j] = fmaxf(s, 0.0f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int o = 0; o < 4; ++o) y[o] = fmaf(w[FM + 1 + o], h[j], y[o]);
+            for (int o = 0; o < 4; ++o) {
+                if (o >= O) break;  // uniform
+                const float* w2 = wf + HM * RW + 8 + FM * HM + o * HM;
+                float s = wf[HM * RW + o];
+#pragma unroll
+                for (int j = 0; j < HM; ++j) s = fmaf(w2[j], h[j], s);
+                y[o] = s;
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
@@ -266,16 +286,17 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
                 db2[o] += d;
             }
             // decoder backward: the hidden pre-activation gradient (zero where
-            // the ReLU output is zero), from b1 | W2 of each row
+            // the ReLU output is zero), output by output from W2's rows
 #pragma unroll
-            for (int j = 0; j < HM; ++j) {
-                const float* r = wb + j * RW + FM;
-                float s = dy[0] * r[1];
-                s = fmaf(dy[1], r[2], s);
-                s = fmaf(dy[2], r[3], s);
-                s = fmaf(dy[3], r[4], s);
-                dpre[j] = h[j] > 0.0f ? s : 0.0f;
+            for (int o = 0; o < 4; ++o) {
+                if (o >= O) break;  // uniform
+                const float* w2 = wb + HM * RW + 8 + FM * HM + o * HM;
+#pragma unroll
+                for (int j = 0; j < HM; ++j) dpre[j] = fmaf(dy[o], w2[j], dpre[j]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int j = 0; j < HM; ++j) dpre[j] = h[j] > 0.0f ? dpre[j] : 0.0f;
             // each level's feature gradient (dpre against two columns of W1),
             // out to the level's slice; a loop that is not unrolled keeps one
             // level's values live at a time
@@ -289,7 +310,7 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
                     df0 = fmaf(dpre[j], c0[j], df0);
                     df1 = fmaf(dpre[j], c0[HM + j], df1);
                 }
-                *reinterpret_cast<float2*>(f.dfeat + 2 * ((size_t)l * a.n + p)) =
+                *reinterpret_cast<float2*>(f.dfeat + 2 * ((size_t)l * f.dstride + p)) =
                     make_float2(lv.mask * df0, lv.mask * df1);
             }
         }
@@ -336,6 +357,7 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
         }
     }
 
+    const int F = 2 * g.n_levels, H = a.hidden, O = a.n_out;
     // the wave's partial, into its own staging slice (which holds it: pm < 16
     // SW): W1, b1, W2, b2 gradients, then the squared-error sum (accumulator
     // lane n + 16 (m/4), register m%4 holds C[m][n])
@@ -371,11 +393,12 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_decode(GridArgs g, HashInrA
     }
 }
 
-// 64-bit fixed point of the table-gradient contributions: 2^-32 residual
-// units, contributions clamped to +-2^8 (a chunk of at most 2^17 points,
-// four corners each, then cannot overflow an entry's sum).
+// 64-bit fixed point of the table-gradient sums a thread adds at once: 2^-32
+// residual units, clamped to +-2^11 (a thread's run has at most 512 points;
+// an entry receives at most 4 x 2^17 such sums per chunk, so its sum stays
+// below 2^62).
 constexpr float kFixScale = 4294967296.0f;
-constexpr float kFixClamp = 256.0f;
+constexpr float kFixClamp = 2048.0f;
 
 __device__ __forceinline__ unsigned long long to_fixed(float v) {
     v = fminf(fmaxf(v, -kFixClamp), kFixClamp);
@@ -383,14 +406,17 @@ __device__ __forceinline__ unsigned long long to_fixed(float v) {
 }
 
 // Scatter jobs, in level order: each level of the LDS prefix in ranges of
-// kInrScatEntries entries, then one job per global-atomic level; blockIdx =
-// job * chunks + chunk.
+// kInrScatEntries entries, then one job per global-atomic level.  The jobs of
+// one chunk run on one XCD (workgroup ids that agree mod 8), where they share
+// the chunk's points in L2.
 template <int DIM>
 __global__ void __launch_bounds__(kInrThreads) k_inr_scatter(GridArgs g, HashInrArgs a, InrStep f) {
     extern __shared__ __attribute__((aligned(16))) unsigned long long acc[];  // [2 * kInrScatEntries]
     const int tid = threadIdx.x;
-    const int chunk = (int)(blockIdx.x % (unsigned)f.scat_chunks);
-    int job = (int)(blockIdx.x / (unsigned)f.scat_chunks);
+    const int xcd = (int)(blockIdx.x & 7u), slot = (int)(blockIdx.x >> 3);
+    int job = slot % f.scat_jobs;
+    const int chunk = (slot / f.scat_jobs) * 8 + xcd;
+    if (chunk >= f.scat_chunks) return;
     int l = 0, r0 = 0;
     for (; l < g.n_levels - 1; ++l) {
         const int ranges = l < f.lds_levels ? (g.size[l] + kInrScatEntries - 1) / kInrScatEntries : 1;
@@ -408,36 +434,53 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_scatter(GridArgs g, HashInr
     // changes: neighbouring points share the entries of coarse levels
     const int64_t p0 = (int64_t)chunk * f.scat_chunk;
     const int64_t p1 = p0 + f.scat_chunk < a.n ? p0 + f.scat_chunk : a.n;
-    const int64_t per = (p1 - p0 + kInrThreads - 1) / kInrThreads;
+    const int64_t per = f.scat_chunk / kInrThreads;  // a multiple of 4, also in a short last chunk
     const int64_t pb = p0 + (int64_t)tid * per;
-    const int64_t pe = pb + per < p1 ? pb + per : p1;
-    const float* dl = f.dfeat + 2 * (size_t)l * a.n;
+    const int64_t pe = pb + per < p1 ? pb + per : p1;  // pe <= pb: nothing to do
+    const float* dl = f.dfeat + 2 * (size_t)l * f.dstride;
     constexpr int NC = 1 << DIM;
     constexpr uint32_t kNone = 0xffffffffu;
+    // pending sums: float32, in the thread's own fixed order; rounded to
+    // fixed point when added to the LDS accumulators
     uint32_t pend[NC];
-    unsigned long long s0[NC], s1[NC];  // fixed point (LDS levels)
-    float g0[NC], g1[NC];               // float (global levels)
+    float g0[NC], g1[NC];
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
         pend[q] = kNone;
-        s0[q] = s1[q] = 0ull;
         g0[q] = g1[q] = 0.0f;
     }
     if (lv.mask != 0.0f) {
-        constexpr int U = 4;  // points whose loads are issued together
+        // 4 points per load group, 16-byte loads (x 16-byte aligned, runs
+        // starting at multiples of 4 points)
+        constexpr int U = 4;
         for (int64_t pg = pb; pg < pe; pg += U) {
             float ux[U][DIM];
             float2 dfs[U];
+            if (pg + U <= pe) {
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int64_t pi = pg + i < pe ? pg + i : pe - 1;
+                for (int i = 0; i < U * DIM; i += 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(a.x + pg * DIM + i);
 #pragma unroll
-                for (int k = 0; k < DIM; ++k) ux[i][k] = a.x[pi * DIM + k];
-                dfs[i] = *reinterpret_cast<const float2*>(dl + 2 * pi);
+                    for (int c = 0; c < 4; ++c) ux[(i + c) / DIM][(i + c) % DIM] = v[c];
+                }
+#pragma unroll
+                for (int i = 0; i < U; i += 2) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(dl + 2 * (pg + i));
+                    dfs[i] = make_float2(v[0], v[1]);
+                    dfs[i + 1] = make_float2(v[2], v[3]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    const int64_t pi = pg + i < pe ? pg + i : pe - 1;
+#pragma unroll
+                    for (int k = 0; k < DIM; ++k) ux[i][k] = a.x[pi * DIM + k];
+                    dfs[i] = *reinterpret_cast<const float2*>(dl + 2 * pi);
+                }
             }
 #pragma unroll
             for (int i = 0; i < U; ++i) {
-                if (pg + i >= pe) break;
+                if (pg + i >= pe) continue;
                 const float2 df = dfs[i];
                 uint32_t e[NC];
                 float wt[NC];
@@ -447,19 +490,18 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_scatter(GridArgs g, HashInr
                     if (use_lds) {
                         const uint32_t k = e[q] - lv.off - (uint32_t)r0;
                         const uint32_t key = k < (uint32_t)n_ent ? k : kNone;
-                        const unsigned long long v0 = key != kNone ? to_fixed(wt[q] * df.x) : 0ull;
-                        const unsigned long long v1 = key != kNone ? to_fixed(wt[q] * df.y) : 0ull;
+                        const float v0 = wt[q] * df.x, v1 = wt[q] * df.y;
                         if (key != pend[q]) {
                             if (pend[q] != kNone) {
-                                atomicAdd(acc + 2 * pend[q], s0[q]);
-                                atomicAdd(acc + 2 * pend[q] + 1, s1[q]);
+                                atomicAdd(acc + 2 * pend[q], to_fixed(g0[q]));
+                                atomicAdd(acc + 2 * pend[q] + 1, to_fixed(g1[q]));
                             }
                             pend[q] = key;
-                            s0[q] = v0;
-                            s1[q] = v1;
+                            g0[q] = v0;
+                            g1[q] = v1;
                         } else {
-                            s0[q] += v0;
-                            s1[q] += v1;
+                            g0[q] += v0;
+                            g1[q] += v1;
                         }
                     } else {
                         const float v0 = wt[q] * df.x, v1 = wt[q] * df.y;
@@ -483,8 +525,8 @@ __global__ void __launch_bounds__(kInrThreads) k_inr_scatter(GridArgs g, HashInr
         for (int q = 0; q < NC; ++q) {
             if (pend[q] == kNone) continue;
             if (use_lds) {
-                atomicAdd(acc + 2 * pend[q], s0[q]);
-                atomicAdd(acc + 2 * pend[q] + 1, s1[q]);
+                atomicAdd(acc + 2 * pend[q], to_fixed(g0[q]));
+                atomicAdd(acc + 2 * pend[q] + 1, to_fixed(g1[q]));
             } else {
                 atomicAdd(f.grad + 2 * (size_t)pend[q], f.dy_scale * g0[q]);
                 atomicAdd(f.grad + 2 * (size_t)pend[q] + 1, f.dy_scale * g1[q]);
@@ -578,6 +620,8 @@ void launch_hash_inr_step(const GridArgs& g, const HashInrArgs& a, hipStream_t s
     f.part_w = sh.part_w;
     f.scat_chunk = sh.scat_chunk;
     f.scat_chunks = sh.scat_chunks;
+    f.scat_jobs = sh.scat_jobs;
+    f.dstride = sh.dstride;
     f.dfeat = w.dfeat;
     f.part_dec = w.part_dec;
     f.part_tab = w.part_tab;
@@ -592,7 +636,7 @@ void launch_hash_inr_step(const GridArgs& g, const HashInrArgs& a, hipStream_t s
         launch_decode_dim<3>(g, a, sh, f, w.wpad, s);
     else
         launch_decode_dim<2>(g, a, sh, f, w.wpad, s);
-    const dim3 scat((unsigned)((int64_t)sh.scat_jobs * sh.scat_chunks));
+    const dim3 scat((unsigned)((int64_t)sh.scat_jobs * ((sh.scat_chunks + 7) / 8 * 8)));
     const size_t scat_lds = 16 * (size_t)kInrScatEntries;
     if (g.dim == 3)
         hipLaunchKernelGGL(k_inr_scatter<3>, scat, dim3(kInrThreads), scat_lds, s, g, a, f);

@@ -31,6 +31,12 @@ inline int inr_decoder_params(const GridArgs& g, int hidden, int n_out) {
     return hidden * 2 * g.n_levels + hidden + n_out * hidden + n_out;
 }
 
+// Floats per staged point of the decoder kernel: dpre | h | feat | 16, padded
+// to 20 mod 32 (LDS banks).
+constexpr int inr_stage_width(int hm, int fm) {
+    return (2 * hm + fm + 16) + ((20 - (2 * hm + fm + 16) % 32) + 32) % 32;
+}
+
 // Launch shape of one step.  The decoder is padded to hm hidden units and fm
 // features (multiples of 16, the MFMA tile).  The table gradients of the
 // first lds_levels levels (sizes grow with the level: a prefix) are
@@ -38,8 +44,8 @@ inline int inr_decoder_params(const GridArgs& g, int hidden, int n_out) {
 // by global atomics.
 struct InrShape {
     int hm, fm;               // padded hidden width (32, 64) and feature width (16, 32)
-    int stage_w;              // floats per staged point: dpre | h | feat | dy (16)
-    int weight_floats;        // padded decoder: hm rows of fm + 8 (W1 row, b1, W2 column, 0s), b2 [8], W1^T
+    int stage_w;              // floats per staged point: dpre | h | feat | dy (16), padded
+    int weight_floats;        // padded decoder: hm rows of fm + 8 (W1 row, b1, W2 column, 0s), b2 [8], W1^T, W2
     int pm;                   // decoder parameters
     int part_w;               // floats per decoder partial: decoder gradient, then the squared-error sum
     int groups;               // decoder workgroups
@@ -49,16 +55,17 @@ struct InrShape {
     int64_t lds_tab_floats;   // their table floats
     int64_t tab_floats;       // all table floats
     int scat_jobs;            // (level, range) pairs, plus one per global-atomic level
-    int64_t scat_chunk;       // points per scatter chunk
+    int64_t scat_chunk;       // points per scatter chunk: a multiple of 4 points per thread
     int scat_chunks;
+    int64_t dstride;          // points per level slice of the feature gradients (even)
 };
 
 inline InrShape inr_shape(const GridArgs& g, int hidden, int n_out, int64_t n) {
     InrShape s{};
     s.hm = hidden <= 32 ? 32 : 64;
     s.fm = 2 * g.n_levels <= 16 ? 16 : 32;
-    s.stage_w = 2 * s.hm + s.fm + 16;
-    s.weight_floats = s.hm * (s.fm + 8) + 8 + s.fm * s.hm;
+    s.stage_w = inr_stage_width(s.hm, s.fm);
+    s.weight_floats = s.hm * (s.fm + 8) + 8 + s.fm * s.hm + 4 * s.hm;
     s.tab_floats = inr_table_floats(g);
     s.pm = inr_decoder_params(g, hidden, n_out);
     s.part_w = (s.pm + 1 + 3) / 4 * 4;
@@ -80,17 +87,18 @@ inline InrShape inr_shape(const GridArgs& g, int hidden, int n_out, int64_t n) {
     s.lds_tab_floats = ltf;
     s.scat_jobs = jobs + (g.n_levels - k);
     int64_t chunk = (n * s.scat_jobs + kInrScatGroups - 1) / kInrScatGroups;
-    chunk = (chunk + kInrThreads - 1) / kInrThreads * kInrThreads;
-    if (chunk < 1024) chunk = 1024;
+    chunk = (chunk + 4 * kInrThreads - 1) / (4 * kInrThreads) * (4 * kInrThreads);
+    if (chunk < 4 * kInrThreads) chunk = 4 * kInrThreads;
     if (chunk > kInrMaxChunk) chunk = kInrMaxChunk;
     s.scat_chunk = chunk;
     s.scat_chunks = (int)((n + chunk - 1) / chunk);
     if (s.scat_chunks < 1) s.scat_chunks = 1;
+    s.dstride = (n + 1) / 2 * 2;
     return s;
 }
 
 struct InrWs {
-    float* dfeat;     // [levels][n][2]: feature gradients
+    float* dfeat;     // [levels][dstride][2]: feature gradients
     float* part_dec;  // [groups][part_w]: decoder-gradient and loss partials
     float* part_tab;  // [scat_chunks][lds_tab_floats]: table-gradient partials of the LDS levels
     float* grad;      // [parameters] when the caller gives none

@@ -107,7 +107,7 @@ size_t hash_inr_workspace_layout(const GridArgs& g, int hidden, int n_out, int64
     };
     const InrShape sh = inr_shape(g, hidden, n_out, n);
     InrWs w{};
-    w.dfeat = take(4 * (size_t)n * 2 * g.n_levels);
+    w.dfeat = take(4 * (size_t)sh.dstride * 2 * g.n_levels);
     w.part_dec = take(4 * (size_t)sh.groups * (size_t)sh.part_w);
     w.part_tab = take(4 * (size_t)sh.scat_chunks * (size_t)sh.lds_tab_floats);
     w.grad = take(4 * (size_t)hash_inr_param_count(g, hidden, n_out));
