@@ -117,6 +117,9 @@ WORKLOADS = {
     # one full-batch Adam step of the 2D hash-grid INR of "Instant-NGP - Visual Experiments", Experiment 2
     # (8 levels, T = 2^12, N 8..160, decoder 16 -> 32 -> 1, lr 1e-2) on its 96 x 96 image; the same model
     # on a 2048 x 2048 image (4.19M points per step)
+    # the page's video: a 24-frame 360 degree pose sweep (30 degrees elevation, radius 4), white background,
+    # coarse 64 + fine 128 on the two 8x256 networks, through nerf_render_poses
+    "sweep": dict(kind=0, frames=24, H=400, W=400, focal=555.0, nc=64, nf=128),
     "hash_inr": dict(kind=0, res=96, L=8, T=2 ** 12, nmin=8, nmax=160, hidden=32, lr=1e-2),
     "hash_inr_4m": dict(kind=0, res=2048, L=8, T=2 ** 12, nmin=8, nmax=160, hidden=32, lr=1e-2),
 }
@@ -443,6 +446,8 @@ def standalone(args, wl):
         return train_bench(args, wl)
     if name.startswith("hash_inr"):
         return inr_bench(args, wl)
+    if name == "sweep":
+        return sweep_bench(args, wl)
     if name == "mlp":
         Rm = wl["rays"]
         x = (ro[:Rm, None, :] + z[:Rm, :, None] * rd[:Rm, None, :]).reshape(-1, 3).contiguous()
@@ -661,6 +666,64 @@ def train_bench(args, wl):
                                                        10, 4, seed=0, mode=mode, ray_offset=s_))
         out_rec["cpu_baseline"] = _cpu_rate(fn, R, args.cpu_seconds, "rays/s", "rays (loss and every gradient)")
     print(json.dumps(out_rec), flush=True)
+
+
+def sweep_bench(args, wl):
+    """The page's pose-sweep video: every frame of a 360 degree sweep rendered
+    with the hierarchical sampler and the two 8x256 networks on a white
+    background (nerf_render_poses), against the MFMA roofline of the render."""
+    import torch
+    import seeded_inputs as si
+    import volume_rendering_amd as v
+    from volume_rendering_amd import _binding as B
+
+    dev = torch.device("cuda")
+    n, H, W, f, NC, NF = wl["frames"], wl["H"], wl["W"], wl["focal"], wl["nc"], wl["nf"]
+    dtype = 1 if args.dtype == "bf16" else 0
+    dt_name = "bf16" if dtype else "f32"
+    P = si.sweep_poses(n, elevation_deg=30.0)
+    pc = si.nerf_params(si.NERF_8x256, seed=0, net_id=0)
+    pf = si.nerf_params(si.NERF_8x256, seed=0, net_id=1)
+    nets = [v.weights.pack_to_device(1, dtype, pc), v.weights.pack_to_device(1, dtype, pf)]
+    w = B.nerf_weights(net=B.nerf_mlp_desc(1, dtype), coarse=nets[0].data_ptr(), fine=nets[1].data_ptr())
+    cfg = B.nerf_render_cfg(mode=B.NERF_MODE_NERF, n_coarse=NC, n_fine=NF, use_pi=1, white_bkgd=1, jitter=1, seed=0)
+    R = H * W
+    rgb = torch.empty((n, R, 3), device=dev)
+    depth = torch.empty((n, R), device=dev)
+    acc = torch.empty((n, R), device=dev)
+    ws = torch.empty(32 * R, dtype=torch.uint8, device=dev)
+
+    def step():
+        v.nerf_render_poses(P, W, H, f, f, 0.5 * W, 0.5 * H, 2.0, 6.0, w, cfg, rgb, depth, acc, workspace=ws)
+
+    ms_step, ms_kernel = _timed(args, step, torch)
+    rays = n * R
+    flops = 2.0 * MACS_8x256 * rays * (NC + NC + NF)
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    out = {
+        "metric": "pose-sweep frames/s (24 frames, 400x400, coarse64+fine128, 8x256, white background; MFMA util %)",
+        "value": n / (ms_step * 1e-3), "unit": "frames/s", "rays_per_sec": rays / (ms_step * 1e-3), "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt_name,
+        "data": "synthetic: seeded sweep poses, He-uniform random weights",
+        "config": {"workload": args.workload, "frames": n, "H": H, "W": W, "focal": f, "n_coarse": NC,
+                   "n_fine": NF, "net": "8x256", "white_bkgd": 1},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[dt_name], "unit": "TFLOP/s",
+                     "frac": achieved / PEAK[dt_name], "traffic": None, "kernel": "k_render_nerf (every frame)",
+                     "kernel_ms": ms_kernel, "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rays as orays
+        o_l, d_l = zip(*[orays.get_rays(H, W, f, f, 0.5 * W, 0.5 * H, P[k]) for k in range(n)])
+        ro, rd = np.concatenate(o_l), np.concatenate(d_l)
+        near, far = np.full(rays, 2.0, np.float32), np.full(rays, 6.0, np.float32)
+        rec = cpu_baseline(dict(wl, poses=n), 1, ro, rd, near, far, pc, pf, args.cpu_seconds)
+        for r in (rec, rec.get("single_thread", {})):
+            if "value" in r:
+                r["value"] /= R  # rays/s -> frames/s
+                r["unit"] = "frames/s"
+        out["cpu_baseline"] = rec
+    print(json.dumps(out), flush=True)
 
 
 def inr_bench(args, wl):
