@@ -388,6 +388,9 @@ __global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
 // Forward and input-gradient products in bfloat16 with the operand tiles
 // copied global -> LDS by direct buffer loads (no register staging), three
 // k-steps deep: while step t multiplies, steps t+1 and t+2 are in flight.
+// 2 x WC waves: two along the product's columns (the weights), WC along its
+// rows (the samples); more waves along the samples share one weight tile
+// among more samples.
 // A tile row is 64 bytes (32 k) whose four 16-byte pieces are XOR-swizzled
 // by row, so that the operand reads (32 rows at one k offset) fall in
 // distinct banks.  Each copy instruction fills 1 KB of LDS (16 rows); rows
@@ -407,12 +410,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* dst, uint3
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (NERF_AS_LDS void*)dst, 16, (int)off, 0, 0, 0);
 }
 
-template <int RB, int CB>
-__global__ void __launch_bounds__(256) k_gemm_nt_dma(GemmNT g) {
+template <int RB, int CB, int WC = 2>
+__global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
     using T = __bf16;
-    constexpr int TR = 64 * RB, TC = 64 * CB;
+    constexpr int NT = 128 * WC;  // threads
+    constexpr int TR = 64 * RB, TC = 32 * CB * WC;
     constexpr int STAGE = (TR + TC) * 64;  // bytes
-    constexpr int QR = TR / 64, QC = TC / 64;  // 1 KB copies per wave per step
+    constexpr int NW = NT / 64;                        // waves
+    constexpr int QR = TR / (16 * NW), QC = TC / (16 * NW);  // 1 KB (16-row) copies per wave per step
     constexpr int PH = 2 < RB ? 2 : RB;        // epilogue: block-rows per phase (128 bytes of features)
     constexpr int FW = 32 * PH;
     constexpr int SP = 2 * FW + 8;             // staged row pitch (elements)
@@ -506,6 +511,7 @@ __global__ void __launch_bounds__(256) k_gemm_nt_dma(GemmNT g) {
     __syncthreads();  // every wave is done with the ring before the epilogue reuses it
     // Epilogue through LDS (as k_gemm_nt): whole 128-byte lines per row
     constexpr int PPR = 2 * FW * 2 / 16;
+    static_assert(TC * PPR % NT == 0, "epilogue pieces per thread");
     T* st = reinterpret_cast<T*>(lds);
 #pragma unroll
     for (int p = 0; p < RB / PH; ++p) {
@@ -531,8 +537,8 @@ __global__ void __launch_bounds__(256) k_gemm_nt_dma(GemmNT g) {
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < TC * PPR / 256; ++q) {
-            const int u = tid + 256 * q;
+        for (int q = 0; q < TC * PPR / NT; ++q) {
+            const int u = tid + NT * q;
             const int ml = u / PPR, pc = u % PPR;
             const int half = pc / (PPR / 2), e0 = (pc % (PPR / 2)) * 8;
             const int m = m0 + ml;
@@ -895,7 +901,7 @@ namespace {
 void gemm_nt_dma(const GemmNT& g, hipStream_t s) {
     const unsigned gx4 = (unsigned)((g.M + 255) / 256), gx2 = (unsigned)((g.M + 127) / 128);
     if (g.N > 128)
-        hipLaunchKernelGGL((k_gemm_nt_dma<4, 2>), dim3(gx2, (unsigned)((g.N + 255) / 256)), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_nt_dma<4, 2, 4>), dim3(gx4, (unsigned)((g.N + 255) / 256)), dim3(512), 0, s, g);
     else if (g.N > 64)
         hipLaunchKernelGGL((k_gemm_nt_dma<2, 2>), dim3(gx2, 1), dim3(256), 0, s, g);
     else
