@@ -34,7 +34,7 @@ CASES = [
     # dim, levels, T, n_min, n_max, hidden, n_out, points, masked level
     (2, 8, 2 ** 12, 8, 160, 32, 1, 3000, None),
     (2, 6, 2 ** 10, 4, 96, 64, 3, 2500, 2),
-    (3, 4, 2 ** 12, 4, 32, 16, 2, 4000, None),
+    (3, 4, 2 ** 12, 4, 32, 16, 2, 4001, None),  # odd: padded level slices
 ]
 
 
@@ -214,3 +214,58 @@ def test_inr_table_size_trades_collisions_for_quality(v):
     assert sum(not d for d in small[1].direct) == 6 and sum(not d for d in large[1].direct) == 1
     assert small[-1] > 1e-4
     assert large[-1] < 1e-8
+
+
+def test_inr_step_is_deterministic(v):
+    """With every level at most 32,768 entries the table gradients are integer
+    sums: two runs of the same step give bit-identical gradients, loss and
+    parameters."""
+    from volume_rendering_amd import _binding as B
+    say("hash inr determinism")
+    g = B.nerf_hashgrid_init(8, 2 ** 12, 8, 160, dim=2)
+    og = encoding.HashGrid(2, 8, 2 ** 12, 8, 160)
+    assert max(og.sizes) <= 32768
+    tables, mlp = si.hash_inr_params(og.sizes, 8, 32, 1, seed=6)
+    flat = si.hash_inr_flat(tables, mlp)
+    coords, target = si.inr_target_image(64)
+    outs = []
+    for _ in range(2):
+        params, m, vv = dev(flat), dev(np.zeros_like(flat)), dev(np.zeros_like(flat))
+        grad, loss = empty(flat.size), empty(1)
+        v.nerf_hash_inr_train_step(dev(coords), dev(target), g, _cfg(B, 32, 1), params, loss, m, vv, 1, grad=grad)
+        outs.append((host(grad), host(loss), host(params)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_inr_gradients_levels_past_the_lds_ranges(v):
+    """Levels with more than 32,768 entries (here T = 2^16 with resolutions up
+    to 512) accumulate their table gradients with global float atomics; the
+    small levels still go through LDS.  Both against the oracle."""
+    from volume_rendering_amd import _binding as B
+    say("hash inr gradients, large levels (global atomics)")
+    L, T = 6, 2 ** 16
+    g = B.nerf_hashgrid_init(L, T, 16, 512, dim=2)
+    og = encoding.HashGrid(2, L, T, 16, 512)
+    assert max(og.sizes) > 32768 and min(og.sizes) <= 32768
+    tables, mlp = si.hash_inr_params(og.sizes, L, 32, 2, seed=9)
+    tables = [t * np.float32(1e3) for t in tables]
+    rng = si.rng(7, 53)
+    x = rng.random((5000, 2)).astype(np.float32)
+    target = rng.random((5000, 2)).astype(np.float32)
+    flat = si.hash_inr_flat(tables, mlp)
+    params, grad, loss = dev(flat), empty(flat.size), empty(1)
+    v.nerf_hash_inr_train_step(dev(x), dev(target), g, _cfg(B, 32, 2), params, loss, grad=grad)
+    ref_loss, _, dt, dm = hash_inr.forward_backward(og, tables, mlp, x, target)
+    got, ref = host(grad).astype(np.float64), hash_inr.flatten(dt, dm)
+    nt = 2 * sum(og.sizes)
+    assert abs(float(host(loss)[0]) - ref_loss) <= 1e-5 * ref_loss
+    off = 0
+    for l, size in enumerate(og.sizes):
+        a, b = got[off:off + 2 * size], ref[off:off + 2 * size]
+        e = np.max(np.abs(a - b)) / max(np.abs(ref[:nt]).max(), 1e-30)
+        say(f"  level {l} ({size} entries): max error {e:.2e} of the largest table gradient")
+        assert e <= 1e-4
+        off += 2 * size
+    e = np.max(np.abs(got[nt:] - ref[nt:])) / np.abs(ref[nt:]).max()
+    assert e <= 1e-4
