@@ -88,6 +88,10 @@ size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, 
         b.bias[l] = (float*)take(4 * (size_t)no);
     }
     b.wt_head = take(es * (size_t)p.W * (p.W + 32));
+    if (bf16) {
+        for (int l = 0; l < p.D; ++l) b.hbits[l] = (unsigned char*)take((size_t)S * p.W / 8);
+        b.gbits = (unsigned char*)take((size_t)S * p.ldG / 8);
+    }
     if (bufs_out) *static_cast<TrainBufs*>(bufs_out) = b;
     return off;
 }

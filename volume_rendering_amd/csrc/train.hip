@@ -81,6 +81,12 @@ struct GemmNT {
     int relu;
     const void* mask;   // keep C[m][n] only where mask[m*ldm + n] > 0, or NULL
     int ldm;
+    // bfloat16 direct-copy products only: the same mask as one bit per element
+    // (bit n%8 of byte bits_in[m*ldbits + n/8]); bits_out receives the bits of
+    // C > 0 as stored
+    const unsigned char* bits_in;
+    unsigned char* bits_out;
+    int ldbits;
     void* c;
     int ldc, c_col0, n_store, c_f32;  // stores columns n < n_store at c[m*ldc + c_col0 + n]
 };
@@ -549,13 +555,24 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
                     T e[8];
                 } x, mk;
                 x.u = *reinterpret_cast<const u32x4*>(st + ml * SP + half * FW + e0);
-                if (g.mask) {
+                if (g.bits_in) {
+                    const uint32_t mb = g.bits_in[(size_t)m * g.ldbits + n / 8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (!((mb >> e) & 1u)) x.e[e] = elt_from<T>(0.0f);
+                } else if (g.mask) {
                     mk.u = *reinterpret_cast<const u32x4*>((const T*)g.mask + (size_t)m * g.ldm + n);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if (!(elt_f(mk.e[e]) > 0.0f)) x.e[e] = elt_from<T>(0.0f);
                 }
                 *reinterpret_cast<u32x4*>((T*)g.c + (size_t)m * g.ldc + n) = x.u;
+                if (g.bits_out) {
+                    uint32_t mb = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mb |= (elt_f(x.e[e]) > 0.0f ? 1u : 0u) << e;
+                    g.bits_out[(size_t)m * g.ldbits + n / 8] = (unsigned char)mb;
+                }
             }
         }
         __syncthreads();
@@ -1033,6 +1050,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         g.c = H(l);
         g.ldc = W;
         g.n_store = W;
+        g.bits_out = b.hbits[l];  // bfloat16 steps only (NULL otherwise)
+        g.ldbits = W / 8;
         gemm_nt<T>(g, s);
     }
     {
@@ -1068,7 +1087,10 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         g.c = b.ptr[BG];
         g.ldc = p.ldG;
         g.n_store = p.ldG;
+        g.bits_out = b.gbits;
+        g.ldbits = p.ldG / 8;
         gemm_nt<T>(g, s);
+        g.bits_out = nullptr;
         g.a0 = SegA{b.ptr[BG], p.ldG, p.ldG, 1};  // rgb head -> raw columns 0..2
         g.a1 = SegA{};
         g.b = b.wf[RGB];
@@ -1103,6 +1125,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         g.N = p.ldG;
         g.mask = b.ptr[BG];
         g.ldm = p.ldG;
+        g.bits_in = b.gbits;  // used instead of mask where present
+        g.ldbits = p.ldG / 8;
         g.c = b.ptr[BDG];
         g.ldc = p.ldG;
         g.n_store = p.ldG;
@@ -1140,6 +1164,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         g.N = W;
         g.mask = H(D - 1);
         g.ldm = W;
+        g.bits_in = b.hbits[D - 1];
+        g.ldbits = W / 8;
         g.c = dh;
         g.ldc = W;
         g.n_store = W;
@@ -1165,6 +1191,8 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
             g.N = W;
             g.mask = H(l - 1);
             g.ldm = W;
+            g.bits_in = b.hbits[l - 1];
+            g.ldbits = W / 8;
             g.c = dh_next;
             g.ldc = W;
             g.n_store = W;

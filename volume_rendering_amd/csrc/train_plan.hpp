@@ -62,6 +62,11 @@ struct TrainBufs {
     void* wt[16];
     float* bias[16];
     void* wt_head;
+    // bfloat16 steps: one bit per hidden activation (and per direction-layer
+    // output), set where the stored value is > 0: the ReLU masks of the
+    // input-gradient products, 1/16 of the activations' bytes
+    unsigned char* hbits[16];
+    unsigned char* gbits;
 };
 
 
