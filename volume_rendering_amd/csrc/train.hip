@@ -404,6 +404,16 @@ __global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
 constexpr int kDmaStages = 3;
 constexpr uint32_t kDmaSkip = 0x7FFFF000u;  // offset beyond any tile: the copy reads zeros
 
+// Workgroup barrier over LDS traffic only: the wave's LDS operations are
+// complete, its global stores may still be in flight (__syncthreads() would
+// wait for those too).
+__device__ __forceinline__ void lds_barrier() {
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base, int bytes) {
@@ -428,11 +438,58 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
     constexpr int FW = 32 * PH;
     constexpr int SP = 2 * FW + 8;             // staged row pitch (elements)
     constexpr int RING = kDmaStages * STAGE, EPI = TC * SP * 2;
+    constexpr int PPR = 2 * FW * 2 / 16;  // epilogue: 16-byte pieces per staged row
+    constexpr int NPH = RB / PH, NQ = TC * PPR / NT;
+    static_assert(TC * PPR % NT == 0 && NT % PPR == 0, "epilogue pieces per thread");
     __shared__ __attribute__((aligned(1024))) char lds[RING > EPI ? RING : EPI];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
     const int n0 = blockIdx.y * TR, m0 = blockIdx.x * TC;
     const int K = g.a0.kpad + g.a1.kpad, nk = K / 32;
+    const int l32 = lane & 31, h = lane >> 5, sw = swz(l32);
+
+    // The bias (as the accumulators' start) and the epilogue's mask bits are
+    // loaded before the first copies, so that their latency overlaps the
+    // ring's fill instead of stalling the epilogue.
+    // Rows n >= N and pieces past M or N are never stored, so their loads
+    // read a clamped in-range address and keep whatever they get.  The loads
+    // land straight in their registers (one per output tile, the row offset
+    // hidden from the compiler so that it neither merges them nor waits for
+    // them before the products need them).
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            if (g.bias) {  // uniform
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    int n = n0 + wr * 32 * RB + 32 * i + 8 * gq + 4 * h;
+                    n = n < g.N ? n : 0;
+                    asm volatile("" : "+v"(n));
+                    const float4 x = *reinterpret_cast<const float4*>(g.bias + n);
+                    acc[i][j][4 * gq] = x.x;
+                    acc[i][j][4 * gq + 1] = x.y;
+                    acc[i][j][4 * gq + 2] = x.z;
+                    acc[i][j][4 * gq + 3] = x.w;
+                }
+            } else {
+                acc[i][j] = f32x16{};
+            }
+        }
+    // epilogue piece q of phase p: staged row tid / PPR + q * NT / PPR, piece tid % PPR
+    const int e_pc = tid % PPR, e_half = e_pc / (PPR / 2), e_e0 = (e_pc % (PPR / 2)) * 8;
+    uint32_t mbits[NPH][NQ];
+#pragma unroll
+    for (int p = 0; p < NPH; ++p)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int m = m0 + tid / PPR + q * (NT / PPR);
+            const int n = n0 + e_half * 32 * RB + p * FW + e_e0;
+            const size_t at = m < g.M && n < g.N ? (size_t)m * g.ldbits + n / 8 : 0;
+            mbits[p][q] = g.bits_in ? g.bits_in[at] : 0xFFu;
+        }
+    compiler_fence();
 
     // buffer resources over this tile's rows of the weights and of each activation segment
     const int nrows = g.N - n0 < TR ? g.N - n0 : TR;
@@ -480,22 +537,28 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
         for (int q = 0; q < QC; ++q)
             dma16(s0 ? rs[0] : rs[1], slot + TR * 64 + (wave * QC + q) * 1024, (s0 ? vc[0][q] : vc[1][q]) + ka);
     };
-    f32x16 acc[RB][CB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
-    const int l32 = lane & 31, h = lane >> 5, sw = swz(l32);
-    issue(0);
-    if (nk > 1) issue(1);
+    for (int t = 0; t < kDmaStages - 1; ++t)
+        if (t < nk) issue(t);
     for (int t = 0; t < nk; ++t) {
-        if (t + 1 < nk)
+        // steps issued after step t: min(stages - 2, nk - 1 - t)
+        const int later = nk - 1 - t < kDmaStages - 2 ? nk - 1 - t : kDmaStages - 2;
+        static_assert(kDmaStages >= 2 && kDmaStages <= 4, "waits below");
+        if (later >= 2)
+            wait_vm_lgkm0<2 * (QR + QC)>();
+        else if (later == 1)
             wait_vm_lgkm0<QR + QC>();
         else
             wait_vm_lgkm0<0>();
+        // A bare barrier: __syncthreads() would add the workgroup fence, which
+        // waits for every copy in flight (vmcnt(0)), the later steps' too.
+        // Each wave has waited for its own copies of step t and for its LDS
+        // reads of step t - 1 above, so after the barrier slot t is complete
+        // and the slot of step t + stages - 1 (that of t - 1) is free.
         compiler_fence();
-        __syncthreads();
-        if (t + 2 < nk) issue(t + 2);
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (t + kDmaStages - 1 < nk) issue(t + kDmaStages - 1);
         const char* slot = lds + (t % kDmaStages) * STAGE;
         const char* R = slot + (wr * 32 * RB) * 64;
         const char* C = slot + TR * 64 + (wc * 32 * CB) * 64;
@@ -516,11 +579,9 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
     }
     __syncthreads();  // every wave is done with the ring before the epilogue reuses it
     // Epilogue through LDS (as k_gemm_nt): whole 128-byte lines per row
-    constexpr int PPR = 2 * FW * 2 / 16;
-    static_assert(TC * PPR % NT == 0, "epilogue pieces per thread");
     T* st = reinterpret_cast<T*>(lds);
 #pragma unroll
-    for (int p = 0; p < RB / PH; ++p) {
+    for (int p = 0; p < NPH; ++p) {
 #pragma unroll
         for (int ii = 0; ii < PH; ++ii) {
             const int i = p * PH + ii;
@@ -530,33 +591,30 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int fl = 32 * ii + 8 * gq + 4 * h;
-                    const int n = n0 + wr * 32 * RB + 32 * i + 8 * gq + 4 * h;
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        v[e] = acc[i][j][4 * gq + e] + (g.bias && n < g.N ? g.bias[n + e] : 0.0f);
+                        v[e] = acc[i][j][4 * gq + e];
                         if (g.relu) v[e] = fmaxf(v[e], 0.0f);
                     }
                     store4<T>(st + ml * SP + wr * FW + fl, v);
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
-        for (int q = 0; q < TC * PPR / NT; ++q) {
-            const int u = tid + NT * q;
-            const int ml = u / PPR, pc = u % PPR;
-            const int half = pc / (PPR / 2), e0 = (pc % (PPR / 2)) * 8;
+        for (int q = 0; q < NQ; ++q) {
+            const int ml = tid / PPR + q * (NT / PPR);
             const int m = m0 + ml;
-            const int n = n0 + half * 32 * RB + p * FW + e0;
+            const int n = n0 + e_half * 32 * RB + p * FW + e_e0;
             if (m < g.M && n < g.N) {
                 union {
                     u32x4 u;
                     T e[8];
                 } x, mk;
-                x.u = *reinterpret_cast<const u32x4*>(st + ml * SP + half * FW + e0);
+                x.u = *reinterpret_cast<const u32x4*>(st + ml * SP + e_half * FW + e_e0);
                 if (g.bits_in) {
-                    const uint32_t mb = g.bits_in[(size_t)m * g.ldbits + n / 8];
+                    const uint32_t mb = mbits[p][q];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if (!((mb >> e) & 1u)) x.e[e] = elt_from<T>(0.0f);
@@ -575,7 +633,7 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
                 }
             }
         }
-        __syncthreads();
+        if (p + 1 < NPH) lds_barrier();
     }
 }
 
