@@ -3,6 +3,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "inr_plan.hpp"
 #include "launch.hpp"
 #include "nets.hpp"
@@ -55,9 +57,14 @@ size_t train_workspace_layout(int kind, int bf16, int64_t R, int N, char* base, 
         return base ? base + at : nullptr;
     };
     // about 128 splits of the samples for the weight gradients (whole
-    // multiples of 64, at least 512 samples each)
+    // multiples of 64, at least 512 samples each), and few enough samples
+    // per split that a split of the widest operand spans under 2^31 bytes
+    // (the weight-gradient products address a split with 32-bit offsets)
     const int64_t per = ((S + 127) / 128 + 63) / 64 * 64;
-    b.k_chunk = (int)(per > 512 ? per : 512);
+    int maxld = p.W;
+    for (int ld : {p.ldE, p.ldG, p.ldV}) maxld = ld > maxld ? ld : maxld;
+    const int64_t cap = (((int64_t)1 << 31) - 1) / ((int64_t)es * maxld) / 64 * 64;
+    b.k_chunk = (int)(per > 512 ? (per < cap ? per : cap) : 512);
     b.splits = (int)((S + b.k_chunk - 1) / b.k_chunk);
     b.ptr[BZ] = take(4 * (size_t)S);
     b.ptr[BE] = take(es * (size_t)S * p.ldE);

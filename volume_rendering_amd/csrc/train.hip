@@ -136,61 +136,84 @@ struct DirectTile {
     }
 };
 
-// One k-step x COLS columns of a k-major (columns contiguous) matrix,
-// transposed into LDS rows [column][k]: each unit loads PER k-rows of PER
-// columns (16 bytes each) and transposes the PER x PER block in registers.
-// Thread t takes units t - base (+256, ...).  k at or beyond k_end and
-// columns at or beyond C read as zero.
-template <class T, int COLS, int KB>
-struct TransTile {
-    static constexpr int PER = Tl<T, KB>::PER;
-    static constexpr int CU = COLS / PER;  // units across the columns
-    static constexpr int UNITS = (Tl<T, KB>::BK / PER) * CU;
-    static constexpr int UPT = (UNITS + 255) / 256;
+// One k-step of both operands of a weight-gradient product, k-major in
+// memory (columns contiguous), transposed into LDS rows [column][k]: TR
+// columns of A (the row tile), then TC columns of B (the column tile).  A
+// unit is PER k-rows x PER columns, 16 bytes per k-row, transposed in
+// registers; the units of both tiles are dealt to the threads in turn
+// (thread t takes units t, t + 256, ...), whole waves to one tile.  The loads
+// are buffer loads over the split's rows, issued by every thread whatever its
+// units: a unit past the last, a column past the matrix or a k past the split
+// gets an offset beyond the buffer and reads zeros.  With no branch around
+// them the compiler counts the loads in flight exactly and waits for the one
+// step it stores, not for the step behind it.  RD: B's row of sample k is
+// k / row_div.
+template <class T, int TR, int TC, int KB, bool RD>
+struct TnTiles {
+    static constexpr int PER = Tl<T, KB>::PER, BK = Tl<T, KB>::BK, P = Tl<T, KB>::P;
+    static constexpr int KU = BK / PER;  // units along k
+    static constexpr int RU = KU * (TR / PER), UNITS = RU + KU * (TC / PER);
+    static constexpr int NU = (UNITS + 255) / 256;  // units per thread
+    static_assert(RU % 64 == 0 && UNITS % 64 == 0, "units in whole waves");
     union Piece {
         u32x4 u;
         T e[PER];
     };
-    Piece v[UPT][PER];
+    __amdgpu_buffer_rsrc_t rs[NU];  // wave-uniform: A's or B's
+    bool of_b[NU];                  // wave-uniform
+    int ld[NU], c[NU], kq[NU], dst[NU];
+    bool live[NU];
+    int row_div, first_b;
+    Piece v[2][NU][PER];  // two steps in flight
 
-    __device__ __forceinline__ void load(const T* src, int ld, int row_div, int c0, int C, int k0, int k_end,
-                                         int t) {
+    __device__ __forceinline__ void setup(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const GemmTN& g,
+                                          int m0, int n0, int first, int tid) {
+        const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
+        row_div = g.b_row_div;
+        first_b = first;
 #pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            const int u = t + 256 * q;
-#pragma unroll
-            for (int r = 0; r < PER; ++r) v[q][r].u = u32x4{0u, 0u, 0u, 0u};
-            if (u >= 0 && u < UNITS) {
-                const int c = c0 + (u % CU) * PER;
-                const int kb = k0 + (u / CU) * PER;
-                if (c < C) {
-#pragma unroll
-                    for (int r = 0; r < PER; ++r) {
-                        const int k = kb + r;
-                        if (k < k_end) {
-                            const int row = row_div == 1 ? k : k / row_div;
-                            v[q][r].u = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + c);
-                        }
-                    }
-                }
-            }
+        for (int q = 0; q < NU; ++q) {
+            const int w0 = wave_base + 256 * q;  // the wave's first unit
+            const bool is_a = w0 < RU;
+            of_b[q] = !is_a;
+            rs[q] = is_a ? ra : rb;
+            ld[q] = is_a ? g.lda : g.ldb;
+            const int u = tid + 256 * q - (is_a ? 0 : RU);
+            const int cu = (is_a ? TR : TC) / PER;  // units across the columns
+            const int cl = (u % cu) * PER;
+            kq[q] = (u / cu) * PER;
+            c[q] = (is_a ? m0 : n0) + cl;
+            live[q] = w0 < UNITS && c[q] < (is_a ? g.M : g.N);
+            dst[q] = (is_a ? 0 : TR * P) + cl * P + kq[q];
         }
     }
-    __device__ __forceinline__ void store(T* lds, int t) const {
+    // k-rows k0 + kq .. of every unit into buffer b; k0 relative to the split start kb
+    __device__ __forceinline__ void load(int b, int kb, int k0, int k_len) {
 #pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            const int u = t + 256 * q;
-            if (u >= 0 && u < UNITS) {
-                const int col = (u % CU) * PER, kq = (u / CU) * PER;
+        for (int q = 0; q < NU; ++q)
 #pragma unroll
-                for (int c = 0; c < PER; ++c) {
+            for (int r = 0; r < PER; ++r) {
+                const int k = k0 + kq[q] + r;  // within the split
+                int row = k;
+                if constexpr (RD)
+                    if (of_b[q]) row = (kb + k) / row_div - first_b;
+                const uint32_t off =
+                    live[q] && k < k_len ? (uint32_t)((row * ld[q] + c[q]) * (int)sizeof(T)) : 0x7FFFF000u;
+                v[b][q][r].u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[q], (int)off, 0, 0));
+            }
+    }
+    __device__ __forceinline__ void store(int b, T* lds) const {
+#pragma unroll
+        for (int q = 0; q < NU; ++q)
+            if (live[q]) {
+#pragma unroll
+                for (int cc = 0; cc < PER; ++cc) {
                     Piece w;
 #pragma unroll
-                    for (int r = 0; r < PER; ++r) w.e[r] = v[q][r].e[c];
-                    *reinterpret_cast<u32x4*>(lds + (col + c) * Tl<T, KB>::P + kq) = w.u;
+                    for (int r = 0; r < PER; ++r) w.e[r] = v[b][q][r].e[cc];
+                    *reinterpret_cast<u32x4*>(lds + dst[q] + cc * P) = w.u;
                 }
             }
-        }
     }
 };
 
@@ -637,16 +660,12 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
     }
 }
 
-// Weight gradients, k-steps of 128 bytes per row.  When both tiles' units
-// fit one pass of the workgroup, the row tile is loaded by the first threads
-// and the column tile by the rest.
-template <class T, int RB, int CB>
+// Weight gradients, k-steps of 128 bytes per row, two steps of loads in
+// flight in registers while the step in LDS is multiplied.
+template <class T, int RB, int CB, bool RD>
 __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     constexpr int KB = 128;
     constexpr int P = Tl<T, KB>::P, BK = Tl<T, KB>::BK, TR = 64 * RB, TC = 64 * CB;
-    using RT = TransTile<T, TR, KB>;
-    using CT = TransTile<T, TC, KB>;
-    constexpr int CBASE = RT::UNITS + CT::UNITS <= 256 ? RT::UNITS : 0;
     __shared__ __attribute__((aligned(16))) T lds[2][(TR + TC) * P];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
@@ -663,39 +682,44 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     const int m0 = mt * TR, n0 = nt * TC;
     const int kb = split * g.k_chunk;
     const int ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
+    const int kl = ke - kb;
     const bool bias = g.bpart && nt == 0 && tid < TR;
-    RT rt;
-    CT ct;
     f32x16 acc[RB][CB];
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
     float bsum = 0.0f;
-    auto load = [&](int k0) {
-        rt.load((const T*)g.a, g.lda, 1, m0, g.M, k0, ke, tid);
-        ct.load((const T*)g.b, g.ldb, g.b_row_div, n0, g.N, k0, ke, tid - CBASE);
-    };
-    auto store = [&](T* l) {
-        rt.store(l, tid);
-        ct.store(l + TR * P, tid - CBASE);
-    };
-    load(kb);
-    store(lds[0]);
-    __syncthreads();
-    int buf = 0;
-    for (int k0 = kb; k0 < ke; k0 += BK) {
-        const bool more = k0 + BK < ke;
-        if (more) load(k0 + BK);
+    // buffer resources over the split's rows of both operands
+    const int bfirst = kb / g.b_row_div, blast = (ke - 1) / g.b_row_div;
+    const __amdgpu_buffer_rsrc_t ra = dma_rsrc((const T*)g.a + (size_t)kb * g.lda, kl * g.lda * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rb =
+        dma_rsrc((const T*)g.b + (size_t)bfirst * g.ldb, (blast - bfirst + 1) * g.ldb * (int)sizeof(T));
+    TnTiles<T, TR, TC, KB, RD> tt;
+    tt.setup(ra, rb, g, m0, n0, bfirst, tid);
+    // an even number of steps (a step past the split multiplies zeros)
+    const int ns = ((kl + BK - 1) / BK + 1) / 2 * 2;
+    tt.load(0, kb, 0, kl);
+    tt.store(0, lds[0]);
+    tt.load(1, kb, BK, kl);
+    tt.load(0, kb, 2 * BK, kl);
+    lds_barrier();
+    // step s is in lds[s % 2], steps s + 1 and s + 2 in register buffers (s + 1) % 2 and s % 2
+    auto step = [&](auto par, int s) {
+        constexpr int p = decltype(par)::value;
         if (bias) {
-            const T* row = lds[buf] + tid * P;
+            const T* row = lds[p] + tid * P;
 #pragma unroll
             for (int k = 0; k < BK; ++k) bsum += elt_f(row[k]);
         }
-        wave_mma<T, RB, CB, KB>(acc, lds[buf] + wr * 32 * RB * P, lds[buf] + TR * P + wc * 32 * CB * P, lane);
-        if (more) store(lds[buf ^ 1]);
-        __syncthreads();
-        buf ^= 1;
+        wave_mma<T, RB, CB, KB>(acc, lds[p] + wr * 32 * RB * P, lds[p] + TR * P + wc * 32 * CB * P, lane);
+        tt.store(p ^ 1, lds[p ^ 1]);
+        tt.load(p ^ 1, kb, (s + 3) * BK, kl);
+        lds_barrier();
+    };
+    for (int s = 0; s < ns; s += 2) {
+        step(IntC<0>{}, s);
+        step(IntC<1>{}, s + 1);
     }
     float* out = g.part + (size_t)split * g.M * g.N;
     const int l32 = lane & 31, h = lane >> 5;
@@ -1023,14 +1047,19 @@ void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int row
     const int RB = rows_pad > 64 ? 2 : 1, CB = cols_pad > 64 ? 2 : 1;
     const int tiles = ((rows_pad + 64 * RB - 1) / (64 * RB)) * ((cols_pad + 64 * CB - 1) / (64 * CB));
     const dim3 grid((unsigned)(tiles * ((b.splits + 7) / 8 * 8)));  // XCD-grouped, see k_gemm_tn
-    if (RB == 2 && CB == 2)
-        hipLaunchKernelGGL((k_gemm_tn<T, 2, 2>), grid, dim3(256), 0, s, g);
+    if (row_div != 1) {  // B rows per ray: the direction encodings, 32 columns in every network
+        if (RB == 2)
+            hipLaunchKernelGGL((k_gemm_tn<T, 2, 1, true>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((k_gemm_tn<T, 1, 1, true>), grid, dim3(256), 0, s, g);
+    } else if (RB == 2 && CB == 2)
+        hipLaunchKernelGGL((k_gemm_tn<T, 2, 2, false>), grid, dim3(256), 0, s, g);
     else if (RB == 2)
-        hipLaunchKernelGGL((k_gemm_tn<T, 2, 1>), grid, dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_tn<T, 2, 1, false>), grid, dim3(256), 0, s, g);
     else if (CB == 2)
-        hipLaunchKernelGGL((k_gemm_tn<T, 1, 2>), grid, dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_tn<T, 1, 2, false>), grid, dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL((k_gemm_tn<T, 1, 1>), grid, dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_tn<T, 1, 1, false>), grid, dim3(256), 0, s, g);
     const int64_t n = (int64_t)rows * ((cols + 3) / 4);
     hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BPART],
                        b.splits, rows_pad, cols_pad, rows, cols, grad, w_off, in_total, col0);
