@@ -178,10 +178,11 @@ struct TnTiles {
             of_b[q] = !is_a;
             rs[q] = is_a ? ra : rb;
             ld[q] = is_a ? g.lda : g.ldb;
+            // consecutive units step through k first: the 64 lanes of one
+            // LDS store then cover 16 distinct 16-byte bank groups
             const int u = tid + 256 * q - (is_a ? 0 : RU);
-            const int cu = (is_a ? TR : TC) / PER;  // units across the columns
-            const int cl = (u % cu) * PER;
-            kq[q] = (u / cu) * PER;
+            const int cl = (u / KU) * PER;
+            kq[q] = (u % KU) * PER;
             c[q] = (is_a ? m0 : n0) + cl;
             live[q] = w0 < UNITS && c[q] < (is_a ? g.M : g.N);
             dst[q] = (is_a ? 0 : TR * P) + cl * P + kq[q];
@@ -660,6 +661,31 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
     }
 }
 
+// s + the N elements of an LDS row (16-byte aligned), in a fixed order.
+template <class T, int N>
+__device__ __forceinline__ float row_sum(const T* row, float s) {
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int k = 0; k < N; k += 8) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + k);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[e], x[e + 1]}, one, s, false);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; k += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(row + k);
+            s += x.x;
+            s += x.y;
+            s += x.z;
+            s += x.w;
+        }
+    }
+    return s;
+}
+
 // Weight gradients, k-steps of 128 bytes per row, two steps of loads in
 // flight in registers while the step in LDS is multiplied.
 template <class T, int RB, int CB, bool RD>
@@ -707,11 +733,7 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     // step s is in lds[s % 2], steps s + 1 and s + 2 in register buffers (s + 1) % 2 and s % 2
     auto step = [&](auto par, int s) {
         constexpr int p = decltype(par)::value;
-        if (bias) {
-            const T* row = lds[p] + tid * P;
-#pragma unroll
-            for (int k = 0; k < BK; ++k) bsum += elt_f(row[k]);
-        }
+        if (bias) bsum = row_sum<T, BK>(lds[p] + tid * P, bsum);
         wave_mma<T, RB, CB, KB>(acc, lds[p] + wr * 32 * RB * P, lds[p] + TR * P + wc * 32 * CB * P, lane);
         tt.store(p ^ 1, lds[p ^ 1]);
         tt.load(p ^ 1, kb, (s + 3) * BK, kl);
