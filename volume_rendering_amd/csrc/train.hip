@@ -1022,7 +1022,7 @@ namespace {
 void gemm_nt_dma(const GemmNT& g, hipStream_t s) {
     const unsigned gx4 = (unsigned)((g.M + 255) / 256), gx2 = (unsigned)((g.M + 127) / 128);
     if (g.N > 128)
-        hipLaunchKernelGGL((k_gemm_nt_dma<4, 2, 4>), dim3(gx4, (unsigned)((g.N + 255) / 256)), dim3(512), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_nt_dma<4, 2, 2>), dim3(gx2, (unsigned)((g.N + 255) / 256)), dim3(256), 0, s, g);
     else if (g.N > 64)
         hipLaunchKernelGGL((k_gemm_nt_dma<2, 2>), dim3(gx2, 1), dim3(256), 0, s, g);
     else
