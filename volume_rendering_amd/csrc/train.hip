@@ -760,28 +760,64 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     if (bias && m0 + tid < g.M) g.bpart[(size_t)split * g.M + m0 + tid] = bsum;
 }
 
-// grad[off + m*ld + col0 + n] = sum over splits (in order) of part[s][m][n],
-// for m < rows, n < cols; N a multiple of 4 (each thread sums 4 columns).
-__global__ void __launch_bounds__(256) k_reduce(const float* part, int splits, int M, int N, int rows, int cols,
-                                                float* grad, int64_t off, int ld, int col0) {
-    const int cq = (cols + 3) / 4;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)rows * cq) return;
-    const int m = (int)(t / cq), n = 4 * (int)(t % cq);
+// out[off + m*ld + col0 + n] = sum over splits of part[s][m][n], for m < rows,
+// n < cols; N a multiple of 4.  A workgroup takes 32 column quads; its 8
+// groups of 32 threads sum every 8th split each (group g: splits g, g + 8,
+// ... in order), and the group sums are added in group order, a fixed order
+// on every call.
+struct RedJob {
+    const float* part;
+    int M, N, rows, cols;
+    float* out;
+    int64_t off;
+    int ld, col0;
+    int blocks;  // workgroups of this job
+};
+constexpr int kRedGroups = 8;
+
+inline RedJob red_job(const float* part, int M, int N, int rows, int cols, float* out, int64_t off, int ld, int col0) {
+    const int64_t quads = (int64_t)rows * ((cols + 3) / 4);
+    return RedJob{part, M, N, rows, cols, out, off, ld, col0, (int)((quads + 31) / 32)};
+}
+
+// Two reductions in one launch: job a's workgroups, then job b's (b.blocks 0: none).
+__global__ void __launch_bounds__(256) k_reduce(RedJob a, RedJob b, int splits) {
+    __shared__ float4 red[kRedGroups][32];
+    const bool first = (int)blockIdx.x < a.blocks;
+    const RedJob& j = first ? a : b;
+    const int blk = first ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
+    const int l32 = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const int cq = (j.cols + 3) / 4;
+    const int64_t t = (int64_t)blk * 32 + l32;
+    const bool ok = t < (int64_t)j.rows * cq;
+    const int m = ok ? (int)(t / cq) : 0, n = ok ? 4 * (int)(t % cq) : 0;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int q = 0; q < splits; ++q) {
-        const float4 x = *reinterpret_cast<const float4*>(part + ((size_t)q * M + m) * N + n);
+    if (ok) {
+#pragma unroll 4
+        for (int q = grp; q < splits; q += kRedGroups) {
+            const float4 x = *reinterpret_cast<const float4*>(j.part + ((size_t)q * j.M + m) * j.N + n);
+            s.x += x.x;
+            s.y += x.y;
+            s.z += x.z;
+            s.w += x.w;
+        }
+    }
+    red[grp][l32] = s;
+    __syncthreads();
+    if (grp != 0 || !ok) return;
+#pragma unroll
+    for (int g2 = 1; g2 < kRedGroups; ++g2) {
+        const float4 x = red[g2][l32];
         s.x += x.x;
         s.y += x.y;
         s.z += x.z;
         s.w += x.w;
     }
     const float v[4] = {s.x, s.y, s.z, s.w};
-    float* o = grad + off + (int64_t)m * ld + col0 + n;
+    float* o = j.out + j.off + (int64_t)m * j.ld + j.col0 + n;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        if (n + e < cols) o[e] = v[e];
+        if (n + e < j.cols) o[e] = v[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -799,23 +835,35 @@ struct AsmArgs {
     int rows, ld, f32, nblocks;
     AsmBlock b[2];
 };
+// Up to kAsmJobs matrices per launch; job q covers elements start[q] ..
+// start[q + 1] - 1 of the launch.
+constexpr int kAsmJobs = 16;
+struct AsmBatch {
+    int n;
+    int64_t start[kAsmJobs + 1];
+    AsmArgs job[kAsmJobs];
+};
 
 template <class T>
-__global__ void __launch_bounds__(256) k_assemble(AsmArgs a, const float* flat) {
+__global__ void __launch_bounds__(256) k_assemble(AsmBatch bt, const float* flat) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)a.rows * a.ld) return;
-    const int r = (int)(t / a.ld), c = (int)(t % a.ld);
+    if (t >= bt.start[bt.n]) return;
+    int q = 0;
+    while (q + 1 < bt.n && t >= bt.start[q + 1]) ++q;
+    const AsmArgs& a = bt.job[q];
+    const int64_t e = t - bt.start[q];
+    const int r = (int)(e / a.ld), c = (int)(e % a.ld);
     float v = 0.0f;
-    for (int q = 0; q < a.nblocks; ++q) {
-        const AsmBlock& k = a.b[q];
-        const int i = r - k.r0, j = c - k.c0;
-        if (i >= 0 && i < k.nr && j >= 0 && j < k.nc)
-            v = flat[k.src + (k.transpose ? (int64_t)j * k.src_ld + i : (int64_t)i * k.src_ld + j)];
+    for (int k = 0; k < a.nblocks; ++k) {
+        const AsmBlock& bk = a.b[k];
+        const int i = r - bk.r0, j = c - bk.c0;
+        if (i >= 0 && i < bk.nr && j >= 0 && j < bk.nc)
+            v = flat[bk.src + (bk.transpose ? (int64_t)j * bk.src_ld + i : (int64_t)i * bk.src_ld + j)];
     }
     if (a.f32)
-        ((float*)a.dst)[t] = v;
+        ((float*)a.dst)[e] = v;
     else
-        ((T*)a.dst)[t] = elt_from<T>(v);
+        ((T*)a.dst)[e] = elt_from<T>(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1082,27 +1130,39 @@ void grad_w(const TrainBufs& b, const void* dpre, int ld_dpre, int rows, int row
         hipLaunchKernelGGL((k_gemm_tn<T, 1, 2, false>), grid, dim3(256), 0, s, g);
     else
         hipLaunchKernelGGL((k_gemm_tn<T, 1, 1, false>), grid, dim3(256), 0, s, g);
-    const int64_t n = (int64_t)rows * ((cols + 3) / 4);
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)b.ptr[BPART],
-                       b.splits, rows_pad, cols_pad, rows, cols, grad, w_off, in_total, col0);
-    if (b_off >= 0)  // bias partials [split][rows_pad]: one row of rows_pad columns per split
-        hipLaunchKernelGGL(k_reduce, dim3((unsigned)((rows + 3) / 4 + 255) / 256), dim3(256), 0, s,
-                           (const float*)b.ptr[BBPART], b.splits, 1, rows_pad, 1, rows, grad, b_off, 0, 0);
+    const RedJob rw = red_job((const float*)b.ptr[BPART], rows_pad, cols_pad, rows, cols, grad, w_off, in_total, col0);
+    // bias partials [split][rows_pad]: one row of rows_pad columns per split
+    RedJob rbias = red_job((const float*)b.ptr[BBPART], 1, rows_pad, 1, rows, grad, b_off, 0, 0);
+    if (b_off < 0) rbias.blocks = 0;
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)(rw.blocks + rbias.blocks)), dim3(256), 0, s, rw, rbias, b.splits);
 }
 
+// Collects weight-assembly jobs and launches them kAsmJobs at a time.
 template <class T>
-void assemble(void* dst, int rows, int ld, int f32, std::initializer_list<AsmBlock> blocks, const float* flat,
-              hipStream_t s) {
-    AsmArgs a{};
-    a.dst = dst;
-    a.rows = rows;
-    a.ld = ld;
-    a.f32 = f32;
-    a.nblocks = 0;
-    for (const AsmBlock& k : blocks) a.b[a.nblocks++] = k;
-    const int64_t n = (int64_t)rows * ld;
-    hipLaunchKernelGGL(k_assemble<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, flat);
-}
+struct Assembler {
+    const float* flat;
+    hipStream_t s;
+    AsmBatch bt{};
+
+    void add(void* dst, int rows, int ld, int f32, std::initializer_list<AsmBlock> blocks) {
+        if (bt.n == kAsmJobs) flush();
+        AsmArgs& a = bt.job[bt.n];
+        a = AsmArgs{};
+        a.dst = dst;
+        a.rows = rows;
+        a.ld = ld;
+        a.f32 = f32;
+        for (const AsmBlock& k : blocks) a.b[a.nblocks++] = k;
+        bt.start[bt.n + 1] = bt.start[bt.n] + (int64_t)rows * ld;
+        ++bt.n;
+    }
+    void flush() {
+        if (bt.n == 0) return;
+        const int64_t n = bt.start[bt.n];
+        hipLaunchKernelGGL(k_assemble<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bt, flat);
+        bt = AsmBatch{};
+    }
+};
 
 template <class T>
 void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
@@ -1117,6 +1177,7 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
     float* grad = t.grad ? t.grad : (float*)b.ptr[BGRAD];
 
     // --- weights of this step ------------------------------------------------
+    Assembler<T> as{t.params, s};
     for (int l = 0; l < nl; ++l) {
         const int no = pad32(L[l].n_out);
         const int w1 = L[l].s0.width, w2 = L[l].s1.width;
@@ -1124,18 +1185,18 @@ void train_step_t(int kind, const TrainArgs& t, hipStream_t s) {
         const int k2 = L[l].s1.kind == SEG_NONE ? 0 : (l == DIR ? p.ldV : p.ldE);
         const int it = p.in_total[l];
         if (k2)
-            assemble<T>(b.wf[l], no, k1 + k2, 0,
-                        {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0},
-                         AsmBlock{0, k1, L[l].n_out, w2, p.w_off[l] + w1, it, 0}},
-                        t.params, s);
+            as.add(b.wf[l], no, k1 + k2, 0,
+                   {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0},
+                    AsmBlock{0, k1, L[l].n_out, w2, p.w_off[l] + w1, it, 0}});
         else
-            assemble<T>(b.wf[l], no, k1, 0, {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0}}, t.params, s);
-        assemble<T>(b.wt[l], k1, no, 0, {AsmBlock{0, 0, w1, L[l].n_out, p.w_off[l], it, 1}}, t.params, s);
-        assemble<T>(b.bias[l], 1, no, 1, {AsmBlock{0, 0, 1, L[l].n_out, p.b_off[l], 0, 0}}, t.params, s);
+            as.add(b.wf[l], no, k1, 0, {AsmBlock{0, 0, L[l].n_out, w1, p.w_off[l], it, 0}});
+        as.add(b.wt[l], k1, no, 0, {AsmBlock{0, 0, w1, L[l].n_out, p.w_off[l], it, 1}});
+        as.add(b.bias[l], 1, no, 1, {AsmBlock{0, 0, 1, L[l].n_out, p.b_off[l], 0, 0}});
     }
     // d(last hidden) = [dF, dSIG] [W_feature^T ; W_sigma^T]
-    assemble<T>(b.wt_head, W, W + 32, 0,
-                {AsmBlock{0, 0, W, W, p.w_off[FEAT], W, 1}, AsmBlock{0, W, W, 1, p.w_off[SIG], W, 1}}, t.params, s);
+    as.add(b.wt_head, W, W + 32, 0,
+           {AsmBlock{0, 0, W, W, p.w_off[FEAT], W, 1}, AsmBlock{0, W, W, 1, p.w_off[SIG], W, 1}});
+    as.flush();
 
     // --- samples and encodings -----------------------------------------------
     hipLaunchKernelGGL(k_train_samples<T>, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, s, t.ro, t.rd, t.tn, t.tf,
