@@ -73,7 +73,7 @@ MEASURED_TRAFFIC = {
     ("hierarchical", "bf16"): (5.126e8, "b9b094be69258203"),   # k_render_nerf per launch
     ("kilo", "bf16"): (1.5036e9, "49519a6fc6d0269f"),          # every kernel of one render
     ("hashgrid", "f32"): (6.4763e9, "3f1ceb18a0ea427d"),       # both encoder kernels
-    ("train", "bf16"): (9.2331e9, "dd0d519f36571d53"),       # every kernel of one step
+    ("train", "bf16"): (9.2289e9, "f83e6240bdb50d04"),       # every kernel of one step
     ("hash_inr", "f32"): (6.49e6, "5be48abb4303c8d5"),         # every kernel of one step, 96 x 96
     ("hash_inr_4m", "f32"): (7.645e8, "5be48abb4303c8d5"),     # every kernel of one step, 2048 x 2048
 }
