@@ -70,12 +70,12 @@ KERNEL_SOURCES = {
     "hash_inr_4m": _INR_SOURCES,
 }
 MEASURED_TRAFFIC = {
-    ("hierarchical", "bf16"): (5.126e8, "b9b094be69258203"),   # k_render_nerf per launch
-    ("kilo", "bf16"): (1.5036e9, "49519a6fc6d0269f"),          # every kernel of one render
-    ("hashgrid", "f32"): (6.4763e9, "3f1ceb18a0ea427d"),       # both encoder kernels
-    ("train", "bf16"): (9.2289e9, "f83e6240bdb50d04"),       # every kernel of one step
-    ("hash_inr", "f32"): (6.49e6, "5be48abb4303c8d5"),         # every kernel of one step, 96 x 96
-    ("hash_inr_4m", "f32"): (7.645e8, "5be48abb4303c8d5"),     # every kernel of one step, 2048 x 2048
+    ("hierarchical", "bf16"): (5.1259e8, "d41e3b55704e15e6"),   # k_render_nerf per launch
+    ("kilo", "bf16"): (1.5028e9, "92b690704e7eddf5"),          # every kernel of one render
+    ("hashgrid", "f32"): (6.4912e9, "839a66438431fb16"),       # both encoder kernels
+    ("train", "bf16"): (9.225e9, "54401cb6260c4e92"),       # every kernel of one step
+    ("hash_inr", "f32"): (6.48e6, "e4dfd796db811fbe"),         # every kernel of one step, 96 x 96
+    ("hash_inr_4m", "f32"): (7.62e8, "e4dfd796db811fbe"),     # every kernel of one step, 2048 x 2048
 }
 
 
