@@ -160,14 +160,16 @@ struct TnTiles {
         T e[PER];
     };
     __amdgpu_buffer_rsrc_t rs[NU];  // wave-uniform: A's or B's
+    const char* base[NU];           // wave-uniform: the split's first row of A or B
     bool of_b[NU];                  // wave-uniform
     int ld[NU], c[NU], kq[NU], dst[NU];
     bool live[NU];
+    uint32_t voff[NU][PER];  // without RD: byte offset of each piece from its step's first row
     int row_div, first_b;
     Piece v[2][NU][PER];  // two steps in flight
 
-    __device__ __forceinline__ void setup(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const GemmTN& g,
-                                          int m0, int n0, int first, int tid) {
+    __device__ __forceinline__ void setup(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const char* pa,
+                                          const char* pb, const GemmTN& g, int m0, int n0, int first, int tid) {
         const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
         row_div = g.b_row_div;
         first_b = first;
@@ -177,6 +179,7 @@ struct TnTiles {
             const bool is_a = w0 < RU;
             of_b[q] = !is_a;
             rs[q] = is_a ? ra : rb;
+            base[q] = is_a ? pa : pb;
             ld[q] = is_a ? g.lda : g.ldb;
             // consecutive units step through k first: the 64 lanes of one
             // LDS store then cover 16 distinct 16-byte bank groups
@@ -186,10 +189,29 @@ struct TnTiles {
             c[q] = (is_a ? m0 : n0) + cl;
             live[q] = w0 < UNITS && c[q] < (is_a ? g.M : g.N);
             dst[q] = (is_a ? 0 : TR * P) + cl * P + kq[q];
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+                voff[q][r] = live[q] ? (uint32_t)(((kq[q] + r) * ld[q] + c[q]) * (int)sizeof(T)) : kBufferOutOfRange;
         }
     }
     // k-rows k0 + kq .. of every unit into buffer b; k0 relative to the split start kb
     __device__ __forceinline__ void load(int b, int kb, int k0, int k_len) {
+        if constexpr (!RD) {
+            // a resource over the split's rows from k0 on: rows past the split
+            // fall outside it and read zeros, so the per-lane offsets stay fixed
+#pragma unroll
+            for (int q = 0; q < NU; ++q) {
+                const int rem = k_len - k0, rowb = ld[q] * (int)sizeof(T);
+                const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<char*>(base[q]) + (size_t)(k0 > 0 ? k0 : 0) * rowb, (short)0, rem > 0 ? rem * rowb : 0,
+                    kBufferWord3);
+#pragma unroll
+                for (int r = 0; r < PER; ++r)
+                    v[b][q][r].u =
+                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)voff[q][r], 0, 0));
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < NU; ++q)
 #pragma unroll
@@ -722,7 +744,8 @@ __global__ void __launch_bounds__(256) k_gemm_tn(GemmTN g) {
     const __amdgpu_buffer_rsrc_t rb =
         dma_rsrc((const T*)g.b + (size_t)bfirst * g.ldb, (blast - bfirst + 1) * g.ldb * (int)sizeof(T));
     TnTiles<T, TR, TC, KB, RD> tt;
-    tt.setup(ra, rb, g, m0, n0, bfirst, tid);
+    tt.setup(ra, rb, (const char*)g.a + (size_t)kb * g.lda * sizeof(T),
+             (const char*)g.b + (size_t)bfirst * g.ldb * sizeof(T), g, m0, n0, bfirst, tid);
     // an even number of steps (a step past the split multiplies zeros)
     const int ns = ((kl + BK - 1) / BK + 1) / 2 * 2;
     tt.load(0, kb, 0, kl);
