@@ -450,6 +450,30 @@ __global__ void __launch_bounds__(256) k_gemm_nt(GemmNT g) {
 constexpr int kDmaStages = 3;
 constexpr uint32_t kDmaSkip = 0x7FFFF000u;  // offset beyond any tile: the copy reads zeros
 
+// Two bfloat16 in one word (the first in the low half), rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+// max(x, 0) of both bfloat16 halves, as int16: negative values and -0 become +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t d) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, d), s16x2{0, 0}));
+}
+// Bit 0: the low bfloat16 is > 0; bit 1: the high one is (-0, negatives and
+// zero give 0; as int16 the positive values are exactly 1..0x7FFF).
+__device__ __forceinline__ uint32_t pos_bits_bf16x2(uint32_t d) {
+    const s16x2 t = __builtin_elementwise_max(
+        __builtin_elementwise_min(__builtin_bit_cast(s16x2, d), s16x2{1, 1}), s16x2{0, 0});
+    const uint32_t u = __builtin_bit_cast(uint32_t, t);
+    return (u & 1u) | ((u >> 15) & 2u);
+}
+// The low / high bfloat16 of d where bit 0 / bit 1 of b is set, else 0.
+__device__ __forceinline__ uint32_t mask_bf16x2(uint32_t d, uint32_t b) {
+    const int lo = (int)(b << 31) >> 31, hi = (int)(b << 30) >> 31;
+    return d & (((uint32_t)hi & 0xFFFF0000u) | ((uint32_t)lo & 0xFFFFu));
+}
+
 // Workgroup barrier over LDS traffic only: the wave's LDS operations are
 // complete, its global stores may still be in flight (__syncthreads() would
 // wait for those too).
@@ -637,13 +661,15 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int fl = 32 * ii + 8 * gq + 4 * h;
-                    float v[4];
+                    // pack, then ReLU as a packed integer max (a negative
+                    // bfloat16, -0 included, is a negative int16)
+                    uint32_t w2[2];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[e] = acc[i][j][4 * gq + e];
-                        if (g.relu) v[e] = fmaxf(v[e], 0.0f);
+                    for (int e = 0; e < 2; ++e) {
+                        w2[e] = pack_bf16x2(acc[i][j][4 * gq + 2 * e], acc[i][j][4 * gq + 2 * e + 1]);
+                        if (g.relu) w2[e] = relu_bf16x2(w2[e]);
                     }
-                    store4<T>(st + ml * SP + wr * FW + fl, v);
+                    *reinterpret_cast<uint2*>(st + ml * SP + wr * FW + fl) = make_uint2(w2[0], w2[1]);
                 }
             }
         }
@@ -662,8 +688,7 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
                 if (g.bits_in) {
                     const uint32_t mb = mbits[p][q];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (!((mb >> e) & 1u)) x.e[e] = elt_from<T>(0.0f);
+                    for (int w = 0; w < 4; ++w) x.u[w] = mask_bf16x2(x.u[w], mb >> (2 * w));
                 } else if (g.mask) {
                     mk.u = *reinterpret_cast<const u32x4*>((const T*)g.mask + (size_t)m * g.ldm + n);
 #pragma unroll
@@ -674,7 +699,7 @@ __global__ void __launch_bounds__(128 * WC) k_gemm_nt_dma(GemmNT g) {
                 if (g.bits_out) {
                     uint32_t mb = 0;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) mb |= (elt_f(x.e[e]) > 0.0f ? 1u : 0u) << e;
+                    for (int w = 0; w < 4; ++w) mb |= pos_bits_bf16x2(x.u[w]) << (2 * w);
                     g.bits_out[(size_t)m * g.ldbits + n / 8] = (unsigned char)mb;
                 }
             }
