@@ -73,7 +73,7 @@ MEASURED_TRAFFIC = {
     ("hierarchical", "bf16"): (5.1259e8, "d41e3b55704e15e6"),   # k_render_nerf per launch
     ("kilo", "bf16"): (1.5028e9, "92b690704e7eddf5"),          # every kernel of one render
     ("hashgrid", "f32"): (6.4912e9, "839a66438431fb16"),       # both encoder kernels
-    ("train", "bf16"): (9.225e9, "54401cb6260c4e92"),       # every kernel of one step
+    ("train", "bf16"): (9.2027e9, "438843994cafed4a"),       # every kernel of one step
     ("hash_inr", "f32"): (6.48e6, "e4dfd796db811fbe"),         # every kernel of one step, 96 x 96
     ("hash_inr_4m", "f32"): (7.62e8, "e4dfd796db811fbe"),     # every kernel of one step, 2048 x 2048
 }
