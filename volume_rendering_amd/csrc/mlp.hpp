@@ -37,6 +37,17 @@ struct TBF16 {
     }
 };
 
+// bfloat16 with one sample block of 32 per wave: half the registers of
+// TBF16, for kernels that need two waves per SIMD.
+struct TBF16S1 {
+    static constexpr int prec = PREC_BF16;
+    static constexpr int SB = 1;
+    using Op = bf16x8;
+    __device__ static __forceinline__ f32x16 mma(Op a, Op b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
 struct TF32 {
     static constexpr int prec = PREC_F32;
     static constexpr int SB = 1;
@@ -312,18 +323,19 @@ __device__ __forceinline__ float to_agpr(float v) {
 // accumulator p.
 template <class T>
 struct Epi;
-template <>
-struct Epi<TBF16> {
-    // The epilogue in 8 units for the slots between matrix instructions: piece
-    // p = (sb, q) turns 8 accumulators into one operand of the next layer;
-    // unit 2p rounds, packs and rectifies piece p into VGPRs (8 VALU), unit
-    // 2p+1 moves it to the AGPR operand of the next layer (4 writes).
-    static constexpr int units = 8;
+template <int NSB>
+struct EpiBf16 {
+    // The epilogue in 4 units per sample block for the slots between matrix
+    // instructions: piece p = (sb, q) turns 8 accumulators into one operand
+    // of the next layer; unit 2p rounds, packs and rectifies piece p into
+    // VGPRs (8 VALU), unit 2p+1 moves it to the AGPR operand of the next
+    // layer (4 writes).
+    static constexpr int units = 4 * NSB;
     struct Tmp {
         i32x4 t;
     };
     template <int U, bool RELU, class Out>
-    __device__ static __forceinline__ void unit(const f32x16 (&acc)[2], Out& out, int ob, Tmp& tmp) {
+    __device__ static __forceinline__ void unit(const f32x16 (&acc)[NSB], Out& out, int ob, Tmp& tmp) {
         constexpr int P = U / 2, sb = P / 2, q = P % 2;
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -343,6 +355,11 @@ struct Epi<TBF16> {
         }
     }
 };
+
+template <>
+struct Epi<TBF16> : EpiBf16<2> {};
+template <>
+struct Epi<TBF16S1> : EpiBf16<1> {};
 
 template <>
 struct Epi<TF32> {
@@ -401,14 +418,16 @@ constexpr int epi_slot(int u) {
 // layer that reads it as its first input segment, writes every operand
 // before the MFMA that reads it (program order decides which value an
 // operand read sees).  bf16: unit 2p+1 writes operand (step 2*OBP + p%2,
-// sample block p/2), read just before slot 2*step + sb.  f32: unit u writes
-// step 16*OBP + u, read before slot 2*step + 1.
+// sample block p/2), read just before slot 2*step + sb (one sample block:
+// before slot 2*step, the slot after the previous step's MFMA being
+// 2*step - 1).  f32: unit u writes step 16*OBP + u, read before slot
+// 2*step + 1.
 template <class T, int S, int OBP>
 constexpr bool epi_defer_ok() {
     for (int u = 0; u < Epi<T>::units; ++u) {
         const int slot = epi_slot<T, S>(u);
         if (slot >= 2 * S) return false;
-        if constexpr (T::SB == 2) {
+        if constexpr (T::prec == PREC_BF16) {
             if (u % 2 == 0) continue;
             const int p = u / 2, k = 2 * OBP + p % 2, sb = p / 2;
             if (k < S && !(slot < 2 * k + sb)) return false;

@@ -265,6 +265,25 @@ __device__ __forceinline__ void grid_operands(bf16x8 (&op)[NS][2], const GridArg
 }
 
 template <int NS>
+__device__ __forceinline__ void grid_operands(bf16x8 (&op)[NS][1], const GridArgs& g, const float (&u)[1][3],
+                                              int lane) {
+    static_assert(NS == 2, "32 grid features");
+    const int h = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bf16x8 v;
+#pragma unroll
+        for (int jl = 0; jl < 4; ++jl) {
+            float f0, f1;
+            grid_level(g, 8 * s + 4 * h + jl, u[0][0], u[0][1], u[0][2], f0, f1, nullptr);
+            v[2 * jl] = to_bf16(f0);
+            v[2 * jl + 1] = to_bf16(f1);
+        }
+        op[s][0] = v;
+    }
+}
+
+template <int NS>
 __device__ __forceinline__ void grid_operands(float (&op)[NS][1], const GridArgs& g, const float (&u)[1][3],
                                               int lane) {
     static_assert(NS == 16, "32 grid features");
@@ -293,14 +312,32 @@ __device__ __forceinline__ void sh_operands(bf16x8 (&op)[NS][2], const float (&s
 }
 
 template <int NS>
+__device__ __forceinline__ void sh_operands(bf16x8 (&op)[NS][1], const float (&sh)[16], int lane) {
+    const int h = lane >> 5;
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = to_bf16(h ? sh[8 + j] : sh[j]);
+    op[0][0] = v;
+}
+
+template <int NS>
 __device__ __forceinline__ void sh_operands(float (&op)[NS][1], const float (&sh)[16], int lane) {
     const int h = lane >> 5;
 #pragma unroll
     for (int s = 0; s < 8; ++s) op[s][0] = h ? sh[2 * s + 1] : sh[2 * s];
 }
 
+// One sample block per wave (TBF16S1) halves the registers so that two
+// workgroups share a CU: the table gathers of one wave then overlap the
+// vector and matrix work of another.  The weight ring is two slots deep to
+// fit two workgroups' LDS.
 template <class T>
-__global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
+constexpr int kHashRenderGroupsPerCu = T::SB == 1 && T::prec == PREC_BF16 ? 2 : 1;
+template <class T>
+constexpr int kHashRenderRing = kHashRenderGroupsPerCu<T> == 2 ? 2 : kRenderRing;
+
+template <class T>
+__global__ void __launch_bounds__(256, kHashRenderGroupsPerCu<T>) k_render_hash(RenderArgs a, GridArgs g) {
     __shared__ RenderLds lds_all[4];
     constexpr int K = NET_HASH_FIELD;
     constexpr int FS = seg_steps(net_layers(K)[0].s0, T::prec);
@@ -374,7 +411,7 @@ __global__ void __launch_bounds__(256) k_render_hash(RenderArgs a, GridArgs g) {
         grid_operands(feats, g, u, lane);
         f32x16 sig[SB], rgb[SB];
         const char* pk = opaque((const char*)a.coarse);
-        LdsStream<T, NET_HASH_FIELD, kRenderRing> ws(pk, lane, wave);
+        LdsStream<T, NET_HASH_FIELD, kHashRenderRing<T>> ws(pk, lane, wave);
         hash_field_forward<T>(feats, shop, ws, (const NERF_AS_LDS float*)bias_lds, sig, rgb, lane);
         if (lane < 32) {
 #pragma unroll

@@ -6,7 +6,7 @@ namespace nerf {
 void launch_render_hash(int bf16, const RenderArgs& a, const GridArgs& g, hipStream_t s) {
     const dim3 grid((unsigned)((a.n_rays + 3) / 4));
     if (bf16)
-        hipLaunchKernelGGL(k_render_hash<TBF16>, grid, dim3(256), 0, s, a, g);
+        hipLaunchKernelGGL(k_render_hash<TBF16S1>, grid, dim3(256), 0, s, a, g);
     else
         hipLaunchKernelGGL(k_render_hash<TF32>, grid, dim3(256), 0, s, a, g);
 }
