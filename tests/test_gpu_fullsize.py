@@ -70,7 +70,12 @@ def test_hierarchical_full(v):
     assert np.array_equal(gz, z2)
     # end to end: rays whose resampled depths differ when the oracle's own coarse weights are used
     _, _, z2_e2e = osamp.hierarchical_fine_samples(zc, coarse["w"].astype(np.float32), 128, 0, sel)
-    say(f"  end-to-end resampling: {100 * np.mean(np.any(z2_e2e != gz, axis=1)):.1f}% of sampled rays differ in a bin")
+    flip = float(np.mean(np.any(z2_e2e != gz, axis=1)))
+    say(f"  end-to-end resampling: {100 * flip:.1f}% of sampled rays differ in a bin")
+    # a ray differs when one of its 128 uniforms falls within the CDF change
+    # the coarse-weight error causes of one of 63 bin edges: with weights
+    # within ~3e-8 of the emulation that is ~0.3% of rays; 2% leaves margin
+    assert flip <= 0.02, flip
     fine = in_chunks(lambda c: oren.nerf_pass(pf, o[c], d[c], gz[c], 10, 4, "f64"), SUBSET)
     emu = in_chunks(lambda c: oren.nerf_pass(pf, o[c], d[c], gz[c], 10, 4, "bf16"), SUBSET)
     bf16_render_check("fine pass", g_rgb, g_dep, g_acc, fine["raw"], emu["raw"], gz, d)
