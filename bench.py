@@ -71,13 +71,13 @@ KERNEL_SOURCES = {
     "hash_inr_4m": _INR_SOURCES,
 }
 MEASURED_TRAFFIC = {
-    ("hierarchical", "bf16"): (5.1258e8, "4a9d57f54df051bc"),   # k_render_nerf per launch
-    ("kilo", "bf16"): (1.5026e9, "25cb46cf82da7e9b"),          # every kernel of one render
-    ("hashgrid", "f32"): (6.4819e9, "839a66438431fb16"),       # both encoder kernels
-    ("train", "bf16"): (9.2043e9, "0027cbc732e38b5d"),       # every kernel of one step
-    ("hash", "bf16"): (1.9769e10, "190ed9b568e25d83"),       # k_render_hash per launch (gathers missing L2)
-    ("hash_inr", "f32"): (6.48e6, "e4dfd796db811fbe"),         # every kernel of one step, 96 x 96
-    ("hash_inr_4m", "f32"): (7.64e8, "e4dfd796db811fbe"),     # every kernel of one step, 2048 x 2048
+    ("hierarchical", "bf16"): (5.1258e8, "f034620437ea85cf"),   # k_render_nerf per launch
+    ("kilo", "bf16"): (1.5026e9, "2b3cdabff501d0ed"),          # every kernel of one render
+    ("hashgrid", "f32"): (6.4819e9, "148a965141f8efaa"),       # both encoder kernels
+    ("train", "bf16"): (9.2043e9, "d4e1de2ca3da3bcb"),       # every kernel of one step
+    ("hash", "bf16"): (1.9769e10, "b9fa053d5b66c96c"),       # k_render_hash per launch (gathers missing L2)
+    ("hash_inr", "f32"): (6.48e6, "90f94c1673d6711e"),         # every kernel of one step, 96 x 96
+    ("hash_inr_4m", "f32"): (7.64e8, "90f94c1673d6711e"),     # every kernel of one step, 2048 x 2048
 }
 
 

@@ -164,6 +164,23 @@ typedef struct {
 /* ---------------------------------------------------------------------- */
 
 int nerf_abi_version(void);
+
+/* Index checks of the kernels.  In a library built with -DNERF_CHECK
+ * (libnerf_mi355x_checked.so) the kernels record failed index-range checks
+ * (hash-grid corner indices, ray-sample and merged-sample positions,
+ * inverse-CDF bins, occupancy words, cell ids, live-list entries and bucket
+ * slots) and failed input preconditions as bits of a flag word instead of
+ * faulting.  This call waits for the
+ * device, returns the bits set since the previous call (0: none) and clears
+ * them; a library built without the checks returns -1.  Bits: 0 hash-grid
+ * corner index outside its level's table, 1 sample index outside a ray's
+ * sample arrays, 2 inverse-CDF bin outside 1 .. n_coarse - 2, 3 merged
+ * sample position outside the merged array, 4 occupancy word outside the
+ * bitset, 5 cell id outside the cell grid, 6 live-list entry or bucket slot
+ * outside the workspace, 7 compaction entry outside a workgroup's LDS list,
+ * 8 an inverse-CDF weight outside nerf_sample_pdf's precondition (finite, in
+ * [0, 100]); all bits set: the flags could not be read. */
+int64_t nerf_check_flags(void);
 const char* nerf_status_str(nerf_status s);
 /* Thread-local text of the last error on this thread ("" if none). */
 const char* nerf_last_error(void);

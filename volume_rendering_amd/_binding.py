@@ -28,7 +28,7 @@ EXPORTED = [
     "nerf_encode_hashgrid", "nerf_mlp", "nerf_composite", "nerf_sample_pdf", "nerf_render",
     "nerf_render_workspace_size", "nerf_render_noalloc", "nerf_render_poses", "nerf_train_param_count",
     "nerf_train_workspace_size", "nerf_train_step", "nerf_hash_inr_param_count", "nerf_hash_inr_workspace_size",
-    "nerf_hash_inr_train_step",
+    "nerf_hash_inr_train_step", "nerf_check_flags",
 ]
 
 
@@ -89,6 +89,7 @@ def lib():
         P, I, I64, U64, S = C.c_void_p, C.c_int, C.c_int64, C.c_uint64, C.c_size_t
         sig = {
             "nerf_abi_version": (I, []),
+            "nerf_check_flags": (I64, []),
             "nerf_status_str": (C.c_char_p, [I]),
             "nerf_last_error": (C.c_char_p, []),
             "nerf_hashgrid_init": (I, [C.POINTER(nerf_hashgrid), I, I, C.c_uint32, I, I]),
@@ -149,6 +150,11 @@ def _stream(device=None):
 
 def nerf_abi_version() -> int:
     return lib().nerf_abi_version()
+
+
+def nerf_check_flags() -> int:
+    """Failed index-check bits since the last call (checked library), or -1."""
+    return int(lib().nerf_check_flags())
 
 
 def nerf_hashgrid_init(n_levels=16, table_size=2 ** 19, n_min=16, n_max=2048, dim=3) -> nerf_hashgrid:

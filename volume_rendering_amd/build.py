@@ -1,6 +1,8 @@
-"""Builds libnerf_mi355x.so in-tree with hipcc for gfx950.
+"""Builds libnerf_mi355x.so in-tree with hipcc for gfx950, and the checked
+library libnerf_mi355x_checked.so (the same sources with -DNERF_CHECK: the
+kernels record failed index-range checks, read back by nerf_check_flags).
 
-    python -m volume_rendering_amd.build          # build (always recompiles)
+    python -m volume_rendering_amd.build          # build both (always recompiles)
 
 Every HIP source is compiled with fused multiply-add contraction off (the
 bit-reproducible steps are written as explicitly rounded float32/float64
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnerf_mi355x.so")
+LIB_CHECKED = os.path.join(PKG, "libnerf_mi355x_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -37,10 +40,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 DEVICE_AGPR_FORM = {"hash_train.hip"}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, checked: bool = False) -> str:
+    obj = os.path.join(BUILD, "checked" if checked else "", os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [HIPCC] + COMMON
+    cmd = [HIPCC] + COMMON + (["-DNERF_CHECK"] if checked else [])
     if src.endswith(".hip"):
         dev = DEVICE if src not in DEVICE_AGPR_FORM else [a for a in DEVICE if a not in ("-mllvm",
                                                                                        "-amdgpu-mfma-vgpr-form")]
@@ -56,12 +59,14 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, checked: bool = False) -> str:
+    """Builds one library (the checked one with checked=True); returns its path."""
+    lib = LIB_CHECKED if checked else LIB
+    os.makedirs(os.path.join(BUILD, "checked") if checked else BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, checked), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -73,11 +78,16 @@ def build(verbose: bool = True) -> str:
     missing = [l.split()[-1] for l in und.stdout.splitlines() if "__device_stub__" in l]
     if missing:
         raise RuntimeError("kernels without host launch stubs:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_all(verbose: bool = True) -> None:
+    build(verbose)
+    build(verbose, checked=True)
 
 
 if __name__ == "__main__":
-    build()
+    build_all()

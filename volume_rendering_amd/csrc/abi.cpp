@@ -8,12 +8,27 @@
 #include <cstdio>
 #include <string>
 
+#include <vector>
+
 #include "abi_util.hpp"
 #include "launch.hpp"
 #include "nerf_mi355x.h"
 #include "nets.hpp"
 
 using namespace nerf;
+
+namespace nerf {
+// Readers of the index-check words of every translation unit of a checked
+// build, registered while the library loads (none without NERF_CHECK).
+std::vector<unsigned (*)()>& check_readers() {
+    static std::vector<unsigned (*)()> readers;
+    return readers;
+}
+int check_register(unsigned (*take)()) {
+    check_readers().push_back(take);
+    return 0;
+}
+}  // namespace nerf
 
 namespace {
 
@@ -119,6 +134,17 @@ nerf_status nerf_fail(nerf_status s, const char* fmt, ...) {
 extern "C" {
 
 int nerf_abi_version(void) { return NERF_ABI_VERSION; }
+
+int64_t nerf_check_flags(void) {
+#ifdef NERF_CHECK
+    if (hipDeviceSynchronize() != hipSuccess) return (int64_t)0xFFFFFFFFu;
+    unsigned v = 0u;
+    for (unsigned (*take)() : nerf::check_readers()) v |= take();
+    return (int64_t)v;
+#else
+    return -1;
+#endif
+}
 
 const char* nerf_status_str(nerf_status s) {
     switch (s) {

@@ -10,6 +10,45 @@ namespace nerf {
 
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------------------
+// Index checks of the checked build (-DNERF_CHECK): a failed check sets its
+// bit in this translation unit's device word (an atomic or; nothing traps,
+// so a bad index is reported after the run instead of faulting the GPU).
+// nerf_check_flags() reads and clears the words of every unit.  Without
+// NERF_CHECK the checks compile to nothing.
+// ---------------------------------------------------------------------------
+enum CheckBit : unsigned {
+    kCheckGridIndex = 0,    // hash-grid corner index outside its level's table
+    kCheckRaySample = 1,    // sample index outside a ray's sample arrays
+    kCheckPdfBin = 2,       // inverse-CDF bin outside 1 .. n_coarse - 2
+    kCheckMerge = 3,        // merged sample position outside the merged array
+    kCheckVoxel = 4,        // occupancy word outside the bitset
+    kCheckCell = 5,         // cell id outside the cell grid
+    kCheckLiveEntry = 6,    // live-list entry or bucket slot outside the workspace
+    kCheckCompactLds = 7,   // compaction entry outside the workgroup's LDS list
+    kCheckPdfWeight = 8,    // inverse-CDF weight outside its precondition: finite, in [0, 100]
+};
+#ifdef NERF_CHECK
+int check_register(unsigned (*take)());
+static __device__ unsigned g_check_word;
+#define NERF_DCHECK(cond, bit)                                                   \
+    do {                                                                         \
+        if (!(cond)) atomicOr(&::nerf::g_check_word, 1u << (unsigned)(bit));    \
+    } while (0)
+// This unit's word, cleared after the read (all bits set if the read failed).
+static unsigned check_take() {
+    unsigned v = 0u, zero = 0u;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_word), sizeof v) != hipSuccess) return ~0u;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_word), &zero, sizeof zero) != hipSuccess) return ~0u;
+    return v;
+}
+static const int g_check_registered = check_register(&check_take);
+#else
+#define NERF_DCHECK(cond, bit) \
+    do {                       \
+    } while (0)
+#endif
+
 // Pointer into LDS (address space 3): reads through it are LDS reads.
 #define NERF_LDS_PTR __attribute__((address_space(3)))*
 

@@ -160,6 +160,8 @@ __device__ __forceinline__ bool classify(const KiloArgs& k, const float (&x)[3],
     const uint64_t res = (uint64_t)k.occ_res;
     const uint64_t vox = ((uint64_t)v[0] * res + (uint64_t)v[1]) * res + (uint64_t)v[2];
     cell = (c[0] * k.cell_res + c[1]) * k.cell_res + c[2];
+    NERF_DCHECK((vox >> 5) < (res * res * res + 31u) / 32u, kCheckVoxel);
+    NERF_DCHECK(cell >= 0 && cell < k.cell_res * k.cell_res * k.cell_res, kCheckCell);
     const bool occ = (k.occ[vox >> 5] >> (uint32_t)(vox & 31u)) & 1u;
     return inside && occ;
 }
@@ -246,6 +248,8 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
         uint32_t c = k.ray_start[r] - e0;
         for (int w = 0; w < k.mask_words; ++w) {
             const unsigned long long mw = mask[w];
+            NERF_DCHECK(!((mw >> lane) & 1ull) || c + __popcll(mw & below) < kCompactRays * kKiloMaxSamples,
+                        kCheckCompactLds);
             if ((mw >> lane) & 1ull)
                 ents[c + __popcll(mw & below)] = (uint16_t)(((uint32_t)(r - r0) << 8) | (uint32_t)(kWave * w + lane));
             c += (uint32_t)__popcll(mw);
@@ -272,6 +276,7 @@ __global__ void __launch_bounds__(256) k_kilo_compact(RenderArgs a, KiloArgs k) 
         else
             slot = kSlotFinal | atomicAdd(&k.cell_count[cell], 1u);
         const uint32_t e = e0 + q;
+        NERF_DCHECK((uint64_t)e < (uint64_t)a.n_rays * (uint64_t)a.n_coarse, kCheckLiveEntry);
         k.ent_ray[e] = (uint32_t)r;
         k.ent_meta[e] = ((uint32_t)i << 16) | (uint32_t)cell;
         k.ent_slot[e] = slot;
@@ -317,6 +322,8 @@ __global__ void __launch_bounds__(256) k_kilo_scatter(RenderArgs a, KiloArgs k) 
         float x[3];
         sample_point(a, R, r, (int)(meta >> 16), x);
         const float dn = sqrtf(R.d[0] * R.d[0] + R.d[1] * R.d[1] + R.d[2] * R.d[2]);
+        NERF_DCHECK((uint64_t)k.cell_start[meta & 0xFFFFu] + k.ent_slot[e] < (uint64_t)a.n_rays * (uint64_t)a.n_coarse,
+                    kCheckLiveEntry);
         f32x4* slot = reinterpret_cast<f32x4*>(k.bucket) + 2 * (size_t)(k.cell_start[meta & 0xFFFFu] + k.ent_slot[e]);
         slot[0] = f32x4{x[0], x[1], x[2], __uint_as_float(e)};
         slot[1] = f32x4{R.d[0] / dn, R.d[1] / dn, R.d[2] / dn, 0.0f};

@@ -90,6 +90,7 @@ __device__ __forceinline__ void sample_pdf_ray(const float* zc, const float* wc,
     double carry = 0.0;
     for (int base = 0; base < B; base += kWave) {
         const int j = base + lane;
+        NERF_DCHECK(j >= B || (wc[j + 1] >= 0.0f && wc[j + 1] <= 100.0f), kCheckPdfWeight);
         const double v = j < B ? (double)__fadd_rn(wc[j + 1], 1e-5f) : 0.0;
         const double incl = wave_scan_add_f64(v);
         if (j < B) cdf[j + 1] = carry + incl;
@@ -109,6 +110,7 @@ __device__ __forceinline__ void sample_pdf_ray(const float* zc, const float* wc,
             else
                 hi = mid;
         }
+        NERF_DCHECK(lo >= 1 && lo <= B, kCheckPdfBin);
         const int below = lo - 1 > 0 ? lo - 1 : 0;
         const int above = lo < B ? lo : B;
         const double cb = cdf[below];
@@ -187,6 +189,7 @@ __device__ __forceinline__ void merge_sorted(const float* a, int na, const float
             else
                 hi = mid;
         }
+        NERF_DCHECK(e + lo < na + nb, kCheckMerge);
         out[e + lo] = v;
     }
     for (int m = lane; m < nb; m += kWave) {
@@ -199,6 +202,7 @@ __device__ __forceinline__ void merge_sorted(const float* a, int na, const float
             else
                 hi = mid;
         }
+        NERF_DCHECK(m + lo < na + nb, kCheckMerge);
         out[m + lo] = v;
     }
 }
@@ -245,6 +249,7 @@ __device__ __forceinline__ bool box_occupied(const uint32_t* occ, int res, float
     }
     const uint64_t r = (uint64_t)res;
     const uint64_t vox = ((uint64_t)v[0] * r + (uint64_t)v[1]) * r + (uint64_t)v[2];
+    NERF_DCHECK((vox >> 5) < (r * r * r + 31u) / 32u, kCheckVoxel);
     return inside && ((occ[vox >> 5] >> (uint32_t)(vox & 31u)) & 1u);
 }
 
@@ -351,6 +356,13 @@ struct GridLookup {
         }
     }
 
+    // entries of a level's table: (N+1)^DIM direct, T hashed
+    __device__ static __forceinline__ uint32_t level_entries(int N, bool direct, uint32_t tmask) {
+        uint32_t e = 1u;
+        for (int a = 0; a < DIM; ++a) e *= (uint32_t)(N + 1);
+        return direct ? e : tmask + 1u;
+    }
+
     __device__ static __forceinline__ uint32_t index(const int (&i)[DIM], int N, bool direct, uint32_t tmask) {
         if constexpr (DIM == 3)
             return grid_index(i[0], i[1], i[2], N, direct, tmask);
@@ -382,6 +394,8 @@ struct GridLookup {
             }
             A0[q] = off + index(ia, N, direct, tmask);
             A1[q] = off + index(ib, N, direct, tmask);
+            NERF_DCHECK(A0[q] - off < level_entries(N, direct, tmask) && A1[q] - off < level_entries(N, direct, tmask),
+                        kCheckGridIndex);
             P[q] = (A0[q] >> 1) == (A1[q] >> 1);
             W[q] = tab.word(A0[q] & ~1u);
             B[q] = tab.entry_unless(A1[q], P[q]);

@@ -69,6 +69,7 @@ __device__ __forceinline__ int live_samples(const RenderArgs& a, const float* zp
             lv = box_occupied(a.occ, a.occ_res, a.vscale, a.box_lo, a.box_hi, x);
         }
         const unsigned long long m = __ballot(lv);
+        NERF_DCHECK(!lv || n + __popcll(m & below) < kMaxRaySamples, kCheckRaySample);
         if (lv) list[n + __popcll(m & below)] = i;
         n += __popcll(m);
     }
@@ -192,6 +193,7 @@ __global__ void __launch_bounds__(256) k_render_nerf(RenderArgs a) {
                 const int j = b * M + sb * 32 + (lane & 31);
                 valid[sb] = !idle && j < n_eval;
                 si[sb] = valid[sb] ? (a.occ ? S.live[j] : j) : 0;
+                NERF_DCHECK(si[sb] >= 0 && si[sb] < N && N <= kMaxRaySamples, kCheckRaySample);
                 const float z = zp[si[sb]];
 #pragma unroll
                 for (int k = 0; k < 3; ++k) x[sb][k] = __fadd_rn(o[k], __fmul_rn(z, d[k]));
