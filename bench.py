@@ -76,8 +76,8 @@ MEASURED_TRAFFIC = {
     ("hashgrid", "f32"): (6.4819e9, "148a965141f8efaa"),       # both encoder kernels
     ("train", "bf16"): (9.2043e9, "d4e1de2ca3da3bcb"),       # every kernel of one step
     ("hash", "bf16"): (1.9769e10, "b9fa053d5b66c96c"),       # k_render_hash per launch (gathers missing L2)
-    ("hash_inr", "f32"): (6.48e6, "90f94c1673d6711e"),         # every kernel of one step, 96 x 96
-    ("hash_inr_4m", "f32"): (7.64e8, "90f94c1673d6711e"),     # every kernel of one step, 2048 x 2048
+    ("hash_inr", "f32"): (6.48e6, "2ab8671f0bf90ff6"),         # every kernel of one step, 96 x 96
+    ("hash_inr_4m", "f32"): (7.64e8, "2ab8671f0bf90ff6"),     # every kernel of one step, 2048 x 2048
 }
 
 

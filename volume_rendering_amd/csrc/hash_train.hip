@@ -117,6 +117,13 @@ __device__ __forceinline__ Level level_params(const GridArgs& g, int l) {
     return Level{g.res[li], (uint32_t)g.offset[li], g.direct[li] != 0, g.mask[li]};
 }
 
+// b^e in 32 bits (the entries of a direct level: (N+1)^DIM).
+__device__ __forceinline__ uint32_t ipow_u32(int b, int e) {
+    uint32_t r = 1u;
+    for (int i = 0; i < e; ++i) r *= (uint32_t)b;
+    return r;
+}
+
 // A level at point u: the 2^DIM corners' absolute table entries and
 // multilinear weights (cell c = u N in float32, corners clamped to [0, N],
 // corner bits lexicographic, first axis most significant).
@@ -152,6 +159,7 @@ __device__ __forceinline__ void level_corners(const Level& lv, uint32_t tmask, c
             idx_d = grid_index(ci[0], ci[1], N, true, tmask);
             idx_h = grid_index(ci[0], ci[1], N, false, tmask);
         }
+        NERF_DCHECK(lv.direct ? idx_d < ipow_u32(N + 1, DIM) : idx_h <= tmask, kCheckGridIndex);
         e[q] = lv.off + (lv.direct ? idx_d : idx_h);
         wt[q] = wq;
     }
