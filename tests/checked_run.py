@@ -136,6 +136,30 @@ def main():
     v.nerf_hash_inr_train_step(xi, torch.rand((3000, 1), device=dev), gi, icfg, ip, empty(1),
                                torch.zeros_like(ip), torch.zeros_like(ip), 1)
     bad |= check("hash-grid INR step")
+    # full-size workloads: the largest indices each path forms
+    Rf = 800 * 800
+    fo, fd, fn, ff = rays(1, 800, 800, 1110.0, Rf, 4)
+    frgb, fdep, facc = empty(Rf, 3), empty(Rf), empty(Rf)
+    w = B.nerf_weights(net=B.nerf_mlp_desc(3, 1), cells=cells.data_ptr(), n_cells=4096)
+    v.nerf_render(fo, fd, fn, ff, w, cfg, frgb, fdep, facc)
+    bad |= check("many-network render, 640,000 rays")
+    nc_ = v.weights.pack_to_device(1, 1, si.nerf_params(si.NERF_8x256, seed=0, net_id=0))
+    nf_ = v.weights.pack_to_device(1, 1, si.nerf_params(si.NERF_8x256, seed=0, net_id=1))
+    w = B.nerf_weights(net=B.nerf_mlp_desc(1, 1), coarse=nc_.data_ptr(), fine=nf_.data_ptr())
+    hcfg = B.nerf_render_cfg(mode=0, n_coarse=64, n_fine=128, use_pi=1, jitter=1, seed=0)
+    v.nerf_render(fo, fd, fn, ff, w, hcfg, frgb, fdep, facc)
+    bad |= check("hierarchical render, one 800 x 800 pose")
+    Rh = 256 * 256
+    ho, hd, hn, hf = rays(1, 256, 256, 355.2, Rh, 5)
+    net = v.weights.pack_to_device(4, 1, si.hash_field_params(seed=3))
+    w = B.nerf_weights(net=B.nerf_mlp_desc(4, 1), coarse=net.data_ptr())
+    w.grid = B.C.pointer(g)
+    cfg_h = B.nerf_render_cfg(mode=1, n_coarse=128, use_pi=1, jitter=1, seed=5, box_lo=-1.5, box_hi=1.5)
+    v.nerf_render(ho, hd, hn, hf, w, cfg_h, empty(Rh, 3), empty(Rh), empty(Rh))
+    bad |= check("hash render, 256 x 256 rays")
+    xq = t(si.query_points(1 << 22, seed=0))
+    v.nerf_encode_hashgrid(xq, g, empty(1 << 22, 32))
+    bad |= check("hash-grid encoder, 2^22 points")
     if bad:
         print(f"FAILED: index checks recorded {bad:#x}")
         return 1
