@@ -35,6 +35,18 @@ def test_library_exports_every_declared_symbol():
     assert set(B.EXPORTED) == names
 
 
+def test_checked_library_exports_the_same_symbols():
+    """The normal library has no index checks (nerf_check_flags returns -1
+    without touching a device); the checked one, built from the same sources
+    with -DNERF_CHECK, exports every declared symbol too."""
+    assert v.nerf_check_flags() == -1
+    path = os.path.join(ROOT, "volume_rendering_amd", "libnerf_mi355x_checked.so")
+    assert os.path.exists(path), "build both libraries: python -m volume_rendering_amd.build"
+    L = C.CDLL(path)
+    for n in declared_symbols():
+        assert hasattr(L, n), n
+
+
 def test_abi_version_and_status_strings():
     L = v.lib()
     assert v.nerf_abi_version() == 2
