@@ -6,7 +6,7 @@ outside its documented precondition (finite weights in [0, 100]; the kernel
 runs on and keeps every index in range), and requires that the precondition
 check records it and nothing else.
 
-Run by tests/test_gpu_checked.py in a process of its own, because the
+Run by tests/test_gpu_zchecked.py in a process of its own, because the
 binding loads one library per process.  Exit status 0 when both hold."""
 import os
 import sys
